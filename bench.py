@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the VQ decode GEMV on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--copies C]
+
+A step is one decode call of one layer: the grouped vq_gemv over the four
+4096x4096 2-bit q/k/v/o matrices of a LLaMA-7B layer, batch 1 (workload 2;
+--workload selects another, see synth).  Inputs are resident in HBM before
+the timed region.  The timed steps rotate through C distinct copies of the
+layer's packed indices (>= 2 GiB in total, larger than the 256 MB
+Infinity Cache and the L2s) so every step streams its indices from HBM.  The
+C calls are captured once in a HIP graph and the graph is replayed; HIP
+events on the launch stream bracket the timed replays.
+
+Prints one JSON line: effective weight-byte throughput (GB/s) as `value`,
+microseconds per layer, the HBM roofline fraction of the lookup kernel and
+the CPU float64 oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, decimal GB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=25600)
+    p.add_argument("--warmup", type=int, default=1024)
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 5])
+    p.add_argument("--copies", type=int, default=0, help="layer copies (0: enough for 2 GiB)")
+    p.add_argument("--no-graph", action="store_true", help="launch from Python instead of a graph")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    return p.parse_args()
+
+
+WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
+                  2: "llama7b-attn-qkvo-4096x4096-2bit-b1",
+                  5: "gemma2-9b-mlp-rotated-vq-residual-3.125bit-b1"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import vector_quantized_decode_amd as vq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.workload(args.workload)
+    residual = wl.residual
+    layer_bytes = synth.weight_bytes(args.workload)
+    copies = args.copies or max(1, -(-(2 << 30) // layer_bytes))
+
+    # ---- inputs: copy 0 from the seeded generator, packed + laid out by the library
+    t0 = time.time()
+    mis = [synth.matrix_inputs(args.workload, m) for m in range(wl.count)]
+    base = []
+    for mi in mis:
+        if residual:
+            base.append(vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
+                                         sign_bits=mi.sign_bits, alpha=mi.alpha, group=mi.group,
+                                         rht_sign=mi.rht_sign, had_block=mi.had_block, device=dev))
+        else:
+            base.append(vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, device=dev))
+    xs = [torch.from_numpy(mi.x).to(dev) for mi in mis]
+    # further copies: seeded uniform random bytes in the device layouts (uniform bytes are
+    # uniform indices and Bernoulli(0.5) sign bits); alpha is shared
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * args.workload + 99)
+    layers = [base]
+    for c in range(1, copies):
+        lay = []
+        for m in base:
+            cp = vq.DeviceMatrix(m.K, m.N, m.d, m.nbits,
+                                 torch.randint(0, 256, m.wi.shape, dtype=torch.uint8, device=dev,
+                                               generator=gen), m.wc)
+            if residual:
+                cp.signs = torch.randint(0, 256, m.signs.shape, dtype=torch.uint8, device=dev,
+                                         generator=gen)
+                cp.alpha, cp.group, cp.rht_sign, cp.had_block = m.alpha, m.group, m.rht_sign, m.had_block
+            lay.append(cp)
+        layers.append(lay)
+    ys = [torch.empty((wl.B, m.N), dtype=torch.float32, device=dev) for m in base]
+    ws = vq.alloc_workspace(base, wl.B, residual=residual, device=dev)
+    call = vq.vq_gemv_residual if residual else vq.vq_gemv
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    print(f"# setup: {copies} copies x {layer_bytes} B in {setup_s:.1f} s", file=sys.stderr, flush=True)
+
+    # ---- sampled parity check of copy 0 in the timed launch configuration
+    parity = None
+    if not args.no_check:
+        import oracle
+        call(layers[0], xs, wl.B, ys, ws, ws.numel())
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(7)
+        worst = 0.0
+        ok = True
+        for mi, y in zip(mis, ys):
+            rows = np.sort(rng.choice(mi.N, size=min(256, mi.N), replace=False))
+            if residual:
+                ref = oracle.vq_gemv_residual(mi.x, mi.wc, oracle.pack_rows(mi.idx[rows], 8),
+                                              oracle.pack_rows(mi.sign_bits[rows], 1),
+                                              mi.alpha[rows], mi.rht_sign, mi.had_block,
+                                              rows.size, mi.K, mi.d, mi.nbits, mi.group)
+            else:
+                ref = oracle.vq_gemv(mi.x, mi.wc, oracle.pack_rows(mi.idx[rows], mi.nbits),
+                                     rows.size, mi.K, mi.d, mi.nbits)
+            got = y.cpu().numpy()[:, rows]
+            rel, mx, rms = oracle.compare(got, ref)
+            worst = max(worst, rel)
+            ok = ok and oracle.within_tolerance(got, ref)
+        parity = {"sampled_rows_per_matrix": 256, "max_rel_l2": worst, "pass": bool(ok)}
+        print(f"# parity (sampled rows): max rel_l2 {worst:.3e} pass={ok}", file=sys.stderr, flush=True)
+
+    # ---- graph of one pass over all copies
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    per_graph = copies
+    graph = None
+    if not args.no_graph:
+        with torch.cuda.stream(stream):
+            for lay in layers[:2]:            # warm the launch path before capture
+                call(lay, xs, wl.B, ys, ws, ws.numel(), stream=stream)
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for lay in layers:
+                call(lay, xs, wl.B, ys, ws, ws.numel(), stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+
+    def run_steps(nsteps):
+        if graph is not None:
+            for _ in range(max(1, nsteps // per_graph)):
+                graph.replay()
+            return max(1, nsteps // per_graph) * per_graph
+        with torch.cuda.stream(stream):
+            for i in range(nsteps):
+                call(layers[i % copies], xs, wl.B, ys, ws, ws.numel(), stream=stream)
+        return nsteps
+
+    with torch.cuda.stream(stream):
+        run_steps(max(args.warmup, per_graph))
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(stream):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        done = run_steps(args.steps)
+        ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    us_per_layer = ms * 1e3 / done
+    gbs = layer_bytes / (us_per_layer * 1e-6) / 1e9
+    print(f"# timed {done} steps in {ms:.2f} ms: {us_per_layer:.3f} us/layer, {gbs:.1f} GB/s",
+          file=sys.stderr, flush=True)
+
+    # ---- CPU oracle baseline on a bounded sample (rank 0, N=1)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        n_rows = 512 if residual else 1024
+        packed = []
+        sample_bytes = 0
+        for mi in mis:
+            if residual:
+                packed.append((oracle.pack_rows(mi.idx[:n_rows], 8),
+                               oracle.pack_rows(mi.sign_bits[:n_rows], 1)))
+                sample_bytes += n_rows * (mi.K // mi.d * mi.nbits // 8 + mi.K // 8 + mi.K // 64)
+            else:
+                packed.append((oracle.pack_rows(mi.idx[:n_rows], mi.nbits), None))
+                sample_bytes += n_rows * mi.K // mi.d * mi.nbits // 8
+            sample_bytes += (1 << mi.nbits) * mi.d * 2
+        reps = []
+        with threadpool_limits(limits=1):
+            for rep in range(4):
+                t = time.perf_counter()
+                for mi, (pw, ps) in zip(mis, packed):
+                    if residual:
+                        oracle.vq_gemv_residual(mi.x, mi.wc, pw, ps, mi.alpha[:n_rows], mi.rht_sign,
+                                                mi.had_block, n_rows, mi.K, mi.d, mi.nbits, mi.group)
+                    else:
+                        oracle.vq_gemv(mi.x, mi.wc, pw, n_rows, mi.K, mi.d, mi.nbits)
+                if rep:
+                    reps.append(time.perf_counter() - t)
+        med = statistics.median(reps)
+        cores = len(os.sched_getaffinity(0))
+        cpu = {"value": round(sample_bytes / med / 1e9, 5), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"first {n_rows} rows of each of the {wl.count} matrices plus their "
+                         f"codebooks ({sample_bytes} weight bytes); float64 numpy oracle (unpack, "
+                         f"output codebook, lookup sum); BLAS limited to 1 thread; median of 3 timed "
+                         f"runs after 1 warm run; host has {cores} cores",
+               "seconds_per_sample": round(med, 4)}
+
+    out = {
+        "metric": "us/layer and effective HBM GB/s (% of peak) for VQ-GEMV at LLaMA-7B, B=1",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": done,
+        "warmup": args.warmup,
+        "ms_per_step": us_per_layer / 1e3,
+        "us_per_layer": round(us_per_layer, 4),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "matrices": wl.count,
+                   "K_N": [[s.K, s.N] for s in wl.matrices], "d": wl.d, "nbits": wl.nbits,
+                   "B": wl.B, "weight_bytes_per_layer": layer_bytes, "layer_copies": copies,
+                   "launch": "hip graph" if graph is not None else "stream"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+"""The C-ABI library loads without a GPU, exports every function that
+include/vqd.h declares, and rejects invalid calls on the host before any
+HIP call (no compute runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vqd.h")
+
+vq = pytest.importorskip("vector_quantized_decode_amd",
+                         reason="libvqd.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(vq_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 14
+    lib = ctypes.CDLL(vq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(vq.EXPORTED) == names
+
+
+def test_status_strings():
+    assert vq.vq_status_str(0) == "VQ_OK"
+    for s in (-1, -2, -3, -4, -5):
+        assert vq.vq_status_str(s).startswith("VQ_E")
+    assert vq.vq_status_str(7) == "unknown"
+
+
+def test_device_layout_sizes():
+    assert vq.vq_wi_device_bytes(4096, 4096, 4, 8) == 4096 * 1024
+    assert vq.vq_wi_device_bytes(100, 1024, 4, 8) == 112 * 256      # rows padded to 16
+    assert vq.vq_wi_device_bytes(64, 1000, 4, 8) == 0                # J not a multiple of 64
+    assert vq.vq_signs_device_bytes(14336, 3584) == 14336 * 448
+    assert vq.vq_signs_device_bytes(100, 512) == 128 * 64            # rows padded to 32
+    assert vq.vq_alpha_device_bytes(3584, 14336, 128) == 3584 * 112 * 2
+    assert vq.vq_alpha_device_bytes(10, 256, 64) == 0
+
+
+FAKE = 0x7f0000000000   # never dereferenced: every call below fails validation first
+
+
+def _m(**kw):
+    a = dict(K=1024, N=64, d=4, nbits=8, wi=FAKE, wc=FAKE, signs=FAKE, alpha=FAKE,
+             group=128, rht_sign=None, had_block=0)
+    a.update(kw)
+    return vq.vq_matrix(**a)
+
+
+def _gemv(mats, xs, B, ys, ws, nbytes, residual=False):
+    f = vq._c["vq_gemv_residual" if residual else "vq_gemv"]
+    arr = (vq.vq_matrix * max(1, len(mats)))(*mats) if mats else None
+    xp = (ctypes.c_void_p * max(1, len(xs)))(*xs) if xs is not None else None
+    yp = (ctypes.c_void_p * max(1, len(ys)))(*ys) if ys is not None else None
+    return f(arr, len(mats), xp, B, yp, ws, nbytes, None)
+
+
+def test_gemv_validation_errors():
+    ok_x, ok_y = [FAKE], [FAKE]
+    assert _gemv([], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL                   # count 0
+    assert _gemv([_m()], None, 1, ok_y, None, 0) == vq.VQ_EINVAL               # x missing
+    assert _gemv([_m()], ok_x, 0, ok_y, None, 0) == vq.VQ_EINVAL               # B < 1
+    assert _gemv([_m(K=1022)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL         # K % d
+    assert _gemv([_m(d=3)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
+    assert _gemv([_m(nbits=17)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
+    assert _gemv([_m(wi=None)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
+    assert _gemv([_m(N=0)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
+    assert _gemv([_m(d=8, nbits=16)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED
+    assert _gemv([_m(K=1088)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # K % 256
+    assert _gemv([_m()], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED        # B = 2
+    assert _gemv([_m(wi=FAKE + 8)], ok_x, 1, ok_y, None, 0) == vq.VQ_EALIGN
+    assert _gemv([_m()], [FAKE + 2], 1, ok_y, None, 0) == vq.VQ_EALIGN
+    assert _gemv([_m()], ok_x, 1, [FAKE + 1], None, 0) == vq.VQ_EALIGN
+    need = vq.vq_workspace_bytes([_m()], 1)
+    assert need > 0
+    assert _gemv([_m()], ok_x, 1, ok_y, None, 0) == vq.VQ_EWORKSPACE
+    assert _gemv([_m()], ok_x, 1, ok_y, FAKE, need - 1) == vq.VQ_EWORKSPACE
+    assert _gemv([_m()], ok_x, 1, ok_y, FAKE + 16, need) == vq.VQ_EALIGN
+    assert _gemv([_m()] * 17, ok_x * 17, 1, ok_y * 17, FAKE, 1 << 30) == vq.VQ_EINVAL
+
+
+def test_gemv_residual_validation_errors():
+    ok_x, ok_y = [FAKE], [FAKE]
+    assert _gemv([_m(signs=None)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
+    assert _gemv([_m(group=64)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
+    assert _gemv([_m(rht_sign=FAKE, had_block=3)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
+    assert _gemv([_m(rht_sign=FAKE, had_block=2048)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
+    assert _gemv([_m(rht_sign=FAKE, had_block=1024)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EWORKSPACE
+    plain = vq.vq_workspace_bytes([_m()], 1)
+    res = vq.vq_workspace_bytes([_m()], 1, residual=True)
+    assert res >= plain + 1024 * 4
+
+
+def test_other_entry_points_validate():
+    c = vq._c
+    assert c["vq_pack_indices"](FAKE, 10, 0, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_pack_indices"](FAKE, 10, 17, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_pack_indices"](None, 10, 8, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_pack_indices"](FAKE + 1, 10, 8, FAKE, None) == vq.VQ_EALIGN
+    assert c["vq_pack_indices"](None, 0, 8, None, None) == vq.VQ_OK          # empty: nothing to do
+    assert c["vq_unpack_indices"](FAKE, -1, 8, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_unpack_indices"](FAKE, 5, 8, FAKE + 2, None) == vq.VQ_EALIGN
+    assert c["vq_repack_wi"](FAKE, 64, 1000, 4, 8, FAKE, None) == vq.VQ_EUNSUPPORTED
+    assert c["vq_repack_wi"](FAKE, 64, 1024, 4, 8, FAKE + 4, None) == vq.VQ_EALIGN
+    assert c["vq_repack_signs"](FAKE, 64, 1000, FAKE, None) == vq.VQ_EUNSUPPORTED
+    assert c["vq_repack_alpha"](FAKE, 64, 1024, 100, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_build_oc"](FAKE, 1, 10, 4, 8, FAKE, FAKE, vq.VQ_F32, None) == vq.VQ_EINVAL
+    assert c["vq_build_oc"](FAKE, 1, 16, 4, 8, FAKE, FAKE, 7, None) == vq.VQ_EINVAL
+    assert c["vq_build_oc"](FAKE, 1, 16, 4, 8, FAKE, FAKE + 2, vq.VQ_F32, None) == vq.VQ_EALIGN
+    assert c["vq_rht"](FAKE, FAKE, 1, 3584, 1024, FAKE, None) == vq.VQ_EINVAL  # 1024 does not divide
+    assert c["vq_rht"](FAKE, FAKE, 1, 1 << 15, 1 << 15, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_rht"](FAKE, None, 1, 1024, 1024, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_workspace_init"](FAKE + 8, 1024, None) == vq.VQ_EALIGN
+    assert c["vq_workspace_init"](None, 1024, None) == vq.VQ_EINVAL
+    assert c["vq_workspace_bytes"](None, 1, 1, 0) == 0

@@ -1,0 +1,285 @@
+"""GPU parity tests: the HIP library (through its C ABI) against the float64
+CPU oracle on the same seeded inputs.
+
+Bars: packing, unpacking and device layouts bit-exact; float outputs within
+relative L2 error 2e-3 and max error 1e-2 * rms(y) per matrix; the output
+codebook within relative L2 error 1e-3.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+import vector_quantized_decode_amd as vq  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _assert_close(y, y_ref, what):
+    rel, mx, rms = oracle.compare(y, y_ref)
+    _say(f"{what}: rel_l2={rel:.3e} max_err={mx:.3e} rms={rms:.3e}")
+    assert rel <= oracle.REL_L2_TOL, what
+    assert mx <= oracle.MAX_ERR_RMS_TOL * rms, what
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(DEV)
+
+
+# ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("nbits", [1, 3, 8, 12, 16])
+@pytest.mark.parametrize("count", [1, 5, 8, 1001, 65536 + 3])
+def test_pack_unpack_bitexact(nbits, count):
+    _say(f"pack nbits={nbits} count={count}")
+    rng = np.random.default_rng(nbits * 1000 + count)
+    idx = rng.integers(0, 1 << nbits, size=count).astype(np.uint32)
+    nbytes = (count * nbits + 7) // 8
+    out = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+    vq.vq_pack_indices(_i32(idx), count, nbits, out)
+    back = torch.zeros(count, dtype=torch.int32, device=DEV)
+    ref_packed = oracle.pack_bits(idx, nbits)
+    vq.vq_unpack_indices(torch.from_numpy(ref_packed).to(DEV), count, nbits, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref_packed)
+    assert np.array_equal(back.cpu().numpy().view(np.uint32), idx)
+
+
+def test_pack_hand_vectors_on_gpu():
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pack_vectors.json")))
+    for case in g["cases"]:
+        v = np.array(case["values"], dtype=np.uint32)
+        out = torch.zeros((v.size * case["nbits"] + 7) // 8, dtype=torch.uint8, device=DEV)
+        vq.vq_pack_indices(_i32(v), v.size, case["nbits"], out)
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes().hex() == case["bytes_hex"], case["note"]
+
+
+def _host_wi_layout(canon, N, J):
+    NG = (N + 15) // 16
+    out = np.zeros((J // 64, NG, 64, 16), dtype=np.uint8)
+    for r in range(N):
+        for j in range(J):
+            out[j // 64, r // 16, j % 64, r % 16] = canon[r, j]
+    return out.reshape(-1)
+
+
+def _host_sign_layout(canon, N, P):
+    NP = (N + 31) // 32
+    out = np.zeros((P // 32, NP, 2, 32, 16), dtype=np.uint8)
+    for r in range(N):
+        out[:, r // 32, (r % 32) // 16, :, r % 16] = canon[r].reshape(P // 32, 32)
+    return out.reshape(-1)
+
+
+def _host_alpha_layout(canon, N, G):
+    NP = (N + 31) // 32
+    out = np.zeros((G // 2, NP, 2, 2, 16), dtype=np.uint16)
+    for r in range(N):
+        for g in range(G):
+            out[g // 2, r // 32, (r % 32) // 16, g % 2, r % 16] = canon[r, g]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(16, 256), (100, 512), (33, 768)])
+def test_repack_layouts_bitexact(N, K):
+    _say(f"repack N={N} K={K}")
+    rng = np.random.default_rng(N + K)
+    J, P, G = K // 4, K // 8, K // 128
+    canon = rng.integers(0, 256, size=(N, J), dtype=np.uint8)
+    dev = torch.full((vq.vq_wi_device_bytes(N, K, 4, 8),), 0x5A, dtype=torch.uint8, device=DEV)
+    vq.vq_repack_wi(torch.from_numpy(canon).to(DEV), N, K, 4, 8, dev)
+    scanon = rng.integers(0, 256, size=(N, P), dtype=np.uint8)
+    sdev = torch.full((vq.vq_signs_device_bytes(N, K),), 0x5A, dtype=torch.uint8, device=DEV)
+    vq.vq_repack_signs(torch.from_numpy(scanon).to(DEV), N, K, sdev)
+    acanon = rng.integers(0, 65536, size=(N, G), dtype=np.uint16)
+    adev = torch.full((vq.vq_alpha_device_bytes(N, K, 128) // 2,), 7, dtype=torch.int16, device=DEV)
+    vq.vq_repack_alpha(torch.from_numpy(acanon.view(np.int16)).to(DEV), N, K, 128, adev)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.cpu().numpy(), _host_wi_layout(canon, N, J))
+    assert np.array_equal(sdev.cpu().numpy(), _host_sign_layout(scanon, N, P))
+    assert np.array_equal(adev.cpu().numpy().view(np.uint16), _host_alpha_layout(acanon, N, G))
+
+
+# ------------------------------------------------------------------ OC build
+@pytest.mark.parametrize("dtype", [vq.VQ_F32, vq.VQ_F16])
+@pytest.mark.parametrize("cfg,m", [(1, 0), (2, 1), (5, 0)])
+def test_build_oc_full(cfg, m, dtype):
+    _say(f"build_oc workload={cfg} matrix={m} dtype={dtype}")
+    mi = synth.matrix_inputs(cfg, m, rows=1)
+    B, K, d, n = mi.B, mi.K, mi.d, mi.nbits
+    J = K // d
+    oc = torch.empty((B * J, 1 << n), dtype=torch.float32 if dtype == vq.VQ_F32 else torch.float16,
+                     device=DEV)
+    vq.vq_build_oc(torch.from_numpy(mi.x).to(DEV), B, K, d, n,
+                   torch.from_numpy(mi.wc).to(DEV), oc, dtype)
+    torch.cuda.synchronize()
+    ref = oracle.output_codebook(mi.x, mi.wc, d).reshape(B * J, 1 << n)
+    got = oc.float().cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    _say(f"  rel_l2={rel:.3e}")
+    assert rel <= 1e-3
+
+
+def test_build_oc_sampled_16bit_codebook():
+    # 16 tokens x 5120 inputs, d=8, n=16: OC is 10240 x 65536 (fp16, 1.34 GB)
+    _say("build_oc workload=4 matrix=0 fp16 sampled rows")
+    mi = synth.matrix_inputs(4, 0, rows=1)
+    B, K, d, n = mi.B, mi.K, mi.d, mi.nbits
+    J = K // d
+    oc = torch.empty((B * J, 1 << n), dtype=torch.float16, device=DEV)
+    vq.vq_build_oc(torch.from_numpy(mi.x).to(DEV), B, K, d, n,
+                   torch.from_numpy(mi.wc).to(DEV), oc, vq.VQ_F16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    rows = np.sort(rng.choice(B * J, size=64, replace=False))
+    got = oc[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    del oc
+    xr = mi.x.astype(np.float64).reshape(B * J, d)[rows]
+    ref = xr @ mi.wc.astype(np.float64).T
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    _say(f"  rel_l2={rel:.3e}")
+    assert rel <= 1e-3
+
+
+# ------------------------------------------------------------------ rotation
+@pytest.mark.parametrize("K,h,B", [(3584, 512, 1), (14336, 2048, 1), (1024, 1024, 3), (256, 1, 1),
+                                   (8192, 8192, 1)])
+def test_rht_matches_oracle(K, h, B):
+    _say(f"rht K={K} h={h} B={B}")
+    rng = np.random.default_rng(K + h)
+    x = rng.standard_normal((B, K)).astype(np.float16)
+    s = np.where(rng.integers(0, 2, K) == 1, 1, -1).astype(np.int8)
+    out = torch.empty((B, K), dtype=torch.float32, device=DEV)
+    vq.vq_rht(torch.from_numpy(x).to(DEV), torch.from_numpy(s).to(DEV), B, K, h, out)
+    torch.cuda.synchronize()
+    ref = oracle.rht(x, s, h)
+    err = np.abs(out.cpu().numpy() - ref).max()
+    _say(f"  max_err={err:.3e}")
+    assert err <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+# ------------------------------------------------------------------ VQ GEMV
+def _upload(mi, residual=False):
+    if residual:
+        return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
+                                sign_bits=mi.sign_bits, alpha=mi.alpha, group=mi.group,
+                                rht_sign=mi.rht_sign, had_block=mi.had_block, device=DEV)
+    return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, device=DEV)
+
+
+def _run_gemv(mats, xs, B=1, residual=False):
+    ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
+    ws = vq.alloc_workspace(mats, B, residual=residual, device=DEV)
+    xt = [torch.from_numpy(x).to(DEV) for x in xs]
+    fn = vq.vq_gemv_residual if residual else vq.vq_gemv
+    fn(mats, xt, B, ys, ws, ws.numel())
+    torch.cuda.synchronize()
+    return [y.cpu().numpy() for y in ys], (mats, xt, ys, ws)
+
+
+def _oracle_plain(mi, rows=None):
+    idx = mi.idx if rows is None else mi.idx[rows]
+    return oracle.vq_gemv(mi.x, mi.wc, oracle.pack_rows(idx, mi.nbits), idx.shape[0], mi.K,
+                          mi.d, mi.nbits)
+
+
+def _oracle_res(mi, rows=None, rotate=True):
+    sel = slice(None) if rows is None else rows
+    idx, bits, alpha = mi.idx[sel], mi.sign_bits[sel], mi.alpha[sel]
+    return oracle.vq_gemv_residual(mi.x, mi.wc, oracle.pack_rows(idx, 8),
+                                   oracle.pack_rows(bits, 1), alpha,
+                                   mi.rht_sign if rotate else None, mi.had_block,
+                                   idx.shape[0], mi.K, mi.d, mi.nbits, mi.group)
+
+
+def test_gemv_workload1_single_matrix():
+    _say("gemv workload 1 (512x512)")
+    mi = synth.matrix_inputs(1, 0)
+    (y,), _ = _run_gemv([_upload(mi)], [mi.x])
+    _assert_close(y, _oracle_plain(mi), "workload1")
+
+
+@pytest.mark.parametrize("K,N", [(256, 1), (256, 17), (512, 100), (768, 333), (1024, 4103),
+                                 (2048, 48), (4096, 513)])
+def test_gemv_shapes_with_ragged_rows(K, N):
+    _say(f"gemv K={K} N={N}")
+    mi = synth.small_matrix(K, N, 4, 8, seed=K + N)
+    (y,), _ = _run_gemv([_upload(mi)], [mi.x])
+    _assert_close(y, _oracle_plain(mi), f"K={K} N={N}")
+
+
+def test_gemv_workload2_grouped_and_deterministic():
+    _say("gemv workload 2 (4 x 4096x4096, one launch)")
+    mis = [synth.matrix_inputs(2, m) for m in range(4)]
+    mats = [_upload(mi) for mi in mis]
+    ys, keep = _run_gemv(mats, [mi.x for mi in mis])
+    for m, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _oracle_plain(mi), f"workload2 matrix {m}")
+    # bitwise reproducible, and the same per matrix whether grouped or not
+    ys2, _ = _run_gemv(mats, [mi.x for mi in mis])
+    for a, b in zip(ys, ys2):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    (y1,), _ = _run_gemv([mats[2]], [mis[2].x])
+    assert np.array_equal(y1.view(np.uint32), ys[2].view(np.uint32))
+
+
+def test_gemv_mixed_group():
+    _say("gemv mixed shapes in one launch")
+    mis = [synth.small_matrix(1024, 300, 4, 8, seed=1), synth.small_matrix(512, 2000, 4, 8, seed=2),
+           synth.small_matrix(2304, 64, 4, 8, seed=3)]
+    ys, _ = _run_gemv([_upload(mi) for mi in mis], [mi.x for mi in mis])
+    for i, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _oracle_plain(mi), f"mixed {i}")
+
+
+def test_workspace_reused_across_calls():
+    _say("workspace reuse: counters left ready")
+    mi = synth.small_matrix(2048, 1500, 4, 8, seed=9)
+    m = _upload(mi)
+    ys, (mats, xt, yt, ws) = _run_gemv([m], [mi.x])
+    ref = _oracle_plain(mi)
+    for _ in range(3):
+        vq.vq_gemv(mats, xt, 1, yt, ws, ws.numel())
+    torch.cuda.synchronize()
+    _assert_close(yt[0].cpu().numpy(), ref, "after reuse")
+    assert np.array_equal(yt[0].cpu().numpy().view(np.uint32), ys[0].view(np.uint32))
+
+
+# ------------------------------------------------------------------ residual
+@pytest.mark.parametrize("K,N,rotate", [(256, 40, True), (1024, 200, True), (1024, 200, False),
+                                        (3584, 300, True), (2048, 1031, True)])
+def test_gemv_residual_shapes(K, N, rotate):
+    _say(f"gemv_residual K={K} N={N} rotate={rotate}")
+    mi = synth.small_matrix(K, N, 4, 8, seed=K * 7 + N, residual=True)
+    m = _upload(mi, residual=True)
+    if not rotate:
+        m.rht_sign = None
+    (y,), _ = _run_gemv([m], [mi.x], residual=True)
+    _assert_close(y, _oracle_res(mi, rotate=rotate), f"residual K={K} N={N}")
+
+
+def test_gemv_residual_workload5_sampled_rows():
+    _say("gemv_residual workload 5 (3584->14336, 14336->3584), sampled rows")
+    mis = [synth.matrix_inputs(5, m) for m in range(2)]
+    mats = [_upload(mi, residual=True) for mi in mis]
+    ys, _ = _run_gemv(mats, [mi.x for mi in mis], residual=True)
+    rng = np.random.default_rng(5)
+    for m, (mi, y) in enumerate(zip(mis, ys)):
+        rows = np.unique(np.concatenate([np.arange(64), rng.choice(mi.N, 192, replace=False),
+                                         np.arange(mi.N - 32, mi.N)]))
+        _assert_close(y[:, rows], _oracle_res(mi, rows=rows), f"workload5 matrix {m} sampled")

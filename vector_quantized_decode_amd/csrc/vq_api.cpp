@@ -1,0 +1,312 @@
+// Host side of libvqd: argument validation, variant selection, workspace
+// layout and kernel launches behind the C ABI of include/vqd.h.
+//
+// Every entry point validates all of its arguments before it enqueues
+// anything; validation touches no HIP API, so an invalid call returns its
+// status even on a machine without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "vq_internal.h"
+
+namespace vqd {
+
+static bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+static bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- shapes
+Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count) {
+  bool all128 = true;
+  int64_t max_n = 0, work = 0;
+  for (int i = 0; i < count; ++i) {
+    const int J = m[i].K / m[i].d;
+    if (J % 128) all128 = false;
+    if (m[i].N > max_n) max_n = m[i].N;
+    work += (int64_t)m[i].N * J;
+  }
+  Lut8Shape s;
+  s.nsub = all128 ? 2 : 1;
+  if (work <= (int64_t)1 << 20) {   // small layers: more, smaller workgroups
+    s.waves = 4;
+    s.steps = 1;
+  } else {
+    s.waves = 16;
+    s.steps = 2;
+  }
+  (void)max_n;
+  return s;
+}
+
+Lut8Shape lut8_shape_residual(const vq_matrix *, int32_t) {
+  Lut8Shape s;
+  s.nsub = 1;
+  s.waves = 16;
+  s.steps = 1;
+  return s;
+}
+
+// ---------------------------------------------------------------- workspace
+struct MatPlan {
+  int J, nsplit, nrb, rows_pad;
+  size_t partial_off, counter_off, xrot_off;
+};
+
+struct Plan {
+  Lut8Shape shape;
+  MatPlan mp[VQ_MAX_GROUP];
+  size_t bytes;
+  int64_t grid;
+};
+
+static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residual, Plan &p) {
+  p.shape = residual ? lut8_shape_residual(m, count) : lut8_shape_plain(m, count);
+  const int R = residual ? p.shape.rows_res() : p.shape.rows();
+  const int JT = residual ? 64 : p.shape.jt();
+  size_t off = 0;
+  // counters first (zeroed by vq_workspace_init), then partials, then x_rot
+  for (int i = 0; i < count; ++i) {
+    MatPlan &q = p.mp[i];
+    q.J = m[i].K / m[i].d;
+    q.nsplit = (q.J + JT - 1) / JT;
+    q.nrb = (m[i].N + R - 1) / R;
+    q.rows_pad = (m[i].N + 31) / 32 * 32;
+    q.counter_off = off;
+    off += round_up((size_t)q.nrb * sizeof(uint32_t), 256);
+  }
+  p.grid = 0;
+  for (int i = 0; i < count; ++i) {
+    MatPlan &q = p.mp[i];
+    q.partial_off = off;
+    if (q.nsplit > 1) off += round_up((size_t)q.nsplit * q.rows_pad * sizeof(float), 256);
+    p.grid += (int64_t)q.nsplit * q.nrb;
+  }
+  for (int i = 0; i < count; ++i) {
+    MatPlan &q = p.mp[i];
+    q.xrot_off = off;
+    if (residual) off += round_up((size_t)B * m[i].K * sizeof(float), 256);
+  }
+  p.bytes = off;
+}
+
+// ---------------------------------------------------------------- validation
+static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
+  if (a.K <= 0 || a.N <= 0) return VQ_EINVAL;
+  if (!(a.d == 1 || a.d == 2 || a.d == 4 || a.d == 8)) return VQ_EINVAL;
+  if (a.nbits < 1 || a.nbits > 16) return VQ_EINVAL;
+  if (a.K % a.d) return VQ_EINVAL;
+  if (!a.wi || !a.wc) return VQ_EINVAL;
+  if ((int64_t)a.N * (a.K / a.d) > ((int64_t)1 << 40)) return VQ_EINVAL;
+  if (residual) {
+    if (!a.signs || !a.alpha) return VQ_EINVAL;
+    if (a.group != 128) return VQ_EUNSUPPORTED;
+    if (a.rht_sign) {
+      if (!is_pow2(a.had_block) || a.had_block > 16384 || a.K % a.had_block) return VQ_EINVAL;
+    }
+  }
+  if (!(a.d == 4 && a.nbits == 8)) return VQ_EUNSUPPORTED;
+  if (a.K % 256) return VQ_EUNSUPPORTED;
+  if (B != 1) return VQ_EUNSUPPORTED;
+  if (!aligned(a.wi, 16) || !aligned(a.wc, 16)) return VQ_EALIGN;
+  if (residual && (!aligned(a.signs, 16) || !aligned(a.alpha, 32))) return VQ_EALIGN;
+  return VQ_OK;
+}
+
+static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                       float *const *y, bool residual) {
+  if (!m || !x || !y) return VQ_EINVAL;
+  if (count < 1 || count > VQ_MAX_GROUP) return VQ_EINVAL;
+  if (B < 1) return VQ_EINVAL;
+  for (int i = 0; i < count; ++i) {
+    const int st = check_matrix(m[i], B, residual);
+    if (st != VQ_OK) return st;
+    if (!x[i] || !y[i]) return VQ_EINVAL;
+    if (!aligned(x[i], 16)) return VQ_EALIGN;
+    if (!aligned(y[i], 4)) return VQ_EALIGN;
+  }
+  return VQ_OK;
+}
+
+static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                       float *const *y, void *workspace, size_t ws_bytes, void *stream, bool residual) {
+  int st = check_group(m, count, x, B, y, residual);
+  if (st != VQ_OK) return st;
+  Plan p;
+  make_plan(m, count, B, residual, p);
+  if (p.grid > 0x7fffffff) return VQ_EUNSUPPORTED;
+  if (p.bytes > 0) {
+    if (!workspace || ws_bytes < p.bytes) return VQ_EWORKSPACE;
+    if (!aligned(workspace, 256)) return VQ_EALIGN;
+  }
+  char *ws = static_cast<char *>(workspace);
+  Lut8Args args;
+  memset(&args, 0, sizeof(args));
+  args.count = count;
+  int wg = 0;
+  for (int i = 0; i < count; ++i) {
+    const MatPlan &q = p.mp[i];
+    Lut8Mat &d = args.mat[i];
+    d.wi = static_cast<const uint8_t *>(m[i].wi);
+    d.wc = m[i].wc;
+    d.x = x[i];
+    d.xr = residual ? reinterpret_cast<const float *>(ws + q.xrot_off) : nullptr;
+    d.signs = residual ? static_cast<const uint8_t *>(m[i].signs) : nullptr;
+    d.alpha = residual ? static_cast<const uint16_t *>(m[i].alpha) : nullptr;
+    d.y = y[i];
+    d.partial = q.nsplit > 1 ? reinterpret_cast<float *>(ws + q.partial_off) : nullptr;
+    d.counter = reinterpret_cast<uint32_t *>(ws + q.counter_off);
+    d.J = q.J;
+    d.N = m[i].N;
+    d.rows_pad = q.rows_pad;
+    d.nsplit = q.nsplit;
+    d.nrb = q.nrb;
+    d.wg_begin = wg;
+    wg += q.nsplit * q.nrb;
+  }
+  int err;
+  if (residual) {
+    for (int i = 0; i < count; ++i) {
+      const int h = m[i].rht_sign ? m[i].had_block : 1;
+      const float scale = (float)(1.0 / sqrt((double)h));
+      err = launch_rht(x[i], m[i].rht_sign, B, m[i].K, h, scale,
+                       reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);
+      if (err) return VQ_EHIP;
+    }
+    err = launch_lut8_residual(args, p.shape, (int)p.grid, stream);
+  } else {
+    err = launch_lut8_plain(args, p.shape, (int)p.grid, stream);
+  }
+  return err ? VQ_EHIP : VQ_OK;
+}
+
+}  // namespace vqd
+
+using namespace vqd;
+
+extern "C" {
+
+const char *vq_status_str(int status) {
+  switch (status) {
+    case VQ_OK: return "VQ_OK";
+    case VQ_EINVAL: return "VQ_EINVAL: invalid argument";
+    case VQ_EUNSUPPORTED: return "VQ_EUNSUPPORTED: shape or format not supported";
+    case VQ_EALIGN: return "VQ_EALIGN: pointer misaligned";
+    case VQ_EWORKSPACE: return "VQ_EWORKSPACE: workspace missing or too small";
+    case VQ_EHIP: return "VQ_EHIP: HIP runtime error";
+    default: return "unknown";
+  }
+}
+
+size_t vq_wi_device_bytes(int32_t N, int32_t K, int32_t d, int32_t nbits) {
+  if (N <= 0 || K <= 0 || d <= 0 || K % d) return 0;
+  if (nbits != 8) return 0;
+  const int64_t J = K / d;
+  if (J % 64) return 0;
+  return (size_t)((N + 15) / 16) * 16 * (size_t)J;
+}
+
+size_t vq_signs_device_bytes(int32_t N, int32_t K) {
+  if (N <= 0 || K <= 0 || K % 256) return 0;
+  return (size_t)((N + 31) / 32) * 32 * (size_t)(K / 8);
+}
+
+size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group) {
+  if (N <= 0 || K <= 0 || group != 128 || K % 256) return 0;
+  const size_t G = (size_t)(K / group);
+  return (size_t)((N + 31) / 32) * 32 * ((G + 1) / 2 * 2) * sizeof(uint16_t);
+}
+
+size_t vq_workspace_bytes(const vq_matrix *m, int32_t count, int32_t B, int32_t residual) {
+  if (!m || count < 1 || count > VQ_MAX_GROUP || B < 1) return 0;
+  for (int i = 0; i < count; ++i) {
+    const vq_matrix &a = m[i];
+    if (a.K <= 0 || a.N <= 0 || a.d <= 0 || a.K % a.d) return 0;
+  }
+  Plan p;
+  make_plan(m, count, B, residual != 0, p);
+  return p.bytes;
+}
+
+int vq_workspace_init(void *workspace, size_t ws_bytes, void *stream) {
+  if (ws_bytes == 0) return VQ_OK;
+  if (!workspace) return VQ_EINVAL;
+  if (!aligned(workspace, 256)) return VQ_EALIGN;
+  return launch_fill_u32(static_cast<uint32_t *>(workspace), ws_bytes / 4, 0u, stream) ? VQ_EHIP : VQ_OK;
+}
+
+int vq_pack_indices(const uint32_t *idx, int64_t count, int32_t nbits, uint8_t *out, void *stream) {
+  if (nbits < 1 || nbits > 16 || count < 0) return VQ_EINVAL;
+  if (count == 0) return VQ_OK;
+  if (!idx || !out) return VQ_EINVAL;
+  if (!aligned(idx, 4)) return VQ_EALIGN;
+  return launch_pack(idx, count, nbits, out, stream) ? VQ_EHIP : VQ_OK;
+}
+
+int vq_unpack_indices(const uint8_t *packed, int64_t count, int32_t nbits, uint32_t *out, void *stream) {
+  if (nbits < 1 || nbits > 16 || count < 0) return VQ_EINVAL;
+  if (count == 0) return VQ_OK;
+  if (!packed || !out) return VQ_EINVAL;
+  if (!aligned(out, 4)) return VQ_EALIGN;
+  return launch_unpack(packed, count, nbits, out, stream) ? VQ_EHIP : VQ_OK;
+}
+
+int vq_repack_wi(const uint8_t *canonical, int32_t N, int32_t K, int32_t d, int32_t nbits,
+                 void *device_layout, void *stream) {
+  if (!canonical || !device_layout) return VQ_EINVAL;
+  if (N <= 0 || K <= 0 || d <= 0 || K % d || nbits < 1 || nbits > 16) return VQ_EINVAL;
+  if (vq_wi_device_bytes(N, K, d, nbits) == 0) return VQ_EUNSUPPORTED;
+  if (!aligned(device_layout, 16)) return VQ_EALIGN;
+  return launch_repack_wi8(canonical, N, K / d, static_cast<uint8_t *>(device_layout), stream) ? VQ_EHIP
+                                                                                               : VQ_OK;
+}
+
+int vq_repack_signs(const uint8_t *canonical, int32_t N, int32_t K, void *device_layout, void *stream) {
+  if (!canonical || !device_layout || N <= 0 || K <= 0 || K % 8) return VQ_EINVAL;
+  if (vq_signs_device_bytes(N, K) == 0) return VQ_EUNSUPPORTED;
+  if (!aligned(device_layout, 16)) return VQ_EALIGN;
+  return launch_repack_signs(canonical, N, K / 8, static_cast<uint8_t *>(device_layout), stream) ? VQ_EHIP
+                                                                                                  : VQ_OK;
+}
+
+int vq_repack_alpha(const uint16_t *canonical, int32_t N, int32_t K, int32_t group, void *device_layout,
+                    void *stream) {
+  if (!canonical || !device_layout || N <= 0 || K <= 0 || group <= 0 || K % group) return VQ_EINVAL;
+  if (vq_alpha_device_bytes(N, K, group) == 0) return VQ_EUNSUPPORTED;
+  if (!aligned(canonical, 2) || !aligned(device_layout, 32)) return VQ_EALIGN;
+  return launch_repack_alpha(canonical, N, K / group, static_cast<uint16_t *>(device_layout), stream)
+             ? VQ_EHIP
+             : VQ_OK;
+}
+
+int vq_build_oc(const uint16_t *x, int32_t B, int32_t K, int32_t d, int32_t nbits, const uint16_t *wc,
+                void *oc, vq_dtype oc_dtype, void *stream) {
+  if (!x || !wc || !oc) return VQ_EINVAL;
+  if (B < 1 || K <= 0 || !(d == 1 || d == 2 || d == 4 || d == 8) || K % d) return VQ_EINVAL;
+  if (nbits < 1 || nbits > 16) return VQ_EINVAL;
+  if (oc_dtype != VQ_F16 && oc_dtype != VQ_F32) return VQ_EINVAL;
+  if ((int64_t)B * (K / d) > ((int64_t)1 << 40) >> nbits) return VQ_EINVAL;
+  if (!aligned(x, 2) || !aligned(wc, 2) || !aligned(oc, oc_dtype == VQ_F32 ? 4 : 2)) return VQ_EALIGN;
+  return launch_build_oc(x, B, K, d, nbits, wc, oc, oc_dtype == VQ_F16, stream) ? VQ_EHIP : VQ_OK;
+}
+
+int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K, int32_t had_block, float *x_rot,
+           void *stream) {
+  if (!x || !sign || !x_rot) return VQ_EINVAL;
+  if (B < 1 || K <= 0 || !is_pow2(had_block) || had_block > 16384 || K % had_block) return VQ_EINVAL;
+  if ((int64_t)B * (K / had_block) > 0x7fffffff) return VQ_EINVAL;
+  if (!aligned(x, 2) || !aligned(x_rot, 4)) return VQ_EALIGN;
+  const float scale = (float)(1.0 / sqrt((double)had_block));
+  return launch_rht(x, sign, B, K, had_block, scale, x_rot, stream) ? VQ_EHIP : VQ_OK;
+}
+
+int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B, float *const *y,
+            void *workspace, size_t ws_bytes, void *stream) {
+  return gemv_common(m, count, x, B, y, workspace, ws_bytes, stream, false);
+}
+
+int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                     float *const *y, void *workspace, size_t ws_bytes, void *stream) {
+  return gemv_common(m, count, x, B, y, workspace, ws_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the host API (vq_api.cpp) and the HIP
+// kernels (vq_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/vqd.h"
+
+namespace vqd {
+
+// Per-matrix descriptor of the 8-bit lookup GEMV kernels.  Lives in the
+// kernel-argument segment; all pointers are device pointers.
+struct Lut8Mat {
+  const uint8_t *wi;      // WI, device layout tile-16x64
+  const uint16_t *wc;     // fp16 codebook [256][4]
+  const uint16_t *x;      // fp16 input [K] (plain kernel)
+  const float *xr;        // fp32 rotated input [K] (residual kernel)
+  const uint8_t *signs;   // sign bits, device layout tile-32x32 (residual)
+  const uint16_t *alpha;  // fp16 scales, device layout (residual)
+  float *y;               // fp32 output [N]
+  float *partial;         // fp32 split partial sums [nsplit][rows_pad]
+  uint32_t *counter;      // completion counters [nrb]
+  int32_t J;              // subvectors per row, K/4
+  int32_t N;              // output rows
+  int32_t rows_pad;       // rows of the padded layout (multiple of 32)
+  int32_t nsplit;         // workgroups sharing a row block (split along J)
+  int32_t nrb;            // row blocks
+  int32_t wg_begin;       // first workgroup id of this matrix in the grid
+};
+
+struct Lut8Args {
+  Lut8Mat mat[VQ_MAX_GROUP];
+  int32_t count;
+};
+
+// Launch shape of one lookup-kernel variant.
+struct Lut8Shape {
+  int nsub;     // 64-subvector tiles per workgroup (1 or 2)
+  int waves;    // wavefronts per workgroup
+  int steps;    // row steps per wave (16 rows each, 32 for the residual kernel)
+  int rows() const { return waves * steps * 16; }
+  int rows_res() const { return waves * steps * 32; }
+  int jt() const { return 64 * nsub; }
+};
+
+// Variant selection (shared by workspace sizing and launch).
+Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count);
+Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count);
+
+// Kernel launchers: return a hipError_t value (0 = success).
+int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream);
+int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream);
+int launch_pack(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, void *stream);
+int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out, void *stream);
+int launch_repack_wi8(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
+int launch_repack_signs(const uint8_t *canon, int N, int P, uint8_t *dev, void *stream);
+int launch_repack_alpha(const uint16_t *canon, int N, int G, uint16_t *dev, void *stream);
+int launch_build_oc(const uint16_t *x, int B, int K, int d, int nbits, const uint16_t *wc,
+                    void *oc, int f16_out, void *stream);
+int launch_rht(const uint16_t *x, const int8_t *sign, int B, int K, int h, float scale,
+               float *x_rot, void *stream);
+int launch_fill_u32(uint32_t *p, size_t n, uint32_t v, void *stream);
+
+}  // namespace vqd

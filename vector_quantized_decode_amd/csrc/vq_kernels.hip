@@ -1,0 +1,642 @@
+// HIP kernels of libvqd for gfx950 (CDNA4, wave64).
+//
+// Sources, cited by page title and section:
+//   [EVA]  "EVA: Accelerating LLM Decoding via an Efficient Vector
+//          Quantization Architecture" -- explainer page, technical summary,
+//          sections 2.A (input-codebook products form the output codebook OC;
+//          lookups into OC are arranged so that simultaneous accesses fall in
+//          different memory banks) and 2.B (an epilogue unit performs the
+//          lookups and sums them with adder trees; the codebooks stay on chip
+//          while indices stream in tiles).
+//   [EDGE] "Replacing MatMul with SRAM lookup: a 3-bit edge inference
+//          architecture" -- article page, section details (randomized
+//          Hadamard rotation, 1-bit sign residual with one fp16 scale per
+//          group of 128 weights, LUT inference with bit operations).
+//
+// How the lookup GEMV maps onto a CDNA4 compute unit (d = 4, n = 8, B = 1):
+//   * A workgroup owns a tile of 64*NSUB subvectors (j) and a block of rows.
+//     It builds the OC tile for its subvectors in LDS, fp32, laid out as
+//     word((s*256 + c)*64 + l) for subvector j = 64 s + l and centroid c, so
+//     the LDS bank of an entry depends only on l.  Lane l of every wavefront
+//     always works on subvector l: the 64 lanes of one LDS read hit 64
+//     different banks whatever the indices are -- the conflict-free lookup
+//     of [EVA 2.A] expressed as a bank layout.
+//   * Indices stream from HBM in 1 KiB chunks (16 rows x 64 subvectors, one
+//     16-byte load per lane, fully coalesced), read once.
+//   * One v_perm_b32 turns an index byte into the LDS byte address
+//     (lane*4 | c<<8 | region<<16): one VALU op, one LDS read and one add per
+//     lookup.
+//   * Each lane accumulates 16 rows; the cross-lane "adder tree" of
+//     [EVA 2.B] is a transposing butterfly built from gfx950 permlane swaps
+//     and DPP moves that leaves row r of the 16 in lanes 4r..4r+3.
+//   * Workgroups that share a row block (a split along J) write fp32 partial
+//     sums; the last one to finish (an atomic counter) adds them in fixed
+//     split order and writes y, so results are bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include "vq_internal.h"
+
+namespace vqd {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+__device__ __forceinline__ float lds_at(const float *base, uint32_t byte_addr) {
+  return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + byte_addr);
+}
+
+// DPP controls (GCN/CDNA encoding)
+constexpr int DPP_QUAD_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_ROR8 = 0x128;        // rotate a 16-lane row by 8 == lane ^ 8
+constexpr int DPP_ROW_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), CTRL, 0xF, 0xF, false));
+}
+
+// Swap the upper 32 lanes of a with the lower 32 lanes of b.
+__device__ __forceinline__ void swap32(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(as_u(a), as_u(b), false, false);
+  a = as_f(r[0]);
+  b = as_f(r[1]);
+}
+// Swap the odd 16-lane rows of a with the even 16-lane rows of b.
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(as_u(a), as_u(b), false, false);
+  a = as_f(r[0]);
+  b = as_f(r[1]);
+}
+
+// Transposing stage over a lane bit handled by a DPP move: lanes with the bit
+// clear keep `lo` and receive the partner's `lo`; lanes with it set keep `hi`.
+template <int CTRL>
+__device__ __forceinline__ float tstage(float lo, float hi, bool bit) {
+  float send = bit ? lo : hi;
+  float keep = bit ? hi : lo;
+  return keep + dpp<CTRL>(send);
+}
+
+// a[0..15] hold per-lane partial sums of rows 0..15.  Returns the full sum
+// over the 64 lanes of row (lane >> 2) & 15 in every lane.
+__device__ __forceinline__ float reduce_rows16(float (&a)[16], int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { swap32(a[i], a[i + 8]); a[i] += a[i + 8]; }
+  // a[i], i < 8: row i + 8*bit5
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { swap16(a[i], a[i + 4]); a[i] += a[i + 4]; }
+  // a[i], i < 4: row i + 4*bit4 + 8*bit5
+  const bool b3 = lane & 8, b2 = lane & 4;
+  a[0] = tstage<DPP_ROW_ROR8>(a[0], a[2], b3);
+  a[1] = tstage<DPP_ROW_ROR8>(a[1], a[3], b3);
+  // a[i], i < 2: row i + 2*bit3 + 4*bit4 + 8*bit5
+  float v = tstage<DPP_ROW_HALF_MIRROR>(a[0], a[1], b2);
+  // v: row bit2 + 2*bit3 + ..., partial over lanes {i, 7-i} of each 8 lanes
+  v += dpp<DPP_QUAD_XOR1>(v);
+  v += dpp<DPP_QUAD_XOR2>(v);
+  return v;
+}
+
+// Rows 0..15 in A, rows 16..31 in Bv, and S holding sign-residual partials
+// of rows 0..15 in lanes 0..31 and rows 16..31 in lanes 32..63.  Returns the
+// full sum of row (lane >> 1) & 31 in every lane.
+__device__ __forceinline__ float reduce_rows32(float (&A)[16], float (&Bv)[16], const float (&S)[16],
+                                               int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { swap32(A[i], Bv[i]); A[i] = A[i] + Bv[i] + S[i]; }
+  // A[i]: row i + 16*bit5
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { swap16(A[i], A[i + 8]); A[i] += A[i + 8]; }
+  // A[i], i < 8: row i + 8*bit4 + 16*bit5
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) A[i] = tstage<DPP_ROW_ROR8>(A[i], A[i + 4], b3);
+  // A[i], i < 4: row i + 4*bit3 + ...
+#pragma unroll
+  for (int i = 0; i < 2; ++i) A[i] = tstage<DPP_ROW_HALF_MIRROR>(A[i], A[i + 2], b2);
+  // A[i], i < 2: row i + 2*bit2 + ...; partial over {i, 7-i}
+  float v = tstage<DPP_QUAD_XOR2>(A[0], A[1], b1);
+  // v: row bit1 + 2*bit2 + ...; partial over {i, 7-i, i^2, 7-(i^2)}
+  v += dpp<DPP_QUAD_XOR1>(v);
+  return v;
+}
+
+// byte k of w -> LDS byte address: byte0 from base (lane*4), byte1 = index,
+// byte2 from base (64 KiB region), byte3 = 0.
+template <int K>
+__device__ __forceinline__ uint32_t lut_addr(uint32_t w, uint32_t base) {
+  return __builtin_amdgcn_perm(w, base, 0x0C020000u | ((4u + K) << 8));
+}
+
+__device__ __forceinline__ int locate_matrix(const Lut8Args &args) {
+  int mi = 0;
+  for (int i = 1; i < args.count; ++i)
+    if ((int)blockIdx.x >= args.mat[i].wg_begin) mi = i;
+  return mi;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint8_t *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Last workgroup of a row block adds the split partials in fixed order.
+__device__ __forceinline__ void split_finish(const Lut8Mat &M, int rb, int R, uint32_t *flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = atomicAdd(&M.counter[rb], 1u);
+    *flag = (prev == (uint32_t)(M.nsplit - 1)) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*flag == 0u) return;
+  __threadfence();
+  for (int t = threadIdx.x; t < R; t += blockDim.x) {
+    const int row = rb * R + t;
+    if (row < M.N) {
+      float s = 0.f;
+      for (int q = 0; q < M.nsplit; ++q) s += M.partial[(size_t)q * M.rows_pad + row];
+      M.y[row] = s;
+    }
+  }
+  if (threadIdx.x == 0) M.counter[rb] = 0u;
+}
+
+// --------------------------------------------------------------------------
+// Plain lookup GEMV: y[r] = sum_j OC[j, WI[r, j]]   [EVA 2.A, 2.B]
+// --------------------------------------------------------------------------
+template <int NSUB, int W, int STEPS>
+__global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args) {
+  __shared__ float lds[NSUB * 16384 + 16];
+  uint32_t *flag = reinterpret_cast<uint32_t *>(lds + NSUB * 16384);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Lut8Mat &M = args.mat[locate_matrix(args)];
+  const int local = blockIdx.x - M.wg_begin;
+  const int sp = local % M.nsplit, rb = local / M.nsplit;
+  const int jtiles = M.J >> 6;
+  const int NG = (M.N + 15) >> 4;
+
+  // 1. issue every index load of this workgroup up front
+  u32x4 v[STEPS][NSUB];
+#pragma unroll
+  for (int g = 0; g < STEPS; ++g) {
+    const int rg = (rb * STEPS + g) * W + wave;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int jt = sp * NSUB + s;
+      if (rg < NG && jt < jtiles)
+        v[g][s] = load16(M.wi + (((size_t)jt * NG + rg) * 64 + lane) * 16);
+      else
+        v[g][s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // 2. output-codebook tile: OC[j][c] = x_j . WC[c], fp16 products summed in fp32
+  {
+    constexpr int CB = W / NSUB;
+    constexpr int CPB = 256 / CB;
+    const int s = wave % NSUB, cb = wave / NSUB;
+    const int j = sp * 64 * NSUB + s * 64 + lane;
+    uint2 xv = make_uint2(0u, 0u);
+    if (j < M.J) xv = *reinterpret_cast<const uint2 *>(M.x + 4 * (size_t)j);
+    const uint32_t *wc32 = reinterpret_cast<const uint32_t *>(M.wc);
+    float *dst = lds + (s * 256 + cb * CPB) * 64 + lane;
+#pragma unroll 8
+    for (int i = 0; i < CPB; ++i) {
+      const int c = cb * CPB + i;
+      const uint32_t w0 = wc32[2 * c], w1 = wc32[2 * c + 1];
+      float o = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(w0), 0.f, false);
+      o = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(w1), o, false);
+      dst[i * 64] = o;
+    }
+  }
+  __syncthreads();
+
+  // 3. conflict-free lookups and the cross-lane adder tree
+  const uint32_t base0 = (uint32_t)lane << 2;
+  float rowval[STEPS];
+#pragma unroll
+  for (int g = 0; g < STEPS; ++g) {
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const uint32_t base = base0 | ((uint32_t)s << 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = v[g][s][q];
+        acc[4 * q + 0] += lds_at(lds, lut_addr<0>(w, base));
+        acc[4 * q + 1] += lds_at(lds, lut_addr<1>(w, base));
+        acc[4 * q + 2] += lds_at(lds, lut_addr<2>(w, base));
+        acc[4 * q + 3] += lds_at(lds, lut_addr<3>(w, base));
+      }
+    }
+    rowval[g] = reduce_rows16(acc, lane);
+  }
+
+  // 4. write rows (lane 4r holds row r of its 16-row group)
+  const int rsel = (lane >> 2) & 15;
+#pragma unroll
+  for (int g = 0; g < STEPS; ++g) {
+    const int rg = (rb * STEPS + g) * W + wave;
+    const int row = rg * 16 + rsel;
+    if ((lane & 3) == 0 && rg < NG) {
+      if (M.nsplit == 1) {
+        if (row < M.N) M.y[row] = rowval[g];
+      } else {
+        M.partial[(size_t)sp * M.rows_pad + row] = rowval[g];
+      }
+    }
+  }
+  if (M.nsplit > 1) split_finish(M, rb, STEPS * W * 16, flag);
+}
+
+// --------------------------------------------------------------------------
+// Rotated lookup GEMV + 1-bit sign residual   [EDGE section details]
+// Region 0 of LDS: OC tile of 64 subvectors (from x_rot).  Region 1: for the
+// 32 sign bytes of the same 256 weights, T[v][p] = sum_i (bit_i(v) ? +1 : -1)
+// * x_rot[8p + i], stored twice (lanes p and p + 32) so that region 1 has the
+// same lane -> bank layout as region 0.
+// --------------------------------------------------------------------------
+template <int W, int STEPS>
+__global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args args) {
+  static_assert(W == 16, "sign-table build assumes 16 waves");
+  __shared__ float lds[2 * 16384 + 16];
+  uint32_t *flag = reinterpret_cast<uint32_t *>(lds + 2 * 16384);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Lut8Mat &M = args.mat[locate_matrix(args)];
+  const int local = blockIdx.x - M.wg_begin;
+  const int sp = local % M.nsplit, rb = local / M.nsplit;
+  const int NG = (M.N + 15) >> 4;
+  const int NP = (M.N + 31) >> 5;
+  const int half = lane >> 5, pl = lane & 31;
+
+  // 1. loads: per 32-row step, two index chunks, one sign chunk, 16 alphas
+  u32x4 va[STEPS], vb[STEPS], vs[STEPS], al0[STEPS], al1[STEPS];
+#pragma unroll
+  for (int g = 0; g < STEPS; ++g) {
+    const int rp = (rb * STEPS + g) * W + wave;
+    const int rga = 2 * rp, rgb = 2 * rp + 1;
+    va[g] = (rga < NG) ? load16(M.wi + (((size_t)sp * NG + rga) * 64 + lane) * 16) : u32x4{0u, 0u, 0u, 0u};
+    vb[g] = (rgb < NG) ? load16(M.wi + (((size_t)sp * NG + rgb) * 64 + lane) * 16) : u32x4{0u, 0u, 0u, 0u};
+    if (rp < NP) {
+      vs[g] = load16(M.signs + (((size_t)sp * NP + rp) * 64 + lane) * 16);
+      const uint16_t *ap = M.alpha + (((size_t)sp * NP + rp) * 4 + half * 2 + (pl >> 4)) * 16;
+      al0[g] = *reinterpret_cast<const u32x4 *>(ap);
+      al1[g] = *reinterpret_cast<const u32x4 *>(ap + 8);
+    } else {
+      vs[g] = u32x4{0u, 0u, 0u, 0u};
+      al0[g] = u32x4{0u, 0u, 0u, 0u};
+      al1[g] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // 2a. OC tile from the rotated input (fp32 x_rot times fp16 codebook)
+  {
+    const int j = sp * 64 + lane;                     // always < J (J % 64 == 0)
+    const float4 xv = *reinterpret_cast<const float4 *>(M.xr + 4 * (size_t)j);
+    const uint32_t *wc32 = reinterpret_cast<const uint32_t *>(M.wc);
+    float *dst = lds + (wave * 16) * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = wave * 16 + i;
+      const half2_t w01 = as_h2(wc32[2 * c]), w23 = as_h2(wc32[2 * c + 1]);
+      float o = xv.x * (float)w01.x;
+      o = __builtin_fmaf(xv.y, (float)w01.y, o);
+      o = __builtin_fmaf(xv.z, (float)w23.x, o);
+      o = __builtin_fmaf(xv.w, (float)w23.y, o);
+      dst[i * 64] = o;
+    }
+  }
+  // 2b. sign table for sign byte p = 32*sp + (lane & 31); wave = high nibble of v
+  {
+    const float *xp = M.xr + 8 * (size_t)(sp * 32 + pl);
+    const float4 lo4 = *reinterpret_cast<const float4 *>(xp);
+    const float4 hi4 = *reinterpret_cast<const float4 *>(xp + 4);
+    const float S = ((lo4.x + lo4.y) + (lo4.z + lo4.w)) + ((hi4.x + hi4.y) + (hi4.z + hi4.w));
+    const int hi = wave;
+    const float H = ((hi & 1) ? hi4.x : 0.f) + ((hi & 2) ? hi4.y : 0.f) +
+                    ((hi & 4) ? hi4.z : 0.f) + ((hi & 8) ? hi4.w : 0.f);
+    const float c0 = 2.f * H - S;
+    float L[16];
+    L[0] = 0.f;
+    const float xl[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+#pragma unroll
+    for (int lo = 1; lo < 16; ++lo) L[lo] = L[lo & (lo - 1)] + xl[__builtin_ctz(lo)];
+    float *dst = lds + 16384 + (hi * 16) * 64 + lane;
+#pragma unroll
+    for (int lo = 0; lo < 16; ++lo) dst[lo * 64] = __builtin_fmaf(2.f, L[lo], c0);
+  }
+  __syncthreads();
+
+  // 3. lookups
+  const uint32_t base0 = (uint32_t)lane << 2;
+  const uint32_t base1 = base0 | 0x10000u;
+  float rowval[STEPS];
+#pragma unroll
+  for (int g = 0; g < STEPS; ++g) {
+    float A[16], Bv[16], S[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { A[i] = 0.f; Bv[i] = 0.f; }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wa = va[g][q], wb = vb[g][q];
+      A[4 * q + 0] = lds_at(lds, lut_addr<0>(wa, base0));
+      A[4 * q + 1] = lds_at(lds, lut_addr<1>(wa, base0));
+      A[4 * q + 2] = lds_at(lds, lut_addr<2>(wa, base0));
+      A[4 * q + 3] = lds_at(lds, lut_addr<3>(wa, base0));
+      Bv[4 * q + 0] = lds_at(lds, lut_addr<0>(wb, base0));
+      Bv[4 * q + 1] = lds_at(lds, lut_addr<1>(wb, base0));
+      Bv[4 * q + 2] = lds_at(lds, lut_addr<2>(wb, base0));
+      Bv[4 * q + 3] = lds_at(lds, lut_addr<3>(wb, base0));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ws = vs[g][q];
+      const uint32_t a01 = (q < 2) ? al0[g][2 * q] : al1[g][2 * q - 4];
+      const uint32_t a23 = (q < 2) ? al0[g][2 * q + 1] : al1[g][2 * q - 3];
+      const half2_t h01 = as_h2(a01), h23 = as_h2(a23);
+      S[4 * q + 0] = (float)h01.x * lds_at(lds, lut_addr<0>(ws, base1));
+      S[4 * q + 1] = (float)h01.y * lds_at(lds, lut_addr<1>(ws, base1));
+      S[4 * q + 2] = (float)h23.x * lds_at(lds, lut_addr<2>(ws, base1));
+      S[4 * q + 3] = (float)h23.y * lds_at(lds, lut_addr<3>(ws, base1));
+    }
+    rowval[g] = reduce_rows32(A, Bv, S, lane);
+  }
+
+  // 4. lane 2r holds row r of the 32-row group
+  const int rsel = (lane >> 1) & 31;
+#pragma unroll
+  for (int g = 0; g < STEPS; ++g) {
+    const int rp = (rb * STEPS + g) * W + wave;
+    const int row = rp * 32 + rsel;
+    if ((lane & 1) == 0 && rp < NP) {
+      if (M.nsplit == 1) {
+        if (row < M.N) M.y[row] = rowval[g];
+      } else {
+        M.partial[(size_t)sp * M.rows_pad + row] = rowval[g];
+      }
+    }
+  }
+  if (M.nsplit > 1) split_finish(M, rb, STEPS * W * 32, flag);
+}
+
+// --------------------------------------------------------------------------
+// launchers of the lookup kernels
+// --------------------------------------------------------------------------
+template <int NSUB, int W, int STEPS>
+static int launch_plain_t(const Lut8Args &a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((lut8_plain_kernel<NSUB, W, STEPS>), dim3(grid), dim3(W * 64), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (s.nsub == 2 && s.waves == 16 && s.steps == 2) return launch_plain_t<2, 16, 2>(a, grid, st);
+  if (s.nsub == 2 && s.waves == 16 && s.steps == 1) return launch_plain_t<2, 16, 1>(a, grid, st);
+  if (s.nsub == 2 && s.waves == 4 && s.steps == 1) return launch_plain_t<2, 4, 1>(a, grid, st);
+  if (s.nsub == 1 && s.waves == 16 && s.steps == 2) return launch_plain_t<1, 16, 2>(a, grid, st);
+  if (s.nsub == 1 && s.waves == 16 && s.steps == 1) return launch_plain_t<1, 16, 1>(a, grid, st);
+  if (s.nsub == 1 && s.waves == 4 && s.steps == 1) return launch_plain_t<1, 4, 1>(a, grid, st);
+  return (int)hipErrorInvalidConfiguration;
+}
+
+int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (s.waves == 16 && s.steps == 1) {
+    hipLaunchKernelGGL((lut8_residual_kernel<16, 1>), dim3(grid), dim3(16 * 64), 0, st, a);
+    return (int)hipGetLastError();
+  }
+  return (int)hipErrorInvalidConfiguration;
+}
+
+// --------------------------------------------------------------------------
+// packing helpers (load time; bit layout of vqd.h)
+// --------------------------------------------------------------------------
+__global__ void pack_kernel(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, int64_t nbytes) {
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < nbytes;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    uint32_t byte = 0u;
+    for (int b = 0; b < 8; ++b) {
+      const int64_t q = o * 8 + b;
+      const int64_t t = q / nbits;
+      const int i = (int)(q - t * nbits);
+      if (t < count) byte |= ((idx[t] >> i) & 1u) << b;
+    }
+    out[o] = (uint8_t)byte;
+  }
+}
+
+__global__ void unpack_kernel(const uint8_t *packed, int64_t count, int nbits, uint32_t *out) {
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < count;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t q0 = t * nbits;
+    uint32_t v = 0u;
+    for (int i = 0; i < nbits; ++i) {
+      const int64_t q = q0 + i;
+      v |= ((uint32_t)(packed[q >> 3] >> (q & 7)) & 1u) << i;
+    }
+    out[t] = v;
+  }
+}
+
+// canonical [N][J] bytes -> tile-16x64
+__global__ void repack_wi8_kernel(const uint8_t *canon, int N, int J, uint8_t *dev) {
+  const int NG = (N + 15) >> 4;
+  const int64_t total = (int64_t)(J >> 6) * NG * 64;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(e & 63);
+    const int64_t chunk = e >> 6;
+    const int rg = (int)(chunk % NG);
+    const int jt = (int)(chunk / NG);
+    const int j = jt * 64 + l;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < 16; ++i) {
+      const int r = rg * 16 + i;
+      const uint32_t b = (r < N) ? canon[(size_t)r * J + j] : 0u;
+      w[i >> 2] |= b << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x4 *>(dev + e * 16) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// canonical signs [N][P] bytes -> tile-32x32
+__global__ void repack_signs_kernel(const uint8_t *canon, int N, int P, uint8_t *dev) {
+  const int NP = (N + 31) >> 5;
+  const int64_t total = (int64_t)(P >> 5) * NP * 64;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(e & 63);
+    const int64_t chunk = e >> 6;
+    const int rp = (int)(chunk % NP);
+    const int pt = (int)(chunk / NP);
+    const int hf = l >> 5, p = pt * 32 + (l & 31);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < 16; ++i) {
+      const int r = rp * 32 + hf * 16 + i;
+      const uint32_t b = (r < N) ? canon[(size_t)r * P + p] : 0u;
+      w[i >> 2] |= b << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x4 *>(dev + e * 16) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// canonical alpha [N][G] fp16 -> ((g/2*NP + r/32)*4 + ((r%32)/16)*2 + g%2)*16 + r%16
+__global__ void repack_alpha_kernel(const uint16_t *canon, int N, int G, uint16_t *dev) {
+  const int NP = (N + 31) >> 5;
+  const int64_t total = (int64_t)((G + 1) >> 1) * NP * 64;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(e & 15);
+    const int gl = (int)((e >> 4) & 1);
+    const int hf = (int)((e >> 5) & 1);
+    const int64_t chunk = e >> 6;
+    const int rp = (int)(chunk % NP);
+    const int g2 = (int)(chunk / NP);
+    const int g = g2 * 2 + gl, r = rp * 32 + hf * 16 + i;
+    dev[e] = (r < N && g < G) ? canon[(size_t)r * G + g] : (uint16_t)0;
+  }
+}
+
+// --------------------------------------------------------------------------
+// output codebook materialized in memory   [EVA 2.A]
+// --------------------------------------------------------------------------
+template <int D>
+__global__ void build_oc_kernel(const _Float16 *x, int B, int K, int nbits, const _Float16 *wc,
+                                void *oc, int f16_out) {
+  const int J = K / D;
+  const int64_t ncent = (int64_t)1 << nbits;
+  const int64_t total = (int64_t)B * J * ncent;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = e & (ncent - 1);
+    const int64_t row = e >> nbits;          // b*J + j
+    const int64_t b = row / J, j = row - b * J;
+    const _Float16 *xp = x + b * K + j * D;
+    const _Float16 *wp = wc + c * D;
+    float o = 0.f;
+#pragma unroll
+    for (int t = 0; t < D; ++t) o = __builtin_fmaf((float)xp[t], (float)wp[t], o);
+    if (f16_out)
+      reinterpret_cast<_Float16 *>(oc)[e] = (_Float16)o;
+    else
+      reinterpret_cast<float *>(oc)[e] = o;
+  }
+}
+
+// --------------------------------------------------------------------------
+// randomized Hadamard rotation   [EDGE section details]
+// One workgroup per (token, block of h): signed input in LDS, in-place
+// radix-2 butterflies in natural (Sylvester) order, scaled by 1/sqrt(h).
+// --------------------------------------------------------------------------
+__global__ void rht_kernel(const _Float16 *x, const int8_t *sign, int K, int h, float scale, float *x_rot) {
+  extern __shared__ float buf[];
+  const int blocks = K / h;
+  const int b = blockIdx.x / blocks, blk = blockIdx.x % blocks;
+  const size_t off = (size_t)b * K + (size_t)blk * h;
+  for (int i = threadIdx.x; i < h; i += blockDim.x) {
+    float v = (float)x[off + i];
+    if (sign) v *= (float)sign[blk * h + i];
+    buf[i] = v;
+  }
+  for (int len = 1; len < h; len <<= 1) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < (h >> 1); t += blockDim.x) {
+      const int i = (t / len) * 2 * len + (t % len);
+      const float a = buf[i], c = buf[i + len];
+      buf[i] = a + c;
+      buf[i + len] = a - c;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < h; i += blockDim.x) x_rot[off + i] = buf[i] * scale;
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+static int grid_for(int64_t work, int block) {
+  int64_t g = (work + block - 1) / block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (int)g;
+}
+
+int launch_pack(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, void *stream) {
+  const int64_t nbytes = (count * nbits + 7) / 8;
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(nbytes, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), idx, count, nbits, out, nbytes);
+  return (int)hipGetLastError();
+}
+
+int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out, void *stream) {
+  hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(count, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), packed, count, nbits, out);
+  return (int)hipGetLastError();
+}
+
+int launch_repack_wi8(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream) {
+  const int64_t total = (int64_t)(J >> 6) * ((N + 15) >> 4) * 64;
+  hipLaunchKernelGGL(repack_wi8_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), canon, N, J, dev);
+  return (int)hipGetLastError();
+}
+
+int launch_repack_signs(const uint8_t *canon, int N, int P, uint8_t *dev, void *stream) {
+  const int64_t total = (int64_t)(P >> 5) * ((N + 31) >> 5) * 64;
+  hipLaunchKernelGGL(repack_signs_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), canon, N, P, dev);
+  return (int)hipGetLastError();
+}
+
+int launch_repack_alpha(const uint16_t *canon, int N, int G, uint16_t *dev, void *stream) {
+  const int64_t total = (int64_t)((G + 1) >> 1) * ((N + 31) >> 5) * 64;
+  hipLaunchKernelGGL(repack_alpha_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), canon, N, G, dev);
+  return (int)hipGetLastError();
+}
+
+int launch_build_oc(const uint16_t *x, int B, int K, int d, int nbits, const uint16_t *wc, void *oc,
+                    int f16_out, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t total = (int64_t)B * (K / d) << nbits;
+  const dim3 grid(grid_for(total, 256)), block(256);
+  const _Float16 *xh = reinterpret_cast<const _Float16 *>(x);
+  const _Float16 *wh = reinterpret_cast<const _Float16 *>(wc);
+  switch (d) {
+    case 1: hipLaunchKernelGGL(build_oc_kernel<1>, grid, block, 0, st, xh, B, K, nbits, wh, oc, f16_out); break;
+    case 2: hipLaunchKernelGGL(build_oc_kernel<2>, grid, block, 0, st, xh, B, K, nbits, wh, oc, f16_out); break;
+    case 4: hipLaunchKernelGGL(build_oc_kernel<4>, grid, block, 0, st, xh, B, K, nbits, wh, oc, f16_out); break;
+    case 8: hipLaunchKernelGGL(build_oc_kernel<8>, grid, block, 0, st, xh, B, K, nbits, wh, oc, f16_out); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_rht(const uint16_t *x, const int8_t *sign, int B, int K, int h, float scale, float *x_rot,
+               void *stream) {
+  const int threads = h >= 256 ? 256 : (h >= 64 ? h : 64);
+  const int grid = B * (K / h);
+  hipLaunchKernelGGL(rht_kernel, dim3(grid), dim3(threads), (size_t)h * sizeof(float),
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const _Float16 *>(x), sign, K, h,
+                     scale, x_rot);
+  return (int)hipGetLastError();
+}
+
+int launch_fill_u32(uint32_t *p, size_t n, uint32_t v, void *stream) {
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for((int64_t)n, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), p, n, v);
+  return (int)hipGetLastError();
+}
+
+}  // namespace vqd

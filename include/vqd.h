@@ -91,6 +91,13 @@ typedef struct {
 const char *vq_status_str(int status);
 
 /*
+ * Description of the HIP runtime error behind the most recent VQ_EHIP
+ * returned to the calling thread ("no HIP error" if there was none).  The
+ * string is static and owned by the HIP runtime.
+ */
+const char *vq_last_error(void);
+
+/*
  * Bytes of the device layouts.  Zero means the shape is unsupported.
  *
  * WI device layout for nbits = 8 ("tile-16x64"): rows are padded with zero

@@ -124,3 +124,13 @@ def test_other_entry_points_validate():
     assert c["vq_workspace_init"](FAKE + 8, 1024, None) == vq.VQ_EALIGN
     assert c["vq_workspace_init"](None, 1024, None) == vq.VQ_EINVAL
     assert c["vq_workspace_bytes"](None, 1, 1, 0) == 0
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the binding leaves exactly one HIP runtime mapped: the one
+    torch loaded.  A second runtime would see no device and reject the
+    library's launches."""
+    pytest.importorskip("torch")
+    import vector_quantized_decode_amd  # noqa: F401
+    maps = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
+    assert len(maps) == 1, maps

@@ -21,6 +21,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
                       "`python -m vector_quantized_decode_amd.build` (or __graft_entry__.build())")
 
+# torch must load its HIP runtime first: libvqd.so then binds to that same
+# runtime (same soname), so torch's device pointers and streams are valid in
+# the library.  Loaded the other way round the process would hold two HIP
+# runtimes, and the second one sees no device.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 VQ_OK, VQ_EINVAL, VQ_EUNSUPPORTED, VQ_EALIGN, VQ_EWORKSPACE, VQ_EHIP = 0, -1, -2, -3, -4, -5
@@ -48,6 +54,7 @@ def _sig(name, restype, argtypes):
 
 _c = {
     "vq_status_str": _sig("vq_status_str", ctypes.c_char_p, [ctypes.c_int]),
+    "vq_last_error": _sig("vq_last_error", ctypes.c_char_p, []),
     "vq_wi_device_bytes": _sig("vq_wi_device_bytes", _sz, [_i32, _i32, _i32, _i32]),
     "vq_signs_device_bytes": _sig("vq_signs_device_bytes", _sz, [_i32, _i32]),
     "vq_alpha_device_bytes": _sig("vq_alpha_device_bytes", _sz, [_i32, _i32, _i32]),
@@ -77,7 +84,10 @@ EXPORTED = tuple(_c)
 class VQError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {vq_status_str(status)} ({status})")
+        msg = f"{where}: {vq_status_str(status)} ({status})"
+        if status == VQ_EHIP:
+            msg += f": {vq_last_error()}"
+        super().__init__(msg)
 
 
 def _check(status: int, where: str) -> None:
@@ -106,6 +116,10 @@ def _stream(stream) -> Optional[int]:
 # ------------------------------------------------------------------ plain calls
 def vq_status_str(status: int) -> str:
     return _c["vq_status_str"](status).decode()
+
+
+def vq_last_error() -> str:
+    return _c["vq_last_error"]().decode()
 
 
 def vq_wi_device_bytes(N: int, K: int, d: int, nbits: int) -> int:

@@ -4,12 +4,22 @@
 // Every entry point validates all of its arguments before it enqueues
 // anything; validation touches no HIP API, so an invalid call returns its
 // status even on a machine without a GPU.
+#include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <string.h>
 
 #include "vq_internal.h"
 
 namespace vqd {
+
+// HIP error behind the most recent VQ_EHIP of the calling thread.
+static thread_local int t_last_hip = 0;
+
+static int hip_status(int err) {
+  if (err == 0) return VQ_OK;
+  t_last_hip = err;
+  return VQ_EHIP;
+}
 
 static bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 static bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -170,13 +180,13 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
       const float scale = (float)(1.0 / sqrt((double)h));
       err = launch_rht(x[i], m[i].rht_sign, B, m[i].K, h, scale,
                        reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);
-      if (err) return VQ_EHIP;
+      if (err) return hip_status(err);
     }
     err = launch_lut8_residual(args, p.shape, (int)p.grid, stream);
   } else {
     err = launch_lut8_plain(args, p.shape, (int)p.grid, stream);
   }
-  return err ? VQ_EHIP : VQ_OK;
+  return hip_status(err);
 }
 
 }  // namespace vqd
@@ -195,6 +205,11 @@ const char *vq_status_str(int status) {
     case VQ_EHIP: return "VQ_EHIP: HIP runtime error";
     default: return "unknown";
   }
+}
+
+const char *vq_last_error(void) {
+  if (t_last_hip == 0) return "no HIP error";
+  return hipGetErrorString(static_cast<hipError_t>(t_last_hip));
 }
 
 size_t vq_wi_device_bytes(int32_t N, int32_t K, int32_t d, int32_t nbits) {
@@ -231,7 +246,7 @@ int vq_workspace_init(void *workspace, size_t ws_bytes, void *stream) {
   if (ws_bytes == 0) return VQ_OK;
   if (!workspace) return VQ_EINVAL;
   if (!aligned(workspace, 256)) return VQ_EALIGN;
-  return launch_fill_u32(static_cast<uint32_t *>(workspace), ws_bytes / 4, 0u, stream) ? VQ_EHIP : VQ_OK;
+  return hip_status(launch_fill_u32(static_cast<uint32_t *>(workspace), ws_bytes / 4, 0u, stream));
 }
 
 int vq_pack_indices(const uint32_t *idx, int64_t count, int32_t nbits, uint8_t *out, void *stream) {
@@ -239,7 +254,7 @@ int vq_pack_indices(const uint32_t *idx, int64_t count, int32_t nbits, uint8_t *
   if (count == 0) return VQ_OK;
   if (!idx || !out) return VQ_EINVAL;
   if (!aligned(idx, 4)) return VQ_EALIGN;
-  return launch_pack(idx, count, nbits, out, stream) ? VQ_EHIP : VQ_OK;
+  return hip_status(launch_pack(idx, count, nbits, out, stream));
 }
 
 int vq_unpack_indices(const uint8_t *packed, int64_t count, int32_t nbits, uint32_t *out, void *stream) {
@@ -247,7 +262,7 @@ int vq_unpack_indices(const uint8_t *packed, int64_t count, int32_t nbits, uint3
   if (count == 0) return VQ_OK;
   if (!packed || !out) return VQ_EINVAL;
   if (!aligned(out, 4)) return VQ_EALIGN;
-  return launch_unpack(packed, count, nbits, out, stream) ? VQ_EHIP : VQ_OK;
+  return hip_status(launch_unpack(packed, count, nbits, out, stream));
 }
 
 int vq_repack_wi(const uint8_t *canonical, int32_t N, int32_t K, int32_t d, int32_t nbits,
@@ -256,16 +271,14 @@ int vq_repack_wi(const uint8_t *canonical, int32_t N, int32_t K, int32_t d, int3
   if (N <= 0 || K <= 0 || d <= 0 || K % d || nbits < 1 || nbits > 16) return VQ_EINVAL;
   if (vq_wi_device_bytes(N, K, d, nbits) == 0) return VQ_EUNSUPPORTED;
   if (!aligned(device_layout, 16)) return VQ_EALIGN;
-  return launch_repack_wi8(canonical, N, K / d, static_cast<uint8_t *>(device_layout), stream) ? VQ_EHIP
-                                                                                               : VQ_OK;
+  return hip_status(launch_repack_wi8(canonical, N, K / d, static_cast<uint8_t *>(device_layout), stream));
 }
 
 int vq_repack_signs(const uint8_t *canonical, int32_t N, int32_t K, void *device_layout, void *stream) {
   if (!canonical || !device_layout || N <= 0 || K <= 0 || K % 8) return VQ_EINVAL;
   if (vq_signs_device_bytes(N, K) == 0) return VQ_EUNSUPPORTED;
   if (!aligned(device_layout, 16)) return VQ_EALIGN;
-  return launch_repack_signs(canonical, N, K / 8, static_cast<uint8_t *>(device_layout), stream) ? VQ_EHIP
-                                                                                                  : VQ_OK;
+  return hip_status(launch_repack_signs(canonical, N, K / 8, static_cast<uint8_t *>(device_layout), stream));
 }
 
 int vq_repack_alpha(const uint16_t *canonical, int32_t N, int32_t K, int32_t group, void *device_layout,
@@ -273,9 +286,7 @@ int vq_repack_alpha(const uint16_t *canonical, int32_t N, int32_t K, int32_t gro
   if (!canonical || !device_layout || N <= 0 || K <= 0 || group <= 0 || K % group) return VQ_EINVAL;
   if (vq_alpha_device_bytes(N, K, group) == 0) return VQ_EUNSUPPORTED;
   if (!aligned(canonical, 2) || !aligned(device_layout, 32)) return VQ_EALIGN;
-  return launch_repack_alpha(canonical, N, K / group, static_cast<uint16_t *>(device_layout), stream)
-             ? VQ_EHIP
-             : VQ_OK;
+  return hip_status(launch_repack_alpha(canonical, N, K / group, static_cast<uint16_t *>(device_layout), stream));
 }
 
 int vq_build_oc(const uint16_t *x, int32_t B, int32_t K, int32_t d, int32_t nbits, const uint16_t *wc,
@@ -286,7 +297,7 @@ int vq_build_oc(const uint16_t *x, int32_t B, int32_t K, int32_t d, int32_t nbit
   if (oc_dtype != VQ_F16 && oc_dtype != VQ_F32) return VQ_EINVAL;
   if ((int64_t)B * (K / d) > ((int64_t)1 << 40) >> nbits) return VQ_EINVAL;
   if (!aligned(x, 2) || !aligned(wc, 2) || !aligned(oc, oc_dtype == VQ_F32 ? 4 : 2)) return VQ_EALIGN;
-  return launch_build_oc(x, B, K, d, nbits, wc, oc, oc_dtype == VQ_F16, stream) ? VQ_EHIP : VQ_OK;
+  return hip_status(launch_build_oc(x, B, K, d, nbits, wc, oc, oc_dtype == VQ_F16, stream));
 }
 
 int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K, int32_t had_block, float *x_rot,
@@ -296,7 +307,7 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K, int32_t 
   if ((int64_t)B * (K / had_block) > 0x7fffffff) return VQ_EINVAL;
   if (!aligned(x, 2) || !aligned(x_rot, 4)) return VQ_EALIGN;
   const float scale = (float)(1.0 / sqrt((double)had_block));
-  return launch_rht(x, sign, B, K, had_block, scale, x_rot, stream) ? VQ_EHIP : VQ_OK;
+  return hip_status(launch_rht(x, sign, B, K, had_block, scale, x_rot, stream));
 }
 
 int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B, float *const *y,

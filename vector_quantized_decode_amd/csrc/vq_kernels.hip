@@ -144,26 +144,41 @@ __device__ __forceinline__ u32x4 load16(const uint8_t *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Cross-workgroup hand-off of split partial sums without cache maintenance.
+// Each XCD has its own L2, so a device-scope fence would write back and
+// invalidate the whole L2 once per wave.  Instead the partials travel with
+// device-scope (sc1) stores and loads, which are coherent across XCDs by
+// themselves; the only ordering needed is that a workgroup's partial stores
+// are acknowledged before it bumps the row block's counter.
+__device__ __forceinline__ void store_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Last workgroup of a row block adds the split partials in fixed order.
 __device__ __forceinline__ void split_finish(const Lut8Mat &M, int rb, int R, uint32_t *flag) {
-  __threadfence();
+  wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t prev = atomicAdd(&M.counter[rb], 1u);
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&M.counter[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = (prev == (uint32_t)(M.nsplit - 1)) ? 1u : 0u;
   }
   __syncthreads();
   if (*flag == 0u) return;
-  __threadfence();
   for (int t = threadIdx.x; t < R; t += blockDim.x) {
     const int row = rb * R + t;
     if (row < M.N) {
       float s = 0.f;
-      for (int q = 0; q < M.nsplit; ++q) s += M.partial[(size_t)q * M.rows_pad + row];
+      for (int q = 0; q < M.nsplit; ++q) s += load_dev(M.partial + (size_t)q * M.rows_pad + row);
       M.y[row] = s;
     }
   }
-  if (threadIdx.x == 0) M.counter[rb] = 0u;
+  if (threadIdx.x == 0) __hip_atomic_store(&M.counter[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------------------
@@ -250,7 +265,7 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
       if (M.nsplit == 1) {
         if (row < M.N) M.y[row] = rowval[g];
       } else {
-        M.partial[(size_t)sp * M.rows_pad + row] = rowval[g];
+        store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
       }
     }
   }
@@ -381,7 +396,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
       if (M.nsplit == 1) {
         if (row < M.N) M.y[row] = rowval[g];
       } else {
-        M.partial[(size_t)sp * M.rows_pad + row] = rowval[g];
+        store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
       }
     }
   }
@@ -393,6 +408,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
 // --------------------------------------------------------------------------
 template <int NSUB, int W, int STEPS>
 static int launch_plain_t(const Lut8Args &a, int grid, hipStream_t st) {
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL((lut8_plain_kernel<NSUB, W, STEPS>), dim3(grid), dim3(W * 64), 0, st, a);
   return (int)hipGetLastError();
 }
@@ -411,6 +427,7 @@ int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid, void *str
 int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (s.waves == 16 && s.steps == 1) {
+    (void)hipGetLastError();  // report only this launch's error
     hipLaunchKernelGGL((lut8_residual_kernel<16, 1>), dim3(grid), dim3(16 * 64), 0, st, a);
     return (int)hipGetLastError();
   }
@@ -574,12 +591,14 @@ static int grid_for(int64_t work, int block) {
 
 int launch_pack(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, void *stream) {
   const int64_t nbytes = (count * nbits + 7) / 8;
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(pack_kernel, dim3(grid_for(nbytes, 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), idx, count, nbits, out, nbytes);
   return (int)hipGetLastError();
 }
 
 int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out, void *stream) {
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(count, 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), packed, count, nbits, out);
   return (int)hipGetLastError();
@@ -587,6 +606,7 @@ int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out
 
 int launch_repack_wi8(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream) {
   const int64_t total = (int64_t)(J >> 6) * ((N + 15) >> 4) * 64;
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(repack_wi8_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), canon, N, J, dev);
   return (int)hipGetLastError();
@@ -594,6 +614,7 @@ int launch_repack_wi8(const uint8_t *canon, int N, int J, uint8_t *dev, void *st
 
 int launch_repack_signs(const uint8_t *canon, int N, int P, uint8_t *dev, void *stream) {
   const int64_t total = (int64_t)(P >> 5) * ((N + 31) >> 5) * 64;
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(repack_signs_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), canon, N, P, dev);
   return (int)hipGetLastError();
@@ -601,6 +622,7 @@ int launch_repack_signs(const uint8_t *canon, int N, int P, uint8_t *dev, void *
 
 int launch_repack_alpha(const uint16_t *canon, int N, int G, uint16_t *dev, void *stream) {
   const int64_t total = (int64_t)((G + 1) >> 1) * ((N + 31) >> 5) * 64;
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(repack_alpha_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), canon, N, G, dev);
   return (int)hipGetLastError();
@@ -627,6 +649,7 @@ int launch_rht(const uint16_t *x, const int8_t *sign, int B, int K, int h, float
                void *stream) {
   const int threads = h >= 256 ? 256 : (h >= 64 ? h : 64);
   const int grid = B * (K / h);
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(rht_kernel, dim3(grid), dim3(threads), (size_t)h * sizeof(float),
                      reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const _Float16 *>(x), sign, K, h,
                      scale, x_rot);
@@ -634,6 +657,7 @@ int launch_rht(const uint16_t *x, const int8_t *sign, int B, int K, int h, float
 }
 
 int launch_fill_u32(uint32_t *p, size_t n, uint32_t v, void *stream) {
+  (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for((int64_t)n, 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), p, n, v);
   return (int)hipGetLastError();

@@ -283,3 +283,53 @@ def test_gemv_residual_workload5_sampled_rows():
         rows = np.unique(np.concatenate([np.arange(64), rng.choice(mi.N, 192, replace=False),
                                          np.arange(mi.N - 32, mi.N)]))
         _assert_close(y[:, rows], _oracle_res(mi, rows=rows), f"workload5 matrix {m} sampled")
+
+
+# ------------------------------------------------------------------ split hand-off edge cases
+def _scaled_matrix(K, N, seed, x_scale=1.0, wc_scale=1.0):
+    mi = synth.small_matrix(K, N, 4, 8, seed=seed)
+    mi.x = (mi.x.astype(np.float64) * x_scale).astype(np.float16)
+    mi.wc = (mi.wc.astype(np.float64) * wc_scale).astype(np.float16)
+    return mi
+
+
+@pytest.mark.parametrize("x_scale,wc_scale", [(1000.0, 100.0), (1e-3, 1e-2), (60.0, 1.0)])
+def test_gemv_split_fixed_point_across_magnitudes(x_scale, wc_scale):
+    # K=4096 splits each row over 8 workgroups: the fixed-point hand-off's step
+    # follows the data's scale, so relative accuracy holds at any magnitude
+    _say(f"gemv split hand-off x*{x_scale} wc*{wc_scale}")
+    mi = _scaled_matrix(4096, 700, seed=21, x_scale=x_scale, wc_scale=wc_scale)
+    (y,), _ = _run_gemv([_upload(mi)], [mi.x])
+    _assert_close(y, _oracle_plain(mi), "scaled")
+
+
+def test_gemv_zero_input_gives_exact_zero():
+    _say("gemv x = 0")
+    mi = synth.small_matrix(4096, 300, 4, 8, seed=22)
+    mi.x = np.zeros_like(mi.x)
+    (y,), _ = _run_gemv([_upload(mi)], [mi.x])
+    assert np.array_equal(y, np.zeros_like(y))
+
+
+@pytest.mark.parametrize("bad", ["inf", "nan"])
+def test_gemv_nonfinite_input_propagates_like_oracle(bad):
+    # a non-finite input leaves the fixed-point path for float partials; the
+    # class of every output (NaN, +inf, -inf, finite) matches the oracle
+    _say(f"gemv non-finite input: {bad}")
+    mi = synth.small_matrix(4096, 200, 4, 8, seed=23)
+    x = mi.x.copy()
+    x[0, 1234] = np.float16(np.inf if bad == "inf" else np.nan)
+    mi.x = x
+    (y,), _ = _run_gemv([_upload(mi)], [mi.x])
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = _oracle_plain(mi)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    if fin.any():
+        _assert_close(y[fin], ref[fin], "finite rows")
+    # the workspace is left ready: a finite call afterwards is exact again
+    mi2 = synth.small_matrix(4096, 200, 4, 8, seed=24)
+    (y2,), _ = _run_gemv([_upload(mi2)], [mi2.x])
+    _assert_close(y2, _oracle_plain(mi2), "after non-finite call")

@@ -59,7 +59,7 @@ Lut8Shape lut8_shape_residual(const vq_matrix *, int32_t) {
 // ---------------------------------------------------------------- workspace
 struct MatPlan {
   int J, nsplit, nrb, rows_pad;
-  size_t partial_off, counter_off, xrot_off;
+  size_t partial_off, counter_off, acc_off, xrot_off;
 };
 
 struct Plan {
@@ -74,7 +74,8 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residua
   const int R = residual ? p.shape.rows_res() : p.shape.rows();
   const int JT = residual ? 64 : p.shape.jt();
   size_t off = 0;
-  // counters first (zeroed by vq_workspace_init), then partials, then x_rot
+  // counters and packed accumulators first (both must start at zero and are
+  // left at zero by every call), then partials, then x_rot
   for (int i = 0; i < count; ++i) {
     MatPlan &q = p.mp[i];
     q.J = m[i].K / m[i].d;
@@ -83,6 +84,8 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residua
     q.rows_pad = (m[i].N + 31) / 32 * 32;
     q.counter_off = off;
     off += round_up((size_t)q.nrb * sizeof(uint32_t), 256);
+    q.acc_off = off;
+    if (q.nsplit > 1) off += round_up((size_t)q.rows_pad * sizeof(uint64_t), 256);
   }
   p.grid = 0;
   for (int i = 0; i < count; ++i) {
@@ -152,7 +155,7 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
   Lut8Args args;
   memset(&args, 0, sizeof(args));
   args.count = count;
-  int wg = 0;
+  int max_wg = 0;
   for (int i = 0; i < count; ++i) {
     const MatPlan &q = p.mp[i];
     Lut8Mat &d = args.mat[i];
@@ -170,8 +173,9 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
     d.rows_pad = q.rows_pad;
     d.nsplit = q.nsplit;
     d.nrb = q.nrb;
-    d.wg_begin = wg;
-    wg += q.nsplit * q.nrb;
+    d.acc = reinterpret_cast<uint64_t *>(ws + q.acc_off);
+    d.nwg = q.nsplit * q.nrb;
+    if (d.nwg > max_wg) max_wg = d.nwg;
   }
   int err;
   if (residual) {
@@ -182,9 +186,9 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
                        reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);
       if (err) return hip_status(err);
     }
-    err = launch_lut8_residual(args, p.shape, (int)p.grid, stream);
+    err = launch_lut8_residual(args, p.shape, max_wg, stream);
   } else {
-    err = launch_lut8_plain(args, p.shape, (int)p.grid, stream);
+    err = launch_lut8_plain(args, p.shape, max_wg, stream);
   }
   return hip_status(err);
 }

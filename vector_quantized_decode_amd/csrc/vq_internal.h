@@ -21,14 +21,17 @@ struct Lut8Mat {
   float *y;               // fp32 output [N]
   float *partial;         // fp32 split partial sums [nsplit][rows_pad]
   uint32_t *counter;      // completion counters [nrb]
+  uint64_t *acc;          // packed fixed-point row accumulators [rows_pad]
   int32_t J;              // subvectors per row, K/4
   int32_t N;              // output rows
   int32_t rows_pad;       // rows of the padded layout (multiple of 32)
   int32_t nsplit;         // workgroups sharing a row block (split along J)
   int32_t nrb;            // row blocks
-  int32_t wg_begin;       // first workgroup id of this matrix in the grid
+  int32_t nwg;            // workgroups of this matrix (nsplit * nrb)
 };
 
+// Matrix m of a grouped call is served by workgroups (x, m) of a 2-D grid
+// with x < mat[m].nwg; the grid is as wide as the largest matrix needs.
 struct Lut8Args {
   Lut8Mat mat[VQ_MAX_GROUP];
   int32_t count;
@@ -49,8 +52,10 @@ Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count);
 Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count);
 
 // Kernel launchers: return a hipError_t value (0 = success).
-int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream);
-int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream);
+// Lookup kernels: grid (grid_x, a.count), grid_x = the most workgroups any
+// matrix of the call needs.
+int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream);
+int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream);
 int launch_pack(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, void *stream);
 int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out, void *stream);
 int launch_repack_wi8(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);

@@ -39,6 +39,8 @@
 namespace vqd {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float f32x32_t __attribute__((ext_vector_type(32)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
@@ -133,13 +135,6 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t w, uint32_t base) {
   return __builtin_amdgcn_perm(w, base, 0x0C020000u | ((4u + K) << 8));
 }
 
-__device__ __forceinline__ int locate_matrix(const Lut8Args &args) {
-  int mi = 0;
-  for (int i = 1; i < args.count; ++i)
-    if ((int)blockIdx.x >= args.mat[i].wg_begin) mi = i;
-  return mi;
-}
-
 __device__ __forceinline__ u32x4 load16(const uint8_t *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
@@ -173,12 +168,114 @@ __device__ __forceinline__ void split_finish(const Lut8Mat &M, int rb, int R, ui
   for (int t = threadIdx.x; t < R; t += blockDim.x) {
     const int row = rb * R + t;
     if (row < M.N) {
+      // loads go out eight at a time; the sum order (split 0, 1, ...) is fixed
+      const float *p = M.partial + row;
       float s = 0.f;
-      for (int q = 0; q < M.nsplit; ++q) s += load_dev(M.partial + (size_t)q * M.rows_pad + row);
+      int q = 0;
+      for (; q + 8 <= M.nsplit; q += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = load_dev(p + (size_t)(q + u) * M.rows_pad);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      for (; q < M.nsplit; ++q) s += load_dev(p + (size_t)q * M.rows_pad);
       M.y[row] = s;
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(&M.counter[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One-round-trip hand-off of split partials.  Every workgroup converts its
+// partial of a row to fixed point with a power-of-two step q shared by the
+// whole matrix, and adds it together with a split count into the row's 64-bit
+// accumulator with one device-scope atomic:
+//   word += 2^57 + (round(p / q) + 2^49)
+// The workgroup whose add completes the count (old count == nsplit - 1) has
+// the full sum in old + own term, writes y and clears the word.  q comes from
+// a bound B >= |p| that every workgroup of the matrix computes identically,
+// with |p|/q < 2^48, so each biased term lies in (0, 2^50) and up to 127
+// splits fit below the count field.  Integer adds are exact and associative:
+// y does not depend on the order in which workgroups arrive.
+struct FixedScale {
+  double inv_q;   // 1 / q
+  double q;       // step, a power of two
+};
+
+__device__ __forceinline__ FixedScale fixed_scale(float bound) {
+  FixedScale f;
+  if (bound > 0.f) {
+    const int e = ilogbf(bound) + 1 - 48;   // bound < 2^(e + 48)
+    f.q = ldexp(1.0, e);
+    f.inv_q = ldexp(1.0, -e);
+  } else {
+    f.q = 1.0;
+    f.inv_q = 1.0;
+  }
+  return f;
+}
+
+__device__ __forceinline__ void packed_add_finish(uint64_t *acc, float *y, float p, const FixedScale &f,
+                                                  int nsplit) {
+  const int64_t v = llrint((double)p * f.inv_q);
+  const uint64_t term = (1ull << 57) + (uint64_t)(v + (1ll << 49));
+  const uint64_t old = __hip_atomic_fetch_add(acc, term, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((int)(old >> 57) == nsplit - 1) {
+    const uint64_t tot = old + term;
+    const int64_t sv = (int64_t)(tot & ((1ull << 57) - 1)) - (int64_t)nsplit * (1ll << 49);
+    *y = (float)((double)sv * f.q);
+    __hip_atomic_store(acc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Sum and max of the magnitudes of 8 fp16 values.
+__device__ __forceinline__ float abs_sum8(u32x4 c) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2_t h = as_h2(c[i] & 0x7fff7fffu);
+    s += (float)h.x + (float)h.y;
+  }
+  return s;
+}
+// Largest magnitude of 8 fp16 values, compared as integer bits so that an
+// infinity or NaN gives +inf (the caller then leaves the fixed-point path).
+__device__ __forceinline__ float abs_max8(u32x4 c) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(c[i] & 0x7fffu, (c[i] >> 16) & 0x7fffu));
+  if (m >= 0x7c00u) return __builtin_inff();
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)m);
+}
+
+// Wave-wide sum and max: quad and row butterflies with DPP, then 16- and
+// 32-lane swaps.  Every lane ends with the same value (IEEE add and max are
+// commutative), identical in every workgroup that holds the same data in the
+// same lanes.
+constexpr int DPP_ROW_MIRROR = 0x140;      // lane i <-> 15 - i within 16 lanes
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<DPP_QUAD_XOR1>(v);
+  v += dpp<DPP_QUAD_XOR2>(v);
+  v += dpp<DPP_ROW_MIRROR>(v);             // quad q + quad 3-q
+  v += dpp<DPP_ROW_ROR8>(v);               // + the other pair: whole row
+  float a = v, b = v;
+  swap16(a, b);
+  v = a + b;                               // rows 2k + rows 2k+1
+  a = v; b = v;
+  swap32(a, b);
+  return a + b;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_ROW_ROR8>(v));
+  float a = v, b = v;
+  swap16(a, b);
+  v = fmaxf(a, b);
+  a = v; b = v;
+  swap32(a, b);
+  return fmaxf(a, b);
 }
 
 // --------------------------------------------------------------------------
@@ -186,53 +283,102 @@ __device__ __forceinline__ void split_finish(const Lut8Mat &M, int rb, int R, ui
 // --------------------------------------------------------------------------
 template <int NSUB, int W, int STEPS>
 __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args) {
-  __shared__ float lds[NSUB * 16384 + 16];
-  uint32_t *flag = reinterpret_cast<uint32_t *>(lds + NSUB * 16384);
+  constexpr int NT = W * 64;
+  constexpr int TASKS = NSUB * 8;                  // OC sub-tiles: 64 subvectors x 32 centroids
+  constexpr int TPW = (TASKS + W - 1) / W;         // sub-tiles per wave
+  __shared__ float lds[NSUB * 16384 + 2 * W + 16];
+  float *bnd = lds + NSUB * 16384;                 // per-wave bound parts
+  uint32_t *flag = reinterpret_cast<uint32_t *>(bnd + 2 * W);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Lut8Mat &M = args.mat[locate_matrix(args)];
-  const int local = blockIdx.x - M.wg_begin;
+  const Lut8Mat &M = args.mat[blockIdx.y];
+  if ((int)blockIdx.x >= M.nwg) return;
+  const int local = blockIdx.x;
   const int sp = local % M.nsplit, rb = local / M.nsplit;
-  const int jtiles = M.J >> 6;
   const int NG = (M.N + 15) >> 4;
+  const uint8_t *xb = reinterpret_cast<const uint8_t *>(M.x);
+  const uint8_t *wcb = reinterpret_cast<const uint8_t *>(M.wc);
 
-  // 1. issue every index load of this workgroup up front
+  // 1. inputs of the output-codebook tile.  Sub-tile t = (s, cb) covers
+  //    subvectors 64 (sp NSUB + s) + l and centroids 32 cb + (l % 32); lane l
+  //    holds x_j and WC[c] as four fp16 each (the host picks NSUB so that
+  //    64*NSUB divides J: every subvector exists).
+  half4_t xa[TPW], wa[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = min(wave + u * W, TASKS - 1);
+    const int s = t >> 3, cb = t & 7;
+    xa[u] = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(xb + 8 * ((size_t)(sp * NSUB + s) * 64 + lane)));
+    wa[u] = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(wcb + 8 * (cb * 32 + (lane & 31))));
+  }
+  //    inputs of the bound |partial| <= sum_k |x_k| * max |WC| used by the
+  //    fixed-point hand-off: x in 16-byte chunks t and t + NT, WC chunk t
+  const int nxc = M.J >> 1;                        // 16-byte chunks of x
+  const int t0 = threadIdx.x, t1 = threadIdx.x + NT;
+  const u32x4 xb0 = load16(xb + 16 * (size_t)min(t0, nxc - 1));
+  const u32x4 xb1 = load16(xb + 16 * (size_t)min(t1, nxc - 1));
+  const u32x4 wb = load16(wcb + 16 * min(t0, 127));
+  // every wave's small loads enter the memory pipeline before the index stream
+  __builtin_amdgcn_s_barrier();
+
+  // 2. every index load of this workgroup, issued up front and unconditional
+  //    (branches here would make the compiler wait for all loads before the
+  //    OC build); streamed past the caches.  Row groups past the end load the
+  //    last row group instead; their sums are never written.
   u32x4 v[STEPS][NSUB];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
-    const int rg = (rb * STEPS + g) * W + wave;
+    const int rg = min((rb * STEPS + g) * W + wave, NG - 1);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const int jt = sp * NSUB + s;
-      if (rg < NG && jt < jtiles)
-        v[g][s] = load16(M.wi + (((size_t)jt * NG + rg) * 64 + lane) * 16);
-      else
-        v[g][s] = u32x4{0u, 0u, 0u, 0u};
+      v[g][s] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(M.wi + (((size_t)jt * NG + rg) * 64 + lane) * 16));
     }
   }
 
-  // 2. output-codebook tile: OC[j][c] = x_j . WC[c], fp16 products summed in fp32
-  {
-    constexpr int CB = W / NSUB;
-    constexpr int CPB = 256 / CB;
-    const int s = wave % NSUB, cb = wave / NSUB;
-    const int j = sp * 64 * NSUB + s * 64 + lane;
-    uint2 xv = make_uint2(0u, 0u);
-    if (j < M.J) xv = *reinterpret_cast<const uint2 *>(M.x + 4 * (size_t)j);
-    const uint32_t *wc32 = reinterpret_cast<const uint32_t *>(M.wc);
-    float *dst = lds + (s * 256 + cb * CPB) * 64 + lane;
-#pragma unroll 8
-    for (int i = 0; i < CPB; ++i) {
-      const int c = cb * CPB + i;
-      const uint32_t w0 = wc32[2 * c], w1 = wc32[2 * c + 1];
-      float o = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(w0), 0.f, false);
-      o = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(w1), o, false);
-      dst[i * 64] = o;
+  // 3. OC[j][c] = x_j . WC[c] on the matrix cores: one 2-block 32x32x4 fp16
+  //    MFMA per sub-tile (fp32 accumulation).  Output register r of lane l
+  //    holds block r/16, centroid row m = ((r%16)/4) 8 + (l/32) 4 + r%4 and
+  //    subvector column l%32; swapping the upper lanes of register i with the
+  //    lower lanes of register i+16 leaves one centroid per register with
+  //    subvector 64 s + l in lane l, so each LDS store hits 64 banks.
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave + u * W;
+    if (t < TASKS) {
+      const int s = t >> 3, cb = t & 7;
+      f32x32_t o = {};
+      o = __builtin_amdgcn_mfma_f32_32x32x4f16(wa[u], xa[u], o, 0, 0, 0);
+      float *dst = lds + (s * 256 + cb * 32) * 64 + lane;
+      const int mhi = (lane >> 5) * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float a = o[i], b = o[i + 16];
+        swap32(a, b);
+        const int m = (i >> 2) * 8 + (i & 3);    // centroid row of a (lanes < 32 half)
+        dst[(m) * 64] = a;                        // centroid 32 cb + m
+        dst[(m + 4) * 64] = b;                    // centroid 32 cb + m + 4
+      }
+      (void)mhi;
     }
   }
+  //    per-wave parts of the bound
+  {
+    float sx = 0.f;
+    if (t0 < nxc) sx += abs_sum8(xb0);
+    if (t1 < nxc) sx += abs_sum8(xb1);
+    for (int t = t0 + 2 * NT; t < nxc; t += NT)   // inputs longer than 16*NT halves
+      sx += abs_sum8(load16(xb + 16 * (size_t)t));
+    const float mw = (t0 < 128) ? abs_max8(wb) : 0.f;
+    const float ws = wave_sum(sx), wm = wave_max(mw);
+    if (lane == 0) { bnd[wave] = ws; bnd[W + wave] = wm; }
+  }
+  // keep index-dependent work out of the OC build (it would wait for loads)
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
-  // 3. conflict-free lookups and the cross-lane adder tree
+  // 4. conflict-free lookups and the cross-lane adder tree
   const uint32_t base0 = (uint32_t)lane << 2;
   float rowval[STEPS];
 #pragma unroll
@@ -255,21 +401,37 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
     rowval[g] = reduce_rows16(acc, lane);
   }
 
-  // 4. write rows (lane 4r holds row r of its 16-row group)
+  // 5. rows out (lane 4r holds row r of its 16-row group)
   const int rsel = (lane >> 2) & 15;
+  if (M.nsplit == 1) {
+#pragma unroll
+    for (int g = 0; g < STEPS; ++g) {
+      const int row = ((rb * STEPS + g) * W + wave) * 16 + rsel;
+      if ((lane & 3) == 0 && row < M.N) M.y[row] = rowval[g];
+    }
+    return;
+  }
+  float S = 0.f, Mw = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) { S += bnd[w]; Mw = fmaxf(Mw, bnd[W + w]); }
+  const float bound = S * Mw * 1.0009765625f;     // margin for fp32 rounding
+  if (bound <= 3.0e38f && M.nsplit <= 127) {      // finite: fixed-point hand-off
+    const FixedScale fs = fixed_scale(bound);
+#pragma unroll
+    for (int g = 0; g < STEPS; ++g) {
+      const int row = ((rb * STEPS + g) * W + wave) * 16 + rsel;
+      if ((lane & 3) == 0 && row < M.N) packed_add_finish(M.acc + row, M.y + row, rowval[g], fs, M.nsplit);
+    }
+    return;
+  }
+  // non-finite inputs: float partials and a last-workgroup sum
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     const int rg = (rb * STEPS + g) * W + wave;
     const int row = rg * 16 + rsel;
-    if ((lane & 3) == 0 && rg < NG) {
-      if (M.nsplit == 1) {
-        if (row < M.N) M.y[row] = rowval[g];
-      } else {
-        store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
-      }
-    }
+    if ((lane & 3) == 0 && rg < NG) store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
   }
-  if (M.nsplit > 1) split_finish(M, rb, STEPS * W * 16, flag);
+  split_finish(M, rb, STEPS * W * 16, flag);
 }
 
 // --------------------------------------------------------------------------
@@ -286,8 +448,9 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   uint32_t *flag = reinterpret_cast<uint32_t *>(lds + 2 * 16384);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Lut8Mat &M = args.mat[locate_matrix(args)];
-  const int local = blockIdx.x - M.wg_begin;
+  const Lut8Mat &M = args.mat[blockIdx.y];
+  if ((int)blockIdx.x >= M.nwg) return;
+  const int local = blockIdx.x;
   const int sp = local % M.nsplit, rb = local / M.nsplit;
   const int NG = (M.N + 15) >> 4;
   const int NP = (M.N + 31) >> 5;
@@ -407,28 +570,28 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
 // launchers of the lookup kernels
 // --------------------------------------------------------------------------
 template <int NSUB, int W, int STEPS>
-static int launch_plain_t(const Lut8Args &a, int grid, hipStream_t st) {
+static int launch_plain_t(const Lut8Args &a, int grid_x, hipStream_t st) {
   (void)hipGetLastError();  // report only this launch's error
-  hipLaunchKernelGGL((lut8_plain_kernel<NSUB, W, STEPS>), dim3(grid), dim3(W * 64), 0, st, a);
+  hipLaunchKernelGGL((lut8_plain_kernel<NSUB, W, STEPS>), dim3(grid_x, a.count), dim3(W * 64), 0, st, a);
   return (int)hipGetLastError();
 }
 
-int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream) {
+int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (s.nsub == 2 && s.waves == 16 && s.steps == 2) return launch_plain_t<2, 16, 2>(a, grid, st);
-  if (s.nsub == 2 && s.waves == 16 && s.steps == 1) return launch_plain_t<2, 16, 1>(a, grid, st);
-  if (s.nsub == 2 && s.waves == 4 && s.steps == 1) return launch_plain_t<2, 4, 1>(a, grid, st);
-  if (s.nsub == 1 && s.waves == 16 && s.steps == 2) return launch_plain_t<1, 16, 2>(a, grid, st);
-  if (s.nsub == 1 && s.waves == 16 && s.steps == 1) return launch_plain_t<1, 16, 1>(a, grid, st);
-  if (s.nsub == 1 && s.waves == 4 && s.steps == 1) return launch_plain_t<1, 4, 1>(a, grid, st);
+  if (s.nsub == 2 && s.waves == 16 && s.steps == 2) return launch_plain_t<2, 16, 2>(a, grid_x, st);
+  if (s.nsub == 2 && s.waves == 16 && s.steps == 1) return launch_plain_t<2, 16, 1>(a, grid_x, st);
+  if (s.nsub == 2 && s.waves == 4 && s.steps == 1) return launch_plain_t<2, 4, 1>(a, grid_x, st);
+  if (s.nsub == 1 && s.waves == 16 && s.steps == 2) return launch_plain_t<1, 16, 2>(a, grid_x, st);
+  if (s.nsub == 1 && s.waves == 16 && s.steps == 1) return launch_plain_t<1, 16, 1>(a, grid_x, st);
+  if (s.nsub == 1 && s.waves == 4 && s.steps == 1) return launch_plain_t<1, 4, 1>(a, grid_x, st);
   return (int)hipErrorInvalidConfiguration;
 }
 
-int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid, void *stream) {
+int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (s.waves == 16 && s.steps == 1) {
     (void)hipGetLastError();  // report only this launch's error
-    hipLaunchKernelGGL((lut8_residual_kernel<16, 1>), dim3(grid), dim3(16 * 64), 0, st, a);
+    hipLaunchKernelGGL((lut8_residual_kernel<16, 1>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
     return (int)hipGetLastError();
   }
   return (int)hipErrorInvalidConfiguration;

@@ -12,15 +12,25 @@ Infinity Cache and the L2s) so every step streams its indices from HBM.  The
 C calls are captured once in a HIP graph and the graph is replayed; HIP
 events on the launch stream bracket the timed replays.
 
-Prints one JSON line: effective weight-byte throughput (GB/s) as `value`,
-microseconds per layer, the HBM roofline fraction of the lookup kernel and
-the CPU float64 oracle timed on a bounded sample of the same workload.
+Prints one JSON line:
+  value            effective weight-byte throughput (GB/s) of back-to-back
+                   layer calls, launch gaps included; us_per_layer beside it
+  roofline         the lookup kernel (one launch per call): algorithmic bytes
+                   per launch over its average launch duration in the timed
+                   region; traffic = HBM bytes per launch from the committed
+                   rocprofv3 counter summary, when it was taken on the
+                   current kernel source (else null)
+  cpu_baseline     the float64 CPU oracle on the same layer, timed on the
+                   host (one thread), repeated until >= 10 s
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -31,6 +41,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, decimal GB/s
+METRIC = "µs/layer and effective HBM GB/s (% of peak) for VQ-GEMV at LLaMA-7B, B=1"
+KERNEL_SRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc", "vq_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
+                  2: "llama7b-attn-qkvo-4096x4096-2bit-b1",
+                  5: "gemma2-9b-mlp-rotated-vq-residual-3.125bit-b1"}
 
 
 def parse():
@@ -38,23 +55,41 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=25600)
     p.add_argument("--warmup", type=int, default=1024)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 5])
+    p.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--copies", type=int, default=0, help="layer copies (0: enough for 2 GiB)")
     p.add_argument("--no-graph", action="store_true", help="launch from Python instead of a graph")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time spent on the oracle baseline")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return p.parse_args()
 
 
-WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
-                  2: "llama7b-attn-qkvo-4096x4096-2bit-b1",
-                  5: "gemma2-9b-mlp-rotated-vq-residual-3.125bit-b1"}
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: int):
+    """HBM bytes per launch of the lookup kernel from the committed counter
+    summary of this workload, if it was taken on the current kernel source."""
+    sha = kernel_source_sha()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        text = open(path).read()
+        m = re.search(r"traffic-record: workload=(\d+) kernel_sha=(\w+) "
+                      r"fetch_bytes=([\d.]+) write_bytes=([\d.]+)", text)
+        if m and int(m.group(1)) == workload and m.group(2) == sha:
+            return float(m.group(3)) + float(m.group(4)), os.path.basename(path)
+    return None, None
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(how the path would shard is described in DESIGN.md)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
@@ -103,8 +138,8 @@ def main():
     ws = vq.alloc_workspace(base, wl.B, residual=residual, device=dev)
     call = vq.vq_gemv_residual if residual else vq.vq_gemv
     torch.cuda.synchronize()
-    setup_s = time.time() - t0
-    print(f"# setup: {copies} copies x {layer_bytes} B in {setup_s:.1f} s", file=sys.stderr, flush=True)
+    print(f"# setup: {copies} copies x {layer_bytes} B in {time.time() - t0:.1f} s",
+          file=sys.stderr, flush=True)
 
     # ---- sampled parity check of copy 0 in the timed launch configuration
     parity = None
@@ -130,7 +165,8 @@ def main():
             worst = max(worst, rel)
             ok = ok and oracle.within_tolerance(got, ref)
         parity = {"sampled_rows_per_matrix": 256, "max_rel_l2": worst, "pass": bool(ok)}
-        print(f"# parity (sampled rows): max rel_l2 {worst:.3e} pass={ok}", file=sys.stderr, flush=True)
+        print(f"# parity (sampled rows): max rel_l2 {worst:.3e} pass={ok}", file=sys.stderr,
+              flush=True)
 
     # ---- graph of one pass over all copies
     stream = torch.cuda.Stream()
@@ -162,6 +198,7 @@ def main():
         run_steps(max(args.warmup, per_graph))
     torch.cuda.synchronize()
 
+    # ---- timed region: back-to-back layer calls
     with torch.cuda.stream(stream):
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
@@ -176,47 +213,66 @@ def main():
     print(f"# timed {done} steps in {ms:.2f} ms: {us_per_layer:.3f} us/layer, {gbs:.1f} GB/s",
           file=sys.stderr, flush=True)
 
-    # ---- CPU oracle baseline on a bounded sample (rank 0, N=1)
+    # One call is one launch of the lookup kernel, so the timed region's
+    # average launch period is that kernel's average duration back to back
+    # (rocprofv3's kernel trace of the same command reports the same figure).
+    launch_us = us_per_layer
+    kernel_gbs = gbs
+
+    # ---- plain copy of known size: the reference reading of the HBM byte counters
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("# copy probe: 5 x 256 MiB device copies", file=sys.stderr, flush=True)
+
+    # ---- CPU oracle baseline: the whole layer, one thread, >= cpu-seconds
     cpu = None
     if not args.no_cpu:
         import oracle
         from threadpoolctl import threadpool_limits
-        n_rows = 512 if residual else 1024
         packed = []
-        sample_bytes = 0
         for mi in mis:
-            if residual:
-                packed.append((oracle.pack_rows(mi.idx[:n_rows], 8),
-                               oracle.pack_rows(mi.sign_bits[:n_rows], 1)))
-                sample_bytes += n_rows * (mi.K // mi.d * mi.nbits // 8 + mi.K // 8 + mi.K // 64)
-            else:
-                packed.append((oracle.pack_rows(mi.idx[:n_rows], mi.nbits), None))
-                sample_bytes += n_rows * mi.K // mi.d * mi.nbits // 8
-            sample_bytes += (1 << mi.nbits) * mi.d * 2
+            pw = oracle.pack_rows(mi.idx, mi.nbits)
+            ps = oracle.pack_rows(mi.sign_bits, 1) if residual else None
+            packed.append((pw, ps))
+
+        def one_layer():
+            for mi, (pw, ps) in zip(mis, packed):
+                if residual:
+                    oracle.vq_gemv_residual(mi.x, mi.wc, pw, ps, mi.alpha, mi.rht_sign,
+                                            mi.had_block, mi.N, mi.K, mi.d, mi.nbits, mi.group)
+                else:
+                    oracle.vq_gemv(mi.x, mi.wc, pw, mi.N, mi.K, mi.d, mi.nbits)
+
         reps = []
         with threadpool_limits(limits=1):
-            for rep in range(4):
+            one_layer()                                   # warm
+            t_all = time.perf_counter()
+            while len(reps) < 3 or time.perf_counter() - t_all < args.cpu_seconds:
                 t = time.perf_counter()
-                for mi, (pw, ps) in zip(mis, packed):
-                    if residual:
-                        oracle.vq_gemv_residual(mi.x, mi.wc, pw, ps, mi.alpha[:n_rows], mi.rht_sign,
-                                                mi.had_block, n_rows, mi.K, mi.d, mi.nbits, mi.group)
-                    else:
-                        oracle.vq_gemv(mi.x, mi.wc, pw, n_rows, mi.K, mi.d, mi.nbits)
-                if rep:
-                    reps.append(time.perf_counter() - t)
+                one_layer()
+                reps.append(time.perf_counter() - t)
         med = statistics.median(reps)
         cores = len(os.sched_getaffinity(0))
-        cpu = {"value": round(sample_bytes / med / 1e9, 5), "unit": "GB/s", "cores": 1,
+        cpu = {"value": round(layer_bytes / med / 1e9, 5), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
-               "sample": f"first {n_rows} rows of each of the {wl.count} matrices plus their "
-                         f"codebooks ({sample_bytes} weight bytes); float64 numpy oracle (unpack, "
-                         f"output codebook, lookup sum); BLAS limited to 1 thread; median of 3 timed "
-                         f"runs after 1 warm run; host has {cores} cores",
-               "seconds_per_sample": round(med, 4)}
+               "sample": f"the whole layer ({wl.count} matrices, {layer_bytes} weight bytes), "
+                         f"float64 numpy oracle (unpack, output codebook, lookup sum"
+                         f"{', rotation, residual' if residual else ''}) on one thread (BLAS "
+                         f"limited to 1), {len(reps)} timed runs after 1 warm run, median; "
+                         f"host has {cores} cores",
+               "us_per_layer": round(med * 1e6, 1)}
+        print(f"# cpu oracle: {med * 1e3:.1f} ms/layer over {len(reps)} runs", file=sys.stderr,
+              flush=True)
 
+    traffic, traffic_src = committed_traffic(args.workload)
     out = {
-        "metric": "us/layer and effective HBM GB/s (% of peak) for VQ-GEMV at LLaMA-7B, B=1",
+        "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -234,8 +290,11 @@ def main():
                    "K_N": [[s.K, s.N] for s in wl.matrices], "d": wl.d, "nbits": wl.nbits,
                    "B": wl.B, "weight_bytes_per_layer": layer_bytes, "layer_copies": copies,
                    "launch": "hip graph" if graph is not None else "stream"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_us": round(launch_us, 4),
+                     "algorithmic_bytes_per_launch": layer_bytes,
+                     "traffic_source": traffic_src, "kernel_source_sha": kernel_source_sha()},
         "cpu_baseline": cpu,
         "parity": parity,
     }

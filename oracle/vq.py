@@ -56,7 +56,7 @@ import numpy as np
 __all__ = [
     "pack_bits", "unpack_bits", "pack_rows", "unpack_rows",
     "sylvester_hadamard", "rht", "output_codebook", "lookup_sum",
-    "vq_gemv", "residual_term", "vq_gemv_residual", "compare",
+    "vq_gemv", "dequant_gemv", "residual_term", "vq_gemv_residual", "compare",
     "within_tolerance", "REL_L2_TOL", "MAX_ERR_RMS_TOL",
 ]
 
@@ -210,6 +210,20 @@ def vq_gemv(x: np.ndarray, wc: np.ndarray, wi_packed: np.ndarray, N: int,
         oc = output_codebook(xf[:, j0 * d:j1 * d], wc, d)
         y += lookup_sum(oc, idx[:, j0:j1])
     return y
+
+
+def dequant_gemv(x: np.ndarray, wc: np.ndarray, wi_packed: np.ndarray, N: int,
+                 K: int, d: int, nbits: int) -> np.ndarray:
+    """The plain definition the lookup form reassociates: dequantize the
+    weights, W_hat[r, j*d + t] = WC[WI[r, j], t], then y = X W_hat^T
+    [EVA 1, 2.A].  float64 [B][N].  Cheap for a few rows of a matrix whose
+    output codebook would be huge (2^n >> N)."""
+    J = K // d
+    idx = unpack_rows(wi_packed, N, J, nbits)
+    w = np.asarray(wc, dtype=np.float64)
+    w_hat = w[idx].reshape(N, K)
+    xf = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    return xf @ w_hat.T
 
 
 # --------------------------------------------------------------------------

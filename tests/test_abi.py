@@ -42,6 +42,13 @@ def test_device_layout_sizes():
     assert vq.vq_wi_device_bytes(4096, 4096, 4, 8) == 4096 * 1024
     assert vq.vq_wi_device_bytes(100, 1024, 4, 8) == 112 * 256      # rows padded to 16
     assert vq.vq_wi_device_bytes(64, 1000, 4, 8) == 0                # J not a multiple of 64
+    assert vq.vq_wi_device_bytes(4096, 4096, 4, 12) == 4096 * 1024 * 3 // 2
+    assert vq.vq_wi_device_bytes(11008, 4096, 4, 12) == 11008 * 1024 * 3 // 2
+    assert vq.vq_wi_device_bytes(100, 1024, 4, 12) == 112 * 256 * 3 // 2   # rows padded to 16
+    assert vq.vq_wi_device_bytes(5120, 13824, 8, 16) == 5120 * 1728 * 2
+    assert vq.vq_wi_device_bytes(20, 256, 8, 16) == 32 * 32 * 2
+    assert vq.vq_wi_device_bytes(16, 128, 8, 16) == 0                 # J not a multiple of 32
+    assert vq.vq_wi_device_bytes(16, 1024, 4, 10) == 0                # no kernel for (4, 10)
     assert vq.vq_signs_device_bytes(14336, 3584) == 14336 * 448
     assert vq.vq_signs_device_bytes(100, 512) == 128 * 64            # rows padded to 32
     assert vq.vq_alpha_device_bytes(3584, 14336, 128) == 3584 * 112 * 2
@@ -76,7 +83,15 @@ def test_gemv_validation_errors():
     assert _gemv([_m(nbits=17)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
     assert _gemv([_m(wi=None)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
     assert _gemv([_m(N=0)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
-    assert _gemv([_m(d=8, nbits=16)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED
+    assert _gemv([_m(d=2, nbits=8)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED   # no kernel
+    assert _gemv([_m(d=4, nbits=12)], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # one token
+    assert _gemv([_m(d=4, nbits=12, K=16640)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED
+    assert _gemv([_m(d=8, nbits=16)], ok_x, 17, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # <= 16 tokens
+    # one kernel per call: every matrix of a group has the same (d, nbits)
+    assert _gemv([_m(), _m(d=4, nbits=12)], ok_x * 2, 1, ok_y * 2, None, 0) == vq.VQ_EUNSUPPORTED
+    # the virtual-codebook formats take no workspace
+    assert vq.vq_workspace_bytes([_m(d=4, nbits=12)], 1) == 0
+    assert vq.vq_workspace_bytes([_m(d=8, nbits=16)], 16) == 0
     assert _gemv([_m(K=1088)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # K % 256
     assert _gemv([_m()], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED        # B = 2
     assert _gemv([_m(wi=FAKE + 8)], ok_x, 1, ok_y, None, 0) == vq.VQ_EALIGN
@@ -94,6 +109,7 @@ def test_gemv_residual_validation_errors():
     ok_x, ok_y = [FAKE], [FAKE]
     assert _gemv([_m(signs=None)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
     assert _gemv([_m(group=64)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
+    assert _gemv([_m(d=4, nbits=12)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(rht_sign=FAKE, had_block=3)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
     assert _gemv([_m(rht_sign=FAKE, had_block=2048)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
     assert _gemv([_m(rht_sign=FAKE, had_block=1024)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EWORKSPACE

@@ -360,3 +360,28 @@ def test_compare_metrics():
     y_ref = np.array([3.0, 4.0])
     rel, mx, rms = o.compare(np.array([3.0, 4.5]), y_ref)
     assert abs(rel - 0.1) < 1e-15 and mx == 0.5 and abs(rms - math.sqrt(12.5)) < 1e-15
+
+
+def test_dequant_form_matches_lookup_form_and_a_loop():
+    # the two definitions agree (reassociation of one sum), and the dequant
+    # form agrees with an explicit triple loop on a tiny case
+    rng = np.random.default_rng(31)
+    for (K, N, d, nb, B) in [(16, 5, 4, 2, 1), (32, 7, 8, 6, 3), (64, 9, 4, 12, 2), (32, 4, 8, 16, 2)]:
+        J = K // d
+        x = rng.standard_normal((B, K)).astype(np.float16)
+        wc = rng.normal(0, 0.02, size=(1 << nb, d)).astype(np.float16)
+        idx = rng.integers(0, 1 << nb, size=(N, J))
+        packed = o.pack_rows(idx, nb)
+        a = o.dequant_gemv(x, wc, packed, N, K, d, nb)
+        b = o.vq_gemv(x, wc, packed, N, K, d, nb)
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+    x = np.array([[1.0, -2.0, 0.5, 4.0]], dtype=np.float16)
+    wc = np.array([[0.25, 1.0], [-0.5, 2.0], [1.5, -1.0], [0.0, 0.75]], dtype=np.float16)
+    idx = np.array([[2, 1], [0, 3], [3, 3]])
+    y = o.dequant_gemv(x, wc, o.pack_rows(idx, 4), 3, 4, 2, 4)
+    ref = np.zeros((1, 3))
+    for r in range(3):
+        for j in range(2):
+            for t in range(2):
+                ref[0, r] += float(x[0, 2 * j + t]) * float(wc[idx[r, j], t])
+    assert np.array_equal(y, ref)

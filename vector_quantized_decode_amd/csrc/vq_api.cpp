@@ -102,6 +102,19 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residua
   p.bytes = off;
 }
 
+// ---------------------------------------------------------------- formats
+// (d, nbits) pairs with a kernel: the 8-bit output-codebook tile kernels, and
+// the virtual-OC kernels for 4096 and 65536 centroids.
+enum Format { FMT_NONE = 0, FMT_LUT8, FMT_WC12, FMT_WC16 };
+
+static Format format_of(int32_t d, int32_t nbits) {
+  if (d == 4 && nbits == 8) return FMT_LUT8;
+  if (d == 4 && nbits == 12) return FMT_WC12;
+  if (d == 8 && nbits == 16) return FMT_WC16;
+  return FMT_NONE;
+}
+static Format format_of(const vq_matrix &a) { return format_of(a.d, a.nbits); }
+
 // ---------------------------------------------------------------- validation
 static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
   if (a.K <= 0 || a.N <= 0) return VQ_EINVAL;
@@ -117,9 +130,13 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
       if (!is_pow2(a.had_block) || a.had_block > 16384 || a.K % a.had_block) return VQ_EINVAL;
     }
   }
-  if (!(a.d == 4 && a.nbits == 8)) return VQ_EUNSUPPORTED;
+  switch (format_of(a)) {
+    case FMT_LUT8: if (B != 1) return VQ_EUNSUPPORTED; break;
+    case FMT_WC12: if (residual || B != 1 || a.K / 4 > 4096) return VQ_EUNSUPPORTED; break;
+    case FMT_WC16: if (residual || B > 16) return VQ_EUNSUPPORTED; break;
+    default: return VQ_EUNSUPPORTED;
+  }
   if (a.K % 256) return VQ_EUNSUPPORTED;
-  if (B != 1) return VQ_EUNSUPPORTED;
   if (!aligned(a.wi, 16) || !aligned(a.wc, 16)) return VQ_EALIGN;
   if (residual && (!aligned(a.signs, 16) || !aligned(a.alpha, 32))) return VQ_EALIGN;
   return VQ_OK;
@@ -133,6 +150,7 @@ static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const 
   for (int i = 0; i < count; ++i) {
     const int st = check_matrix(m[i], B, residual);
     if (st != VQ_OK) return st;
+    if (format_of(m[i]) != format_of(m[0])) return VQ_EUNSUPPORTED;   // one kernel per call
     if (!x[i] || !y[i]) return VQ_EINVAL;
     if (!aligned(x[i], 16)) return VQ_EALIGN;
     if (!aligned(y[i], 4)) return VQ_EALIGN;
@@ -140,10 +158,41 @@ static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const 
   return VQ_OK;
 }
 
+// Virtual-OC kernels: whole rows per workgroup, no workspace.
+static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                   float *const *y, void *stream) {
+  const Format f = format_of(m[0]);
+  const int R = (f == FMT_WC12) ? wc12_rows_per_wg() : wc16_rows_per_wg();
+  WcArgs args;
+  memset(&args, 0, sizeof(args));
+  args.count = count;
+  int64_t max_wg = 0;
+  int max_j = 0;
+  for (int i = 0; i < count; ++i) {
+    WcMat &d = args.mat[i];
+    d.wi = static_cast<const uint8_t *>(m[i].wi);
+    d.wc = m[i].wc;
+    d.x = x[i];
+    d.y = y[i];
+    d.J = m[i].K / m[i].d;
+    d.N = m[i].N;
+    d.B = B;
+    d.ldy = m[i].N;
+    d.nwg = (m[i].N + R - 1) / R;
+    if (d.nwg > max_wg) max_wg = d.nwg;
+    if (d.J > max_j) max_j = d.J;
+  }
+  if (max_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
+  const int err = (f == FMT_WC12) ? launch_wc12(args, (int)max_wg, max_j, stream)
+                                  : launch_wc16(args, (int)max_wg, stream);
+  return hip_status(err);
+}
+
 static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                        float *const *y, void *workspace, size_t ws_bytes, void *stream, bool residual) {
   int st = check_group(m, count, x, B, y, residual);
   if (st != VQ_OK) return st;
+  if (format_of(m[0]) != FMT_LUT8) return gemv_wc(m, count, x, B, y, stream);
   Plan p;
   make_plan(m, count, B, residual, p);
   if (p.grid > 0x7fffffff) return VQ_EUNSUPPORTED;
@@ -218,10 +267,14 @@ const char *vq_last_error(void) {
 
 size_t vq_wi_device_bytes(int32_t N, int32_t K, int32_t d, int32_t nbits) {
   if (N <= 0 || K <= 0 || d <= 0 || K % d) return 0;
-  if (nbits != 8) return 0;
   const int64_t J = K / d;
-  if (J % 64) return 0;
-  return (size_t)((N + 15) / 16) * 16 * (size_t)J;
+  const size_t rows = (size_t)((N + 15) / 16) * 16;
+  switch (format_of(d, nbits)) {
+    case FMT_LUT8: return (J % 64) ? 0 : rows * (size_t)J;
+    case FMT_WC12: return (J % 64) ? 0 : rows * (size_t)J * 3 / 2;
+    case FMT_WC16: return (J % 32) ? 0 : rows * (size_t)J * 2;
+    default: return 0;
+  }
 }
 
 size_t vq_signs_device_bytes(int32_t N, int32_t K) {
@@ -241,6 +294,7 @@ size_t vq_workspace_bytes(const vq_matrix *m, int32_t count, int32_t B, int32_t 
     const vq_matrix &a = m[i];
     if (a.K <= 0 || a.N <= 0 || a.d <= 0 || a.K % a.d) return 0;
   }
+  if (format_of(m[0]) != FMT_LUT8) return 0;     // the virtual-OC kernels use none
   Plan p;
   make_plan(m, count, B, residual != 0, p);
   return p.bytes;
@@ -275,7 +329,15 @@ int vq_repack_wi(const uint8_t *canonical, int32_t N, int32_t K, int32_t d, int3
   if (N <= 0 || K <= 0 || d <= 0 || K % d || nbits < 1 || nbits > 16) return VQ_EINVAL;
   if (vq_wi_device_bytes(N, K, d, nbits) == 0) return VQ_EUNSUPPORTED;
   if (!aligned(device_layout, 16)) return VQ_EALIGN;
-  return hip_status(launch_repack_wi8(canonical, N, K / d, static_cast<uint8_t *>(device_layout), stream));
+  uint8_t *dev = static_cast<uint8_t *>(device_layout);
+  switch (format_of(d, nbits)) {
+    case FMT_LUT8: return hip_status(launch_repack_wi8(canonical, N, K / d, dev, stream));
+    case FMT_WC12: return hip_status(launch_repack_wi12(canonical, N, K / d, dev, stream));
+    case FMT_WC16:
+      if (!aligned(canonical, 2)) return VQ_EALIGN;
+      return hip_status(launch_repack_wi16(canonical, N, K / d, dev, stream));
+    default: return VQ_EUNSUPPORTED;
+  }
 }
 
 int vq_repack_signs(const uint8_t *canonical, int32_t N, int32_t K, void *device_layout, void *stream) {

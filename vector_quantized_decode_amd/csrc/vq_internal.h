@@ -37,6 +37,31 @@ struct Lut8Args {
   int32_t count;
 };
 
+// Per-matrix descriptor of the virtual-OC kernels (n = 12 and n = 16).
+struct WcMat {
+  const uint8_t *wi;      // WI, device layout tile-16x64-12 or tile-16x32-16
+  const uint16_t *wc;     // fp16 codebook [2^n][d]
+  const uint16_t *x;      // fp16 input [B][K]
+  float *y;               // fp32 output [B][N], row stride ldy
+  int32_t J;              // subvectors per row, K/d
+  int32_t N;              // output rows
+  int32_t B;              // tokens
+  int32_t ldy;            // y row stride (N)
+  int32_t nwg;            // workgroups of this matrix
+};
+
+struct WcArgs {
+  WcMat mat[VQ_MAX_GROUP];
+  int32_t count;
+};
+
+int wc12_rows_per_wg();
+int wc16_rows_per_wg();
+int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
+int launch_wc16(const WcArgs &a, int grid_x, void *stream);
+int launch_repack_wi12(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
+int launch_repack_wi16(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
+
 // Launch shape of one lookup-kernel variant.
 struct Lut8Shape {
   int nsub;     // 64-subvector tiles per workgroup (1 or 2)

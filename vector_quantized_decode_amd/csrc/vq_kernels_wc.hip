@@ -1,0 +1,358 @@
+// HIP kernels of libvqd for large codebooks (gfx950): the output codebook is
+// kept virtual -- each entry OC[j][c] = x_j . WC[c] is formed when an index
+// asks for it.
+//
+// Sources, cited by page title and section:
+//   [EVA]  "EVA: Accelerating LLM Decoding via an Efficient Vector
+//          Quantization Architecture" -- explainer page, technical summary,
+//          section 2.A (input-codebook products form the output codebook;
+//          lookups into it by the weight indices) and section 2.B (the
+//          codebooks stay on chip while indices stream in tiles).
+//
+// Why virtual.  A workgroup that owns R rows would build 2^n OC entries per
+// subvector for R lookups per subvector.  At n = 8 and R = 512 that is half an
+// entry per lookup and the OC tile pays for itself (vq_kernels.hip).  At
+// n = 12 (4096 centroids) the rows of a matrix number 4096-11008, so any tile
+// costs at least one entry -- one LDS store -- per lookup, and splitting the
+// subvectors over workgroups adds a cross-workgroup hand-off.  Forming the
+// entry at lookup time costs the same arithmetic (a d-term dot product) and
+// needs only the codebook on chip:
+//   * wc12_kernel (d = 4, n = 12, one token): WC (4096 x 4 fp16, 32 KiB) and
+//     x sit in LDS; a lane owns one subvector j, reads WC[c] (8 bytes) for each
+//     index and adds x_j . WC[c] with two packed fp16 dot products into fp32.
+//     Each workgroup covers whole rows: no partial sums leave it.
+//   * wc16_kernel (d = 8, n = 16, up to 16 tokens): the codebook (65536 x 8
+//     fp16, 1 MiB) does not fit in LDS and is gathered from the caches; the
+//     16-token contraction sum_j x_b,j . WC[c_rj] runs on the matrix cores,
+//     one v_mfma_f32_16x16x32_f16 per 16 rows x 4 subvectors, where a lane's
+//     gathered codebook row is exactly its 8-element slice of the B operand.
+#include <hip/hip_runtime.h>
+
+#include "vq_internal.h"
+
+namespace vqd {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+__device__ __forceinline__ half2_t h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ float f_of(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t u_of(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+constexpr int WDPP_QUAD_XOR1 = 0xB1;
+constexpr int WDPP_QUAD_XOR2 = 0x4E;
+constexpr int WDPP_ROW_ROR8 = 0x128;
+constexpr int WDPP_ROW_HALF_MIRROR = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float wdpp(float v) {
+  return f_of((uint32_t)__builtin_amdgcn_update_dpp(0, (int)u_of(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void wswap32(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(u_of(a), u_of(b), false, false);
+  a = f_of(r[0]);
+  b = f_of(r[1]);
+}
+__device__ __forceinline__ void wswap16(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(u_of(a), u_of(b), false, false);
+  a = f_of(r[0]);
+  b = f_of(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float wtstage(float lo, float hi, bool bit) {
+  const float send = bit ? lo : hi;
+  const float keep = bit ? hi : lo;
+  return keep + wdpp<CTRL>(send);
+}
+// a[0..15]: per-lane partial sums of rows 0..15 -> full 64-lane sum of row
+// (lane >> 2) & 15 in every lane (transposing butterfly, [EVA] 2.B adder tree)
+__device__ __forceinline__ float wreduce_rows16(float (&a)[16], int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { wswap32(a[i], a[i + 8]); a[i] += a[i + 8]; }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { wswap16(a[i], a[i + 4]); a[i] += a[i + 4]; }
+  const bool b3 = lane & 8, b2 = lane & 4;
+  a[0] = wtstage<WDPP_ROW_ROR8>(a[0], a[2], b3);
+  a[1] = wtstage<WDPP_ROW_ROR8>(a[1], a[3], b3);
+  float v = wtstage<WDPP_ROW_HALF_MIRROR>(a[0], a[1], b2);
+  v += wdpp<WDPP_QUAD_XOR1>(v);
+  v += wdpp<WDPP_QUAD_XOR2>(v);
+  return v;
+}
+
+// --------------------------------------------------------------------------
+// d = 4, n = 12, one token
+// --------------------------------------------------------------------------
+// Byte address in LDS of WC[c] for index i (0..7) of a 96-bit group of eight
+// 12-bit indices (index i in bits [12 i, 12 i + 12)), times 8 bytes per entry.
+template <int I>
+__device__ __forceinline__ uint32_t wc12_addr(uint32_t w0, uint32_t w1, uint32_t w2) {
+  uint32_t c;
+  if (I == 0) c = w0 & 0xfffu;
+  else if (I == 1) c = (w0 >> 12) & 0xfffu;
+  else if (I == 2) c = __builtin_amdgcn_alignbit(w1, w0, 24) & 0xfffu;
+  else if (I == 3) c = (w1 >> 4) & 0xfffu;
+  else if (I == 4) c = (w1 >> 16) & 0xfffu;
+  else if (I == 5) c = __builtin_amdgcn_alignbit(w2, w1, 28) & 0xfffu;
+  else if (I == 6) c = (w2 >> 8) & 0xfffu;
+  else c = w2 >> 20;
+  return c << 3;
+}
+
+__device__ __forceinline__ uint2 lds_u2(const char *base, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint2 *>(base + byte_addr);
+}
+
+// One 64-subvector chunk of 16 rows: w[0..2] rows 0-7, w[3..5] rows 8-15.
+__device__ __forceinline__ void wc12_chunk(float (&acc)[16], const uint32_t (&w)[6], uint2 xj,
+                                           const char *wc) {
+#define WC12_ONE(R, I, A, B, C)                                            \
+  {                                                                        \
+    const uint2 e = lds_u2(wc, wc12_addr<I>(A, B, C));                     \
+    acc[R] = __builtin_amdgcn_fdot2(h2(xj.x), h2(e.x), acc[R], false);     \
+    acc[R] = __builtin_amdgcn_fdot2(h2(xj.y), h2(e.y), acc[R], false);     \
+  }
+  WC12_ONE(0, 0, w[0], w[1], w[2]) WC12_ONE(1, 1, w[0], w[1], w[2])
+  WC12_ONE(2, 2, w[0], w[1], w[2]) WC12_ONE(3, 3, w[0], w[1], w[2])
+  WC12_ONE(4, 4, w[0], w[1], w[2]) WC12_ONE(5, 5, w[0], w[1], w[2])
+  WC12_ONE(6, 6, w[0], w[1], w[2]) WC12_ONE(7, 7, w[0], w[1], w[2])
+  WC12_ONE(8, 0, w[3], w[4], w[5]) WC12_ONE(9, 1, w[3], w[4], w[5])
+  WC12_ONE(10, 2, w[3], w[4], w[5]) WC12_ONE(11, 3, w[3], w[4], w[5])
+  WC12_ONE(12, 4, w[3], w[4], w[5]) WC12_ONE(13, 5, w[3], w[4], w[5])
+  WC12_ONE(14, 6, w[3], w[4], w[5]) WC12_ONE(15, 7, w[3], w[4], w[5])
+#undef WC12_ONE
+}
+
+__device__ __forceinline__ void load_chunk12(uint32_t (&w)[6], const uint8_t *p) {
+  const u32x3 a = *reinterpret_cast<const u32x3 *>(p);
+  const u32x3 b = *reinterpret_cast<const u32x3 *>(p + 12);
+  w[0] = a[0]; w[1] = a[1]; w[2] = a[2];
+  w[3] = b[0]; w[4] = b[1]; w[5] = b[2];
+}
+
+// Workgroup: W waves, wave w owns the 16 rows of row group blockIdx.x * W + w
+// and walks all J/64 subvector chunks, PF chunks of indices in flight.
+// Dynamic LDS: WC (32 KiB) then x (J * 8 bytes).
+template <int W, int PF>
+__global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
+  extern __shared__ __align__(16) char smem[];
+  const WcMat &M = args.mat[blockIdx.y];
+  if ((int)blockIdx.x >= M.nwg) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int JT = M.J >> 6;
+  const int NG = (M.N + 15) >> 4;
+  const int rg = min((int)blockIdx.x * W + wave, NG - 1);
+  char *wc = smem;
+  char *xs = smem + 4096 * 8;
+
+  // 1. codebook and x into LDS (16-byte pieces), issued before the index stream
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(M.wc);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(wc);
+    for (int t = threadIdx.x; t < 2048; t += W * 64) dst[t] = src[t];
+    const u32x4 *xsrc = reinterpret_cast<const u32x4 *>(M.x);
+    u32x4 *xdst = reinterpret_cast<u32x4 *>(xs);
+    for (int t = threadIdx.x; t < (M.J >> 1); t += W * 64) xdst[t] = xsrc[t];
+  }
+  // 2. first PF chunks of this wave's rows (24 bytes per lane each)
+  const uint8_t *wi = M.wi + ((size_t)rg * JT * 64 + lane) * 24;
+  uint32_t buf[PF][6];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_chunk12(buf[p], wi + (size_t)min(p, JT - 1) * 64 * 24);
+  __syncthreads();
+
+  // 3. lookups: OC[j][c] = x_j . WC[c] formed per index, summed per row
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const uint2 *xl = reinterpret_cast<const uint2 *>(xs) + lane;
+  for (int k0 = 0; k0 < JT; k0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int k = k0 + p;
+      uint32_t cur[6];
+#pragma unroll
+      for (int q = 0; q < 6; ++q) cur[q] = buf[p][q];
+      // refill this slot with chunk k + PF (clamped: in-bounds, unused)
+      load_chunk12(buf[p], wi + (size_t)min(k + PF, JT - 1) * 64 * 24);
+      if (k < JT) wc12_chunk(acc, cur, xl[k * 64], wc);
+    }
+  }
+
+  // 4. rows out: lane 4r holds row r of the 16
+  const float v = wreduce_rows16(acc, lane);
+  const int row = ((int)blockIdx.x * W + wave) * 16 + ((lane >> 2) & 15);
+  if ((lane & 3) == 0 && (int)blockIdx.x * W + wave < NG && row < M.N) M.y[row] = v;
+}
+
+// --------------------------------------------------------------------------
+// d = 8, n = 16, up to 16 tokens
+// --------------------------------------------------------------------------
+// Wave = 16 rows x all tokens x all J subvectors.  Index chunk (row group rg,
+// subvector block jb of 32): lane l holds 8 uint16 indices, the q-th of row
+// 16 rg + l%16 at subvector 32 jb + l/16 + 4 q.  MFMA q of the block contracts
+// subvectors 32 jb + 4 q .. + 3: lane l's A slice is x[token l%16] at those
+// subvectors' 8 inputs (l/16 picks the subvector), its B slice the gathered
+// WC row of its own index.  D[token][row]: lane l holds tokens 4(l/16) .. +3
+// of row l%16.
+template <int W>
+__global__ void __launch_bounds__(W * 64) wc16_kernel(const WcArgs args) {
+  const WcMat &M = args.mat[blockIdx.y];
+  if ((int)blockIdx.x >= M.nwg) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int JB = M.J >> 5;
+  const int NG = (M.N + 15) >> 4;
+  const int rgw = (int)blockIdx.x * W + wave;
+  const int rg = min(rgw, NG - 1);
+  const int tok = lane & 15, sub = lane >> 4;
+  const bool has_tok = tok < M.B;
+  const int K = M.J * 8;
+  const uint8_t *xrow = reinterpret_cast<const uint8_t *>(M.x) + (size_t)(has_tok ? tok : 0) * K * 2;
+  const uint8_t *wcb = reinterpret_cast<const uint8_t *>(M.wc);
+  const uint8_t *wi = M.wi + ((size_t)rg * JB * 64 + lane) * 16;
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  u32x4 idx = *reinterpret_cast<const u32x4 *>(wi);
+  for (int jb = 0; jb < JB; ++jb) {
+    // gathers of this block, then the next block's indices
+    half8_t b[8], a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t c = (idx[q >> 1] >> ((q & 1) * 16)) & 0xffffu;
+      b[q] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4 *>(wcb + (size_t)c * 16));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = jb * 32 + 4 * q + sub;
+      const u32x4 xv = has_tok ? *reinterpret_cast<const u32x4 *>(xrow + (size_t)j * 16)
+                               : u32x4{0u, 0u, 0u, 0u};
+      a[q] = __builtin_bit_cast(half8_t, xv);
+    }
+    idx = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb + 1, JB - 1) * 64 * 16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[q], acc, 0, 0, 0);
+  }
+  if (rgw < NG) {
+    const int row = rgw * 16 + tok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = sub * 4 + i;
+      if (t < M.B && row < M.N) M.y[(size_t)t * M.ldy + row] = acc[i];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// device layouts
+// --------------------------------------------------------------------------
+// canonical 12-bit rows ([N] rows of J indices, LSB-first bit stream, each row
+// 1.5 J bytes) -> tile-16x64-12: chunk (rg, jt), lane l = subvector 64 jt + l,
+// 24 bytes = indices of rows 16 rg + i (i < 16) at bits [12 i, 12 i + 12)
+__global__ void repack_wi12_kernel(const uint8_t *canon, int N, int J, uint8_t *dev) {
+  const int NG = (N + 15) >> 4, JT = J >> 6;
+  const int64_t total = (int64_t)NG * JT * 64;
+  const int64_t rb = (int64_t)J * 3 / 2;   // bytes per canonical row
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(e & 63);
+    const int64_t chunk = e >> 6;
+    const int jt = (int)(chunk % JT);
+    const int rg = (int)(chunk / JT);
+    const int j = jt * 64 + l;
+    uint32_t out[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+    for (int i = 0; i < 16; ++i) {
+      const int r = rg * 16 + i;
+      uint32_t c = 0u;
+      if (r < N) {
+        const int64_t bit = (int64_t)j * 12;
+        const uint8_t *p = canon + (int64_t)r * rb + (bit >> 3);
+        const uint32_t two = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+        c = (two >> (bit & 7)) & 0xfffu;
+      }
+      const int q = i >> 3, ib = (i & 7) * 12;     // 96-bit half q, bit offset ib
+      const int w = ib >> 5, s = ib & 31;
+      out[q * 3 + w] |= c << s;
+      if (s > 20) out[q * 3 + w + 1] |= c >> (32 - s);
+    }
+    uint8_t *d = dev + e * 24;
+    for (int q = 0; q < 6; ++q) *reinterpret_cast<uint32_t *>(d + 4 * q) = out[q];
+  }
+}
+
+// canonical 16-bit rows (little-endian uint16, [N][J]) -> tile-16x32-16:
+// chunk (rg, jb), lane l holds the indices of row 16 rg + l%16 at subvectors
+// 32 jb + l/16 + 4 q, q < 8
+__global__ void repack_wi16_kernel(const uint8_t *canon, int N, int J, uint8_t *dev) {
+  const int NG = (N + 15) >> 4, JB = J >> 5;
+  const int64_t total = (int64_t)NG * JB * 64;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(e & 63);
+    const int64_t chunk = e >> 6;
+    const int jb = (int)(chunk % JB);
+    const int rg = (int)(chunk / JB);
+    const int r = rg * 16 + (l & 15);
+    uint16_t v[8];
+    for (int q = 0; q < 8; ++q) {
+      const int j = jb * 32 + (l >> 4) + 4 * q;
+      v[q] = (r < N) ? reinterpret_cast<const uint16_t *>(canon)[(int64_t)r * J + j] : (uint16_t)0;
+    }
+    uint16_t *d = reinterpret_cast<uint16_t *>(dev + e * 16);
+    for (int q = 0; q < 8; ++q) d[q] = v[q];
+  }
+}
+
+// --------------------------------------------------------------------------
+// launchers
+// --------------------------------------------------------------------------
+static int wgrid(int64_t work, int block) {
+  int64_t g = (work + block - 1) / block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (int)g;
+}
+
+constexpr int WC12_W = 4;
+constexpr int WC12_PF = 4;
+constexpr int WC16_W = 4;
+
+int wc12_rows_per_wg() { return WC12_W * 16; }
+int wc16_rows_per_wg() { return WC16_W * 16; }
+
+int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
+  const size_t lds = 4096 * 8 + (size_t)max_j * 8;
+  (void)hipGetLastError();  // report only this launch's error
+  hipLaunchKernelGGL((wc12_kernel<WC12_W, WC12_PF>), dim3(grid_x, a.count), dim3(WC12_W * 64), lds,
+                     reinterpret_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+int launch_wc16(const WcArgs &a, int grid_x, void *stream) {
+  (void)hipGetLastError();  // report only this launch's error
+  hipLaunchKernelGGL((wc16_kernel<WC16_W>), dim3(grid_x, a.count), dim3(WC16_W * 64), 0,
+                     reinterpret_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+int launch_repack_wi12(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream) {
+  const int64_t total = (int64_t)((N + 15) >> 4) * (J >> 6) * 64;
+  (void)hipGetLastError();  // report only this launch's error
+  hipLaunchKernelGGL(repack_wi12_kernel, dim3(wgrid(total, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), canon, N, J, dev);
+  return (int)hipGetLastError();
+}
+
+int launch_repack_wi16(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream) {
+  const int64_t total = (int64_t)((N + 15) >> 4) * (J >> 5) * 64;
+  (void)hipGetLastError();  // report only this launch's error
+  hipLaunchKernelGGL(repack_wi16_kernel, dim3(wgrid(total, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), canon, N, J, dev);
+  return (int)hipGetLastError();
+}
+
+}  // namespace vqd

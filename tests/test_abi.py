@@ -51,7 +51,7 @@ def test_device_layout_sizes():
     assert vq.vq_wi_device_bytes(16, 1024, 4, 10) == 0                # no kernel for (4, 10)
     assert vq.vq_signs_device_bytes(14336, 3584) == 14336 * 448
     assert vq.vq_signs_device_bytes(100, 512) == 128 * 64            # rows padded to 32
-    assert vq.vq_alpha_device_bytes(3584, 14336, 128) == 3584 * 112 * 2
+    assert vq.vq_alpha_device_bytes(3584, 14336, 128) == 3584 * 112 * 2 + 256   # + header
     assert vq.vq_alpha_device_bytes(10, 256, 64) == 0
 
 

@@ -112,7 +112,11 @@ def test_repack_layouts_bitexact(N, K):
     torch.cuda.synchronize()
     assert np.array_equal(dev.cpu().numpy(), _host_wi_layout(canon, N, J))
     assert np.array_equal(sdev.cpu().numpy(), _host_sign_layout(scanon, N, P))
-    assert np.array_equal(adev.cpu().numpy().view(np.uint16), _host_alpha_layout(acanon, N, G))
+    body = _host_alpha_layout(acanon, N, G)
+    got = adev.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[:body.size], body)
+    # header after the tiled scales: the largest fp16 magnitude, as bits
+    assert got[body.size:body.size + 2].view(np.uint32)[0] == int((acanon & 0x7FFF).max())
 
 
 # ------------------------------------------------------------------ OC build
@@ -261,11 +265,17 @@ def test_workspace_reused_across_calls():
 
 
 # ------------------------------------------------------------------ residual
-@pytest.mark.parametrize("K,N,rotate", [(256, 40, True), (1024, 200, True), (1024, 200, False),
-                                        (3584, 300, True), (2048, 1031, True)])
-def test_gemv_residual_shapes(K, N, rotate):
-    _say(f"gemv_residual K={K} N={N} rotate={rotate}")
-    mi = synth.small_matrix(K, N, 4, 8, seed=K * 7 + N, residual=True)
+@pytest.mark.parametrize("K,N,rotate,h", [(256, 40, True, 0), (1024, 200, True, 0), (1024, 200, False, 0),
+                                          (3584, 300, True, 0), (2048, 1031, True, 0), (768, 50, True, 0),
+                                          (1024, 64, True, 64), (512, 33, True, 1), (1024, 96, True, 2),
+                                          (4096, 80, True, 4096), (8192, 100, True, 8192),
+                                          (1024, 3000, True, 0), (2048, 4500, True, 0)])
+def test_gemv_residual_shapes(K, N, rotate, h):
+    # h = 0: the largest power of two dividing K.  Blocks up to 2048 are
+    # rotated inside the lookup kernel (h < 256: whole blocks per tile);
+    # 4096 and 8192 go through the separate rotation kernel.
+    _say(f"gemv_residual K={K} N={N} rotate={rotate} h={h}")
+    mi = synth.small_matrix(K, N, 4, 8, seed=K * 7 + N, residual=True, had_block=h or None)
     m = _upload(mi, residual=True)
     if not rotate:
         m.rht_sign = None
@@ -333,3 +343,12 @@ def test_gemv_nonfinite_input_propagates_like_oracle(bad):
     mi2 = synth.small_matrix(4096, 200, 4, 8, seed=24)
     (y2,), _ = _run_gemv([_upload(mi2)], [mi2.x])
     _assert_close(y2, _oracle_plain(mi2), "after non-finite call")
+
+
+def test_gemv_residual_large_magnitudes():
+    _say("gemv_residual with large x and alpha")
+    mi = synth.small_matrix(3584, 200, 4, 8, seed=77, residual=True)
+    mi.x = (mi.x.astype(np.float64) * 300.0).astype(np.float16)
+    mi.alpha = (mi.alpha.astype(np.float64) * 50.0).astype(np.float16)
+    (y,), _ = _run_gemv([_upload(mi, residual=True)], [mi.x], residual=True)
+    _assert_close(y, _oracle_res(mi), "residual large magnitudes")

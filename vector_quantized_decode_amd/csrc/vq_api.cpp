@@ -48,11 +48,17 @@ Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count) {
   return s;
 }
 
-Lut8Shape lut8_shape_residual(const vq_matrix *, int32_t) {
+Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count) {
+  // two 32-row steps per wave (1024 rows per workgroup) once the matrices are
+  // tall enough to fill them: the per-workgroup OC tile and sign table are
+  // then shared by twice the lookups
+  int64_t max_n = 0;
+  for (int i = 0; i < count; ++i)
+    if (m[i].N > max_n) max_n = m[i].N;
   Lut8Shape s;
   s.nsub = 1;
   s.waves = 16;
-  s.steps = 1;
+  s.steps = max_n > 2048 ? 2 : 1;
   return s;
 }
 
@@ -102,6 +108,14 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residua
   p.bytes = off;
 }
 
+// Alpha device layout: the tiled scales, then a 256-byte header whose first
+// word holds the largest |alpha| as fp16 magnitude bits (written by
+// vq_repack_alpha, read by the residual kernel to scale its hand-off).
+static size_t alpha_body_bytes(int32_t N, int32_t K) {
+  const size_t G = (size_t)(K / 128);
+  return (size_t)((N + 31) / 32) * 32 * ((G + 1) / 2 * 2) * sizeof(uint16_t);
+}
+
 // ---------------------------------------------------------------- formats
 // (d, nbits) pairs with a kernel: the 8-bit output-codebook tile kernels, and
 // the virtual-OC kernels for 4096 and 65536 centroids.
@@ -139,6 +153,7 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
   if (a.K % 256) return VQ_EUNSUPPORTED;
   if (!aligned(a.wi, 16) || !aligned(a.wc, 16)) return VQ_EALIGN;
   if (residual && (!aligned(a.signs, 16) || !aligned(a.alpha, 32))) return VQ_EALIGN;
+  if (residual && a.rht_sign && !aligned(a.rht_sign, 4)) return VQ_EALIGN;
   return VQ_OK;
 }
 
@@ -223,15 +238,27 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
     d.nsplit = q.nsplit;
     d.nrb = q.nrb;
     d.acc = reinterpret_cast<uint64_t *>(ws + q.acc_off);
+    if (residual) {
+      const int h = m[i].rht_sign ? m[i].had_block : 1;
+      d.rs = m[i].rht_sign;
+      d.had = h;
+      d.had_scale = (float)(1.0 / sqrt((double)h));
+      d.alpha_hdr = reinterpret_cast<const uint32_t *>(static_cast<const char *>(m[i].alpha) +
+                                                       alpha_body_bytes(m[i].N, m[i].K));
+      // blocks up to 2048 are rotated inside the lookup kernel; larger ones first
+      // by the rotation kernel, into the workspace
+      if (h > 2048) d.xr = reinterpret_cast<const float *>(ws + q.xrot_off);
+      else d.xr = nullptr;
+    }
     d.nwg = q.nsplit * q.nrb;
     if (d.nwg > max_wg) max_wg = d.nwg;
   }
   int err;
   if (residual) {
     for (int i = 0; i < count; ++i) {
-      const int h = m[i].rht_sign ? m[i].had_block : 1;
-      const float scale = (float)(1.0 / sqrt((double)h));
-      err = launch_rht(x[i], m[i].rht_sign, B, m[i].K, h, scale,
+      if (!args.mat[i].xr) continue;          // rotated inside the lookup kernel
+      const int h = args.mat[i].had;
+      err = launch_rht(x[i], m[i].rht_sign, B, m[i].K, h, args.mat[i].had_scale,
                        reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);
       if (err) return hip_status(err);
     }
@@ -284,8 +311,7 @@ size_t vq_signs_device_bytes(int32_t N, int32_t K) {
 
 size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group) {
   if (N <= 0 || K <= 0 || group != 128 || K % 256) return 0;
-  const size_t G = (size_t)(K / group);
-  return (size_t)((N + 31) / 32) * 32 * ((G + 1) / 2 * 2) * sizeof(uint16_t);
+  return alpha_body_bytes(N, K) + 256;
 }
 
 size_t vq_workspace_bytes(const vq_matrix *m, int32_t count, int32_t B, int32_t residual) {
@@ -352,7 +378,9 @@ int vq_repack_alpha(const uint16_t *canonical, int32_t N, int32_t K, int32_t gro
   if (!canonical || !device_layout || N <= 0 || K <= 0 || group <= 0 || K % group) return VQ_EINVAL;
   if (vq_alpha_device_bytes(N, K, group) == 0) return VQ_EUNSUPPORTED;
   if (!aligned(canonical, 2) || !aligned(device_layout, 32)) return VQ_EALIGN;
-  return hip_status(launch_repack_alpha(canonical, N, K / group, static_cast<uint16_t *>(device_layout), stream));
+  uint32_t *hdr = reinterpret_cast<uint32_t *>(static_cast<char *>(device_layout) + alpha_body_bytes(N, K));
+  return hip_status(launch_repack_alpha(canonical, N, K / group, static_cast<uint16_t *>(device_layout), hdr,
+                                        stream));
 }
 
 int vq_build_oc(const uint16_t *x, int32_t B, int32_t K, int32_t d, int32_t nbits, const uint16_t *wc,

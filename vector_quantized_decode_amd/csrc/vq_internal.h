@@ -22,6 +22,10 @@ struct Lut8Mat {
   float *partial;         // fp32 split partial sums [nsplit][rows_pad]
   uint32_t *counter;      // completion counters [nrb]
   uint64_t *acc;          // packed fixed-point row accumulators [rows_pad]
+  const int8_t *rs;       // residual: rotation signs [K] (+-1), or null
+  const uint32_t *alpha_hdr;  // residual: largest |alpha| (fp16 magnitude bits)
+  float had_scale;        // residual: 1/sqrt(had)
+  int32_t had;            // residual: Hadamard block (1: no rotation)
   int32_t J;              // subvectors per row, K/4
   int32_t N;              // output rows
   int32_t rows_pad;       // rows of the padded layout (multiple of 32)
@@ -85,7 +89,8 @@ int launch_pack(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, voi
 int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out, void *stream);
 int launch_repack_wi8(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
 int launch_repack_signs(const uint8_t *canon, int N, int P, uint8_t *dev, void *stream);
-int launch_repack_alpha(const uint16_t *canon, int N, int G, uint16_t *dev, void *stream);
+int launch_repack_alpha(const uint16_t *canon, int N, int G, uint16_t *dev, uint32_t *hdr,
+                        void *stream);
 int launch_build_oc(const uint16_t *x, int B, int K, int d, int nbits, const uint16_t *wc,
                     void *oc, int f16_out, void *stream);
 int launch_rht(const uint16_t *x, const int8_t *sign, int B, int K, int h, float scale,

@@ -238,6 +238,18 @@ __device__ __forceinline__ float abs_sum8(u32x4 c) {
   }
   return s;
 }
+// Sum of squares of 8 fp16 values (fp32).
+__device__ __forceinline__ float sq_sum8(u32x4 c) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2_t h = as_h2(c[i]);
+    s = __builtin_fmaf((float)h.x, (float)h.x, s);
+    s = __builtin_fmaf((float)h.y, (float)h.y, s);
+  }
+  return s;
+}
+
 // Largest magnitude of 8 fp16 values, compared as integer bits so that an
 // infinity or NaN gives +inf (the caller then leaves the fixed-point path).
 __device__ __forceinline__ float abs_max8(u32x4 c) {
@@ -440,12 +452,28 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
 // 32 sign bytes of the same 256 weights, T[v][p] = sum_i (bit_i(v) ? +1 : -1)
 // * x_rot[8p + i], stored twice (lanes p and p + 32) so that region 1 has the
 // same lane -> bank layout as region 0.
+//
+// The rotation is fused for Hadamard blocks h <= 2048.  In Sylvester (natural)
+// order H_h = H_{h/256} (x) H_256 for h >= 256, so the 256 rotated inputs of a
+// tile, which sit in sub-block q of their block, are the 256-point transform
+// of sum_{q'} (-1)^popcount(q & q') (s (.) x)[sub-block q'].  Every wave forms
+// that combination and the 256-point butterfly in registers (lane l holds
+// elements 4l .. 4l+3, partners across lanes by xor shuffles), ending with
+// x_rot of subvector l in lane l -- no LDS and no barrier.  For h < 256 the
+// tile holds whole blocks and only the butterfly stages below h run.  Larger
+// blocks are rotated by rht_kernel into the workspace first (M.xr).
 // --------------------------------------------------------------------------
+__device__ __forceinline__ float sign_of_byte(uint32_t s4, int t) {
+  return (float)(int8_t)((s4 >> (8 * t)) & 0xffu);
+}
+
 template <int W, int STEPS>
 __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args args) {
-  static_assert(W == 16, "sign-table build assumes 16 waves");
-  __shared__ float lds[2 * 16384 + 16];
-  uint32_t *flag = reinterpret_cast<uint32_t *>(lds + 2 * 16384);
+  static_assert(W == 16, "the OC tile takes waves 0-7, the sign table waves 8-15");
+  constexpr int NT = W * 64;
+  __shared__ float lds[2 * 16384 + 2 * W + 16];
+  float *bnd = lds + 2 * 16384;
+  uint32_t *flag = reinterpret_cast<uint32_t *>(bnd + 2 * W);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Lut8Mat &M = args.mat[blockIdx.y];
@@ -455,66 +483,160 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   const int NG = (M.N + 15) >> 4;
   const int NP = (M.N + 31) >> 5;
   const int half = lane >> 5, pl = lane & 31;
+  const uint8_t *xb = reinterpret_cast<const uint8_t *>(M.x);
+  const uint8_t *wcb = reinterpret_cast<const uint8_t *>(M.wc);
+  const bool oc_wave = wave < 8;
 
-  // 1. loads: per 32-row step, two index chunks, one sign chunk, 16 alphas
+  // 1. small loads first.  Rotation inputs: sub-block u of the tile's
+  //    Hadamard block, elements 4 lane .. 4 lane + 3 (clamped, in bounds).
+  const int h = M.had;                       // 1: no rotation
+  const int k0 = sp * 256;
+  const int QS = h > 256 ? (h >> 8) : 1;
+  const int kb = h > 256 ? (k0 / h) * h : k0;
+  const int qt = h > 256 ? ((k0 - kb) >> 8) : 0;
+  const bool fused = (M.xr == nullptr);
+  uint2 xq[8];
+  uint32_t sq[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = kb + 256 * min(u, QS - 1) + 4 * lane;
+    xq[u] = *reinterpret_cast<const uint2 *>(xb + 2 * (size_t)e);
+    sq[u] = M.rs ? *reinterpret_cast<const uint32_t *>(M.rs + e) : 0x01010101u;
+  }
+  float4 xrw = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!fused) xrw = *reinterpret_cast<const float4 *>(M.xr + k0 + 4 * lane);
+  //    OC waves: centroids 32 wave + (lane % 32) as the MFMA A operand
+  const half4_t wa = __builtin_bit_cast(
+      half4_t, reinterpret_cast<const uint2 *>(M.wc)[(oc_wave ? wave : 0) * 32 + (lane & 31)]);
+  //    bound inputs: x in 16-byte chunks t and t + NT, WC chunk t, max |alpha|
+  const int nxc = M.J >> 1;
+  const int t0 = threadIdx.x, t1 = threadIdx.x + NT;
+  const u32x4 xb0 = load16(xb + 16 * (size_t)min(t0, nxc - 1));
+  const u32x4 xb1 = load16(xb + 16 * (size_t)min(t1, nxc - 1));
+  const u32x4 wb = load16(wcb + 16 * min(t0, 127));
+  const uint32_t amax_bits = *M.alpha_hdr;
+  __builtin_amdgcn_s_barrier();
+
+  // 2. index, sign and alpha loads: per 32-row step, two index chunks, one
+  //    sign chunk, 16 alphas
   u32x4 va[STEPS], vb[STEPS], vs[STEPS], al0[STEPS], al1[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
-    const int rp = (rb * STEPS + g) * W + wave;
-    const int rga = 2 * rp, rgb = 2 * rp + 1;
-    va[g] = (rga < NG) ? load16(M.wi + (((size_t)sp * NG + rga) * 64 + lane) * 16) : u32x4{0u, 0u, 0u, 0u};
-    vb[g] = (rgb < NG) ? load16(M.wi + (((size_t)sp * NG + rgb) * 64 + lane) * 16) : u32x4{0u, 0u, 0u, 0u};
-    if (rp < NP) {
-      vs[g] = load16(M.signs + (((size_t)sp * NP + rp) * 64 + lane) * 16);
-      const uint16_t *ap = M.alpha + (((size_t)sp * NP + rp) * 4 + half * 2 + (pl >> 4)) * 16;
-      al0[g] = *reinterpret_cast<const u32x4 *>(ap);
-      al1[g] = *reinterpret_cast<const u32x4 *>(ap + 8);
-    } else {
-      vs[g] = u32x4{0u, 0u, 0u, 0u};
-      al0[g] = u32x4{0u, 0u, 0u, 0u};
-      al1[g] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int rp = min((rb * STEPS + g) * W + wave, NP - 1);
+    const int rga = min(2 * rp, NG - 1), rgb = min(2 * rp + 1, NG - 1);
+    va[g] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4 *>(M.wi + (((size_t)sp * NG + rga) * 64 + lane) * 16));
+    vb[g] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4 *>(M.wi + (((size_t)sp * NG + rgb) * 64 + lane) * 16));
+    vs[g] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4 *>(M.signs + (((size_t)sp * NP + rp) * 64 + lane) * 16));
+    const uint16_t *ap = M.alpha + (((size_t)sp * NP + rp) * 4 + half * 2 + (pl >> 4)) * 16;
+    al0[g] = *reinterpret_cast<const u32x4 *>(ap);
+    al1[g] = *reinterpret_cast<const u32x4 *>(ap + 8);
   }
 
-  // 2a. OC tile from the rotated input (fp32 x_rot times fp16 codebook)
-  {
-    const int j = sp * 64 + lane;                     // always < J (J % 64 == 0)
-    const float4 xv = *reinterpret_cast<const float4 *>(M.xr + 4 * (size_t)j);
-    const uint32_t *wc32 = reinterpret_cast<const uint32_t *>(M.wc);
-    float *dst = lds + (wave * 16) * 64 + lane;
+  // 3. x_rot of subvector `lane` of this tile
+  float xr[4];
+  if (fused) {
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < QS) {
+        const float sg = (__builtin_popcount(qt & u) & 1) ? -1.f : 1.f;
+        const half2_t a = as_h2(xq[u].x), b = as_h2(xq[u].y);
+        c[0] += sg * sign_of_byte(sq[u], 0) * (float)a.x;
+        c[1] += sg * sign_of_byte(sq[u], 1) * (float)a.y;
+        c[2] += sg * sign_of_byte(sq[u], 2) * (float)b.x;
+        c[3] += sg * sign_of_byte(sq[u], 3) * (float)b.y;
+      }
+    }
+    const int hl = h < 256 ? h : 256;
+    if (hl >= 2) {
+      const float a0 = c[0] + c[1], a1 = c[0] - c[1], a2 = c[2] + c[3], a3 = c[2] - c[3];
+      c[0] = a0; c[1] = a1; c[2] = a2; c[3] = a3;
+    }
+    if (hl >= 4) {
+      const float a0 = c[0] + c[2], a2 = c[0] - c[2], a1 = c[1] + c[3], a3 = c[1] - c[3];
+      c[0] = a0; c[1] = a1; c[2] = a2; c[3] = a3;
+    }
+    for (int m = 1; 4 * m < hl; m <<= 1) {
+      const bool upper = lane & m;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float p = __shfl_xor(c[t], m, 64);
+        c[t] = upper ? (p - c[t]) : (c[t] + p);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xr[t] = c[t] * M.had_scale;
+  } else {
+    xr[0] = xrw.x; xr[1] = xrw.y; xr[2] = xrw.z; xr[3] = xrw.w;
+  }
+
+  if (oc_wave) {
+    // 4. OC tile, centroids 32 wave .. +31, on the matrix cores.  x_rot is
+    //    split into fp16 high and low parts (x = hi + lo to ~2^-22), so two
+    //    fp16 MFMAs give the fp32 product; the output registers are placed as
+    //    in the plain kernel (one centroid per register after the swap).
+    half4_t xh, xl;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const _Float16 hi = (_Float16)xr[t];
+      xh[t] = hi;
+      xl[t] = (_Float16)(xr[t] - (float)hi);
+    }
+    f32x32_t o = {};
+    o = __builtin_amdgcn_mfma_f32_32x32x4f16(wa, xh, o, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_32x32x4f16(wa, xl, o, 0, 0, 0);
+    float *dst = lds + (wave * 32) * 64 + lane;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int c = wave * 16 + i;
-      const half2_t w01 = as_h2(wc32[2 * c]), w23 = as_h2(wc32[2 * c + 1]);
-      float o = xv.x * (float)w01.x;
-      o = __builtin_fmaf(xv.y, (float)w01.y, o);
-      o = __builtin_fmaf(xv.z, (float)w23.x, o);
-      o = __builtin_fmaf(xv.w, (float)w23.y, o);
-      dst[i * 64] = o;
+      float a = o[i], b = o[i + 16];
+      swap32(a, b);
+      const int m = (i >> 2) * 8 + (i & 3);
+      dst[m * 64] = a;
+      dst[(m + 4) * 64] = b;
     }
-  }
-  // 2b. sign table for sign byte p = 32*sp + (lane & 31); wave = high nibble of v
-  {
-    const float *xp = M.xr + 8 * (size_t)(sp * 32 + pl);
-    const float4 lo4 = *reinterpret_cast<const float4 *>(xp);
-    const float4 hi4 = *reinterpret_cast<const float4 *>(xp + 4);
-    const float S = ((lo4.x + lo4.y) + (lo4.z + lo4.w)) + ((hi4.x + hi4.y) + (hi4.z + hi4.w));
-    const int hi = wave;
-    const float H = ((hi & 1) ? hi4.x : 0.f) + ((hi & 2) ? hi4.y : 0.f) +
-                    ((hi & 4) ? hi4.z : 0.f) + ((hi & 8) ? hi4.w : 0.f);
-    const float c0 = 2.f * H - S;
+  } else {
+    // 5. sign table for sign byte p = 32*sp + (lane & 31): the 8 rotated
+    //    inputs 8p .. 8p+7 live in lanes 2p (first four) and 2p+1; this wave
+    //    writes high nibbles 2 (wave - 8) and 2 (wave - 8) + 1
+    float lo4[4], hi4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      lo4[t] = __shfl(xr[t], 2 * pl, 64);
+      hi4[t] = __shfl(xr[t], 2 * pl + 1, 64);
+    }
+    const float S = ((lo4[0] + lo4[1]) + (lo4[2] + lo4[3])) + ((hi4[0] + hi4[1]) + (hi4[2] + hi4[3]));
     float L[16];
     L[0] = 0.f;
-    const float xl[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
 #pragma unroll
-    for (int lo = 1; lo < 16; ++lo) L[lo] = L[lo & (lo - 1)] + xl[__builtin_ctz(lo)];
-    float *dst = lds + 16384 + (hi * 16) * 64 + lane;
+    for (int lo = 1; lo < 16; ++lo) L[lo] = L[lo & (lo - 1)] + lo4[__builtin_ctz(lo)];
 #pragma unroll
-    for (int lo = 0; lo < 16; ++lo) dst[lo * 64] = __builtin_fmaf(2.f, L[lo], c0);
+    for (int e = 0; e < 2; ++e) {
+      const int hi = 2 * (wave - 8) + e;
+      const float H = ((hi & 1) ? hi4[0] : 0.f) + ((hi & 2) ? hi4[1] : 0.f) +
+                      ((hi & 4) ? hi4[2] : 0.f) + ((hi & 8) ? hi4[3] : 0.f);
+      const float c0 = 2.f * H - S;
+      float *dst = lds + 16384 + (hi * 16) * 64 + lane;
+#pragma unroll
+      for (int lo = 0; lo < 16; ++lo) dst[lo * 64] = __builtin_fmaf(2.f, L[lo], c0);
+    }
   }
+  // 6. per-wave parts of the bound sum_k |x_rot_k| <= sqrt(K) ||x||_2
+  {
+    float s2 = 0.f;
+    if (t0 < nxc) s2 += sq_sum8(xb0);
+    if (t1 < nxc) s2 += sq_sum8(xb1);
+    for (int t = t0 + 2 * NT; t < nxc; t += NT) s2 += sq_sum8(load16(xb + 16 * (size_t)t));
+    const float mw = (t0 < 128) ? abs_max8(wb) : 0.f;
+    const float ws = wave_sum(s2), wm = wave_max(mw);
+    if (lane == 0) { bnd[wave] = ws; bnd[W + wave] = wm; }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
-  // 3. lookups
+  // 7. lookups
   const uint32_t base0 = (uint32_t)lane << 2;
   const uint32_t base1 = base0 | 0x10000u;
   float rowval[STEPS];
@@ -522,48 +644,67 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   for (int g = 0; g < STEPS; ++g) {
     float A[16], Bv[16], S[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { A[i] = 0.f; Bv[i] = 0.f; }
-#pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t wa = va[g][q], wb = vb[g][q];
-      A[4 * q + 0] = lds_at(lds, lut_addr<0>(wa, base0));
-      A[4 * q + 1] = lds_at(lds, lut_addr<1>(wa, base0));
-      A[4 * q + 2] = lds_at(lds, lut_addr<2>(wa, base0));
-      A[4 * q + 3] = lds_at(lds, lut_addr<3>(wa, base0));
-      Bv[4 * q + 0] = lds_at(lds, lut_addr<0>(wb, base0));
-      Bv[4 * q + 1] = lds_at(lds, lut_addr<1>(wb, base0));
-      Bv[4 * q + 2] = lds_at(lds, lut_addr<2>(wb, base0));
-      Bv[4 * q + 3] = lds_at(lds, lut_addr<3>(wb, base0));
+      const uint32_t wq = va[g][q], wbq = vb[g][q];
+      A[4 * q + 0] = lds_at(lds, lut_addr<0>(wq, base0));
+      A[4 * q + 1] = lds_at(lds, lut_addr<1>(wq, base0));
+      A[4 * q + 2] = lds_at(lds, lut_addr<2>(wq, base0));
+      A[4 * q + 3] = lds_at(lds, lut_addr<3>(wq, base0));
+      Bv[4 * q + 0] = lds_at(lds, lut_addr<0>(wbq, base0));
+      Bv[4 * q + 1] = lds_at(lds, lut_addr<1>(wbq, base0));
+      Bv[4 * q + 2] = lds_at(lds, lut_addr<2>(wbq, base0));
+      Bv[4 * q + 3] = lds_at(lds, lut_addr<3>(wbq, base0));
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t ws = vs[g][q];
+      const uint32_t ws4 = vs[g][q];
       const uint32_t a01 = (q < 2) ? al0[g][2 * q] : al1[g][2 * q - 4];
       const uint32_t a23 = (q < 2) ? al0[g][2 * q + 1] : al1[g][2 * q - 3];
       const half2_t h01 = as_h2(a01), h23 = as_h2(a23);
-      S[4 * q + 0] = (float)h01.x * lds_at(lds, lut_addr<0>(ws, base1));
-      S[4 * q + 1] = (float)h01.y * lds_at(lds, lut_addr<1>(ws, base1));
-      S[4 * q + 2] = (float)h23.x * lds_at(lds, lut_addr<2>(ws, base1));
-      S[4 * q + 3] = (float)h23.y * lds_at(lds, lut_addr<3>(ws, base1));
+      S[4 * q + 0] = (float)h01.x * lds_at(lds, lut_addr<0>(ws4, base1));
+      S[4 * q + 1] = (float)h01.y * lds_at(lds, lut_addr<1>(ws4, base1));
+      S[4 * q + 2] = (float)h23.x * lds_at(lds, lut_addr<2>(ws4, base1));
+      S[4 * q + 3] = (float)h23.y * lds_at(lds, lut_addr<3>(ws4, base1));
     }
     rowval[g] = reduce_rows32(A, Bv, S, lane);
   }
 
-  // 4. lane 2r holds row r of the 32-row group
+  // 8. rows out: lane 2r holds row r of each 32-row group
   const int rsel = (lane >> 1) & 31;
+  if (M.nsplit == 1) {
+#pragma unroll
+    for (int g = 0; g < STEPS; ++g) {
+      const int rp = (rb * STEPS + g) * W + wave;
+      const int row = rp * 32 + rsel;
+      if ((lane & 1) == 0 && rp < NP && row < M.N) M.y[row] = rowval[g];
+    }
+    return;
+  }
+  float X2 = 0.f, Mw = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) { X2 += bnd[w]; Mw = fmaxf(Mw, bnd[W + w]); }
+  const float amax = (amax_bits & 0x7fffu) >= 0x7c00u
+                         ? __builtin_inff()
+                         : (float)__builtin_bit_cast(_Float16, (uint16_t)(amax_bits & 0x7fffu));
+  const float bound = __builtin_sqrtf((float)(M.J * 4) * X2) * (Mw + amax) * 1.0009765625f;
+  if (bound <= 3.0e38f && M.nsplit <= 127) {
+    const FixedScale fs = fixed_scale(bound);
+#pragma unroll
+    for (int g = 0; g < STEPS; ++g) {
+      const int rp = (rb * STEPS + g) * W + wave;
+      const int row = rp * 32 + rsel;
+      if ((lane & 1) == 0 && rp < NP && row < M.N)
+        packed_add_finish(M.acc + row, M.y + row, rowval[g], fs, M.nsplit);
+    }
+    return;
+  }
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     const int rp = (rb * STEPS + g) * W + wave;
     const int row = rp * 32 + rsel;
-    if ((lane & 1) == 0 && rp < NP) {
-      if (M.nsplit == 1) {
-        if (row < M.N) M.y[row] = rowval[g];
-      } else {
-        store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
-      }
-    }
+    if ((lane & 1) == 0 && rp < NP) store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
   }
-  if (M.nsplit > 1) split_finish(M, rb, STEPS * W * 32, flag);
+  split_finish(M, rb, STEPS * W * 32, flag);
 }
 
 // --------------------------------------------------------------------------
@@ -592,6 +733,11 @@ int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void
   if (s.waves == 16 && s.steps == 1) {
     (void)hipGetLastError();  // report only this launch's error
     hipLaunchKernelGGL((lut8_residual_kernel<16, 1>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
+    return (int)hipGetLastError();
+  }
+  if (s.waves == 16 && s.steps == 2) {
+    (void)hipGetLastError();  // report only this launch's error
+    hipLaunchKernelGGL((lut8_residual_kernel<16, 2>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
     return (int)hipGetLastError();
   }
   return (int)hipErrorInvalidConfiguration;
@@ -670,9 +816,10 @@ __global__ void repack_signs_kernel(const uint8_t *canon, int N, int P, uint8_t 
 }
 
 // canonical alpha [N][G] fp16 -> ((g/2*NP + r/32)*4 + ((r%32)/16)*2 + g%2)*16 + r%16
-__global__ void repack_alpha_kernel(const uint16_t *canon, int N, int G, uint16_t *dev) {
+__global__ void repack_alpha_kernel(const uint16_t *canon, int N, int G, uint16_t *dev, uint32_t *hdr) {
   const int NP = (N + 31) >> 5;
   const int64_t total = (int64_t)((G + 1) >> 1) * NP * 64;
+  uint32_t mx = 0u;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int i = (int)(e & 15);
@@ -682,8 +829,11 @@ __global__ void repack_alpha_kernel(const uint16_t *canon, int N, int G, uint16_
     const int rp = (int)(chunk % NP);
     const int g2 = (int)(chunk / NP);
     const int g = g2 * 2 + gl, r = rp * 32 + hf * 16 + i;
-    dev[e] = (r < N && g < G) ? canon[(size_t)r * G + g] : (uint16_t)0;
+    const uint16_t v = (r < N && g < G) ? canon[(size_t)r * G + g] : (uint16_t)0;
+    dev[e] = v;
+    mx = max(mx, (uint32_t)(v & 0x7fffu));
   }
+  atomicMax(hdr, mx);    // largest fp16 magnitude, compared as bits
 }
 
 // --------------------------------------------------------------------------
@@ -783,11 +933,13 @@ int launch_repack_signs(const uint8_t *canon, int N, int P, uint8_t *dev, void *
   return (int)hipGetLastError();
 }
 
-int launch_repack_alpha(const uint16_t *canon, int N, int G, uint16_t *dev, void *stream) {
+int launch_repack_alpha(const uint16_t *canon, int N, int G, uint16_t *dev, uint32_t *hdr, void *stream) {
   const int64_t total = (int64_t)((G + 1) >> 1) * ((N + 31) >> 5) * 64;
+  const int err = launch_fill_u32(hdr, 64, 0u, stream);
+  if (err) return err;
   (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(repack_alpha_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), canon, N, G, dev);
+                     reinterpret_cast<hipStream_t>(stream), canon, N, G, dev, hdr);
   return (int)hipGetLastError();
 }
 

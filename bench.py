@@ -21,7 +21,7 @@ Prints one JSON line:
                    rocprofv3 counter summary, when it was taken on the
                    current kernel source (else null)
   cpu_baseline     the float64 CPU oracle on the same layer, timed on the
-                   host (one thread), repeated until >= 10 s
+                   host (one thread), repeated until >= --cpu-seconds
 """
 from __future__ import annotations
 
@@ -47,6 +47,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
                   2: "llama7b-attn-qkvo-4096x4096-2bit-b1",
+                  3: "llama7b-decoder-7-linears-3bit-b1",
+                  4: "llama13b-shaped-batched-decode-2bit-d8-b16",
                   5: "gemma2-9b-mlp-rotated-vq-residual-3.125bit-b1"}
 
 
@@ -253,7 +255,7 @@ def main():
         with threadpool_limits(limits=1):
             one_layer()                                   # warm
             t_all = time.perf_counter()
-            while len(reps) < 3 or time.perf_counter() - t_all < args.cpu_seconds:
+            while not reps or time.perf_counter() - t_all < args.cpu_seconds:
                 t = time.perf_counter()
                 one_layer()
                 reps.append(time.perf_counter() - t)
@@ -264,7 +266,7 @@ def main():
                "sample": f"the whole layer ({wl.count} matrices, {layer_bytes} weight bytes), "
                          f"float64 numpy oracle (unpack, output codebook, lookup sum"
                          f"{', rotation, residual' if residual else ''}) on one thread (BLAS "
-                         f"limited to 1), {len(reps)} timed runs after 1 warm run, median; "
+                         f"limited to 1), {len(reps)} timed run(s) after 1 warm run, median; "
                          f"host has {cores} cores",
                "us_per_layer": round(med * 1e6, 1)}
         print(f"# cpu oracle: {med * 1e3:.1f} ms/layer over {len(reps)} runs", file=sys.stderr,

@@ -85,7 +85,6 @@ def test_gemv_validation_errors():
     assert _gemv([_m(N=0)], ok_x, 1, ok_y, None, 0) == vq.VQ_EINVAL
     assert _gemv([_m(d=2, nbits=8)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED   # no kernel
     assert _gemv([_m(d=4, nbits=12)], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # one token
-    assert _gemv([_m(d=4, nbits=12, K=16640)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(d=8, nbits=16)], ok_x, 17, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # <= 16 tokens
     # one kernel per call: every matrix of a group has the same (d, nbits)
     assert _gemv([_m(), _m(d=4, nbits=12)], ok_x * 2, 1, ok_y * 2, None, 0) == vq.VQ_EUNSUPPORTED

@@ -110,7 +110,8 @@ def _up(mi):
     return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, device=DEV)
 
 
-@pytest.mark.parametrize("K,N", [(256, 1), (256, 40), (1024, 100), (4096, 333), (11008, 64)])
+@pytest.mark.parametrize("K,N", [(256, 1), (256, 40), (1024, 100), (4096, 333), (11008, 64),
+                                 (16384, 50), (6400, 17)])
 def test_gemv_12bit_shapes(K, N):
     _say(f"gemv 12-bit K={K} N={N}")
     mi = synth.small_matrix(K, N, 4, 12, seed=K + 3 * N)

@@ -146,7 +146,7 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
   }
   switch (format_of(a)) {
     case FMT_LUT8: if (B != 1) return VQ_EUNSUPPORTED; break;
-    case FMT_WC12: if (residual || B != 1 || a.K / 4 > 4096) return VQ_EUNSUPPORTED; break;
+    case FMT_WC12: if (residual || B != 1) return VQ_EUNSUPPORTED; break;
     case FMT_WC16: if (residual || B > 16) return VQ_EUNSUPPORTED; break;
     default: return VQ_EUNSUPPORTED;
   }
@@ -177,14 +177,25 @@ static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const 
 static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                    float *const *y, void *stream) {
   const Format f = format_of(m[0]);
-  const int R = (f == FMT_WC12) ? wc12_rows_per_wg() : wc16_rows_per_wg();
   WcArgs args;
   memset(&args, 0, sizeof(args));
   args.count = count;
   int64_t max_wg = 0;
   int max_j = 0;
-  for (int i = 0; i < count; ++i) {
-    WcMat &d = args.mat[i];
+  // Workgroups are dispatched in grid order, matrix by matrix; the matrices
+  // with the longest rows (most work per wave) go first so they do not start
+  // last and set the tail.  Results do not depend on the order.
+  int order[VQ_MAX_GROUP];
+  for (int i = 0; i < count; ++i) order[i] = i;
+  for (int a = 1; a < count; ++a)
+    for (int b = a; b > 0 && m[order[b]].K / m[order[b]].d > m[order[b - 1]].K / m[order[b - 1]].d; --b) {
+      const int t = order[b];
+      order[b] = order[b - 1];
+      order[b - 1] = t;
+    }
+  for (int s = 0; s < count; ++s) {
+    const int i = order[s];
+    WcMat &d = args.mat[s];
     d.wi = static_cast<const uint8_t *>(m[i].wi);
     d.wc = m[i].wc;
     d.x = x[i];
@@ -193,6 +204,8 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     d.N = m[i].N;
     d.B = B;
     d.ldy = m[i].N;
+    d.jsplit = (f == FMT_WC12) ? wc12_jsplit(d.J) : 1;
+    const int R = (f == FMT_WC12) ? wc12_rows_per_wg(d.jsplit) : wc16_rows_per_wg();
     d.nwg = (m[i].N + R - 1) / R;
     if (d.nwg > max_wg) max_wg = d.nwg;
     if (d.J > max_j) max_j = d.J;

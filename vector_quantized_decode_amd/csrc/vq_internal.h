@@ -52,6 +52,7 @@ struct WcMat {
   int32_t B;              // tokens
   int32_t ldy;            // y row stride (N)
   int32_t nwg;            // workgroups of this matrix
+  int32_t jsplit;         // waves sharing a row group along J (1, 2, 4)
 };
 
 struct WcArgs {
@@ -59,7 +60,8 @@ struct WcArgs {
   int32_t count;
 };
 
-int wc12_rows_per_wg();
+int wc12_rows_per_wg(int jsplit);
+int wc12_jsplit(int J);
 int wc16_rows_per_wg();
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
 int launch_wc16(const WcArgs &a, int grid_x, void *stream);

@@ -215,17 +215,30 @@ __device__ __forceinline__ FixedScale fixed_scale(float bound) {
   return f;
 }
 
-__device__ __forceinline__ void packed_add_finish(uint64_t *acc, float *y, float p, const FixedScale &f,
-                                                  int nsplit) {
+__device__ __forceinline__ uint64_t packed_term(float p, const FixedScale &f) {
   const int64_t v = llrint((double)p * f.inv_q);
-  const uint64_t term = (1ull << 57) + (uint64_t)(v + (1ll << 49));
-  const uint64_t old = __hip_atomic_fetch_add(acc, term, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (1ull << 57) + (uint64_t)(v + (1ll << 49));
+}
+__device__ __forceinline__ uint64_t packed_add(uint64_t *acc, uint64_t term) {
+  return __hip_atomic_fetch_add(acc, term, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// After the add: the workgroup whose add completed the count writes y and
+// clears the word.  The clear is a plain store: no other workgroup touches
+// the word again in this launch, and the kernel's end writes it back (L2
+// write-back is byte-masked) before the next launch's atomics reach it.
+__device__ __forceinline__ void packed_finish(uint64_t *acc, float *y, uint64_t old, uint64_t term,
+                                              const FixedScale &f, int nsplit) {
   if ((int)(old >> 57) == nsplit - 1) {
     const uint64_t tot = old + term;
     const int64_t sv = (int64_t)(tot & ((1ull << 57) - 1)) - (int64_t)nsplit * (1ll << 49);
     *y = (float)((double)sv * f.q);
-    __hip_atomic_store(acc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *acc = 0ull;
   }
+}
+__device__ __forceinline__ void packed_add_finish(uint64_t *acc, float *y, float p, const FixedScale &f,
+                                                  int nsplit) {
+  const uint64_t term = packed_term(p, f);
+  packed_finish(acc, y, packed_add(acc, term), term, f, nsplit);
 }
 
 // Sum and max of the magnitudes of 8 fp16 values.
@@ -390,9 +403,21 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
-  // 4. conflict-free lookups and the cross-lane adder tree
+  // 4. the hand-off's scale (uniform): fixed point unless an input is not finite
+  float S = 0.f, Mw = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) { S += bnd[w]; Mw = fmaxf(Mw, bnd[W + w]); }
+  const float bound = S * Mw * 1.0009765625f;     // margin for fp32 rounding
+  const bool packed = M.nsplit > 1 && bound <= 3.0e38f && M.nsplit <= 127;
+  const FixedScale fs = fixed_scale(bound);
+  const int rsel = (lane >> 2) & 15;
+
+  // 5. conflict-free lookups and the cross-lane adder tree; with the
+  //    fixed-point hand-off a step's atomics are issued before the next
+  //    step's lookups so their round trips overlap
   const uint32_t base0 = (uint32_t)lane << 2;
   float rowval[STEPS];
+  uint64_t term[STEPS], old[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     float acc[16];
@@ -411,10 +436,16 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
       }
     }
     rowval[g] = reduce_rows16(acc, lane);
+    const int row = ((rb * STEPS + g) * W + wave) * 16 + rsel;
+    old[g] = 0ull;
+    term[g] = 0ull;
+    if (packed && (lane & 3) == 0 && row < M.N) {
+      term[g] = packed_term(rowval[g], fs);
+      old[g] = packed_add(M.acc + row, term[g]);
+    }
   }
 
-  // 5. rows out (lane 4r holds row r of its 16-row group)
-  const int rsel = (lane >> 2) & 15;
+  // 6. rows out (lane 4r holds row r of its 16-row group)
   if (M.nsplit == 1) {
 #pragma unroll
     for (int g = 0; g < STEPS; ++g) {
@@ -423,16 +454,11 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
     }
     return;
   }
-  float S = 0.f, Mw = 0.f;
-#pragma unroll
-  for (int w = 0; w < W; ++w) { S += bnd[w]; Mw = fmaxf(Mw, bnd[W + w]); }
-  const float bound = S * Mw * 1.0009765625f;     // margin for fp32 rounding
-  if (bound <= 3.0e38f && M.nsplit <= 127) {      // finite: fixed-point hand-off
-    const FixedScale fs = fixed_scale(bound);
+  if (packed) {
 #pragma unroll
     for (int g = 0; g < STEPS; ++g) {
       const int row = ((rb * STEPS + g) * W + wave) * 16 + rsel;
-      if ((lane & 3) == 0 && row < M.N) packed_add_finish(M.acc + row, M.y + row, rowval[g], fs, M.nsplit);
+      if ((lane & 3) == 0 && row < M.N) packed_finish(M.acc + row, M.y + row, old[g], term[g], fs, M.nsplit);
     }
     return;
   }

@@ -17,8 +17,8 @@
 // subvectors over workgroups adds a cross-workgroup hand-off.  Forming the
 // entry at lookup time costs the same arithmetic (a d-term dot product) and
 // needs only the codebook on chip:
-//   * wc12_kernel (d = 4, n = 12, one token): WC (4096 x 4 fp16, 32 KiB) and
-//     x sit in LDS; a lane owns one subvector j, reads WC[c] (8 bytes) for each
+//   * wc12_kernel (d = 4, n = 12, one token): WC (4096 x 4 fp16, 32 KiB) sits
+//     in LDS; a lane owns one subvector j, reads WC[c] (8 bytes) for each
 //     index and adds x_j . WC[c] with two packed fp16 dot products into fp32.
 //     Each workgroup covers whole rows: no partial sums leave it.
 //   * wc16_kernel (d = 8, n = 16, up to 16 tokens): the codebook (65536 x 8
@@ -133,60 +133,87 @@ __device__ __forceinline__ void load_chunk12(uint32_t (&w)[6], const uint8_t *p)
   w[3] = b[0]; w[4] = b[1]; w[5] = b[2];
 }
 
-// Workgroup: W waves, wave w owns the 16 rows of row group blockIdx.x * W + w
-// and walks all J/64 subvector chunks, PF chunks of indices in flight.
-// Dynamic LDS: WC (32 KiB) then x (J * 8 bytes).
+// Workgroup: W waves over W/S row groups of 16 rows; the S waves of a row
+// group split its J/64 subvector chunks into S contiguous segments (S = 1, 2
+// or 4, chosen by the host so no wave walks much more than the others), each
+// with PF chunks of indices (and the matching x slices) in flight.  The S
+// partial row sums meet in LDS and are added in segment order.  LDS holds the
+// codebook (32 KiB), so several workgroups share a compute unit.
 template <int W, int PF>
 __global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
-  extern __shared__ __align__(16) char smem[];
+  constexpr int NT = W * 64;
+  constexpr int WCP = 2048 / NT;              // 16-byte codebook pieces per thread
+  __shared__ __align__(16) char wc[4096 * 8];
+  __shared__ float part[W * 64];
   const WcMat &M = args.mat[blockIdx.y];
   if ((int)blockIdx.x >= M.nwg) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = M.jsplit;
+  const int rgl = wave / S, sg = wave % S;
   const int JT = M.J >> 6;
   const int NG = (M.N + 15) >> 4;
-  const int rg = min((int)blockIdx.x * W + wave, NG - 1);
-  char *wc = smem;
-  char *xs = smem + 4096 * 8;
+  const int rgw = (int)blockIdx.x * (W / S) + rgl;
+  const int rg = min(rgw, NG - 1);
+  const int seg = (JT + S - 1) / S;
+  const int kbeg = min(sg * seg, JT), kend = min(kbeg + seg, JT);
 
-  // 1. codebook and x into LDS (16-byte pieces), issued before the index stream
+  // 1. codebook pieces for LDS, then the first PF index chunks and x slices:
+  //    every load is issued before the first wait
+  u32x4 wcp[WCP];
   {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(M.wc);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(wc);
-    for (int t = threadIdx.x; t < 2048; t += W * 64) dst[t] = src[t];
-    const u32x4 *xsrc = reinterpret_cast<const u32x4 *>(M.x);
-    u32x4 *xdst = reinterpret_cast<u32x4 *>(xs);
-    for (int t = threadIdx.x; t < (M.J >> 1); t += W * 64) xdst[t] = xsrc[t];
-  }
-  // 2. first PF chunks of this wave's rows (24 bytes per lane each)
-  const uint8_t *wi = M.wi + ((size_t)rg * JT * 64 + lane) * 24;
-  uint32_t buf[PF][6];
 #pragma unroll
-  for (int p = 0; p < PF; ++p) load_chunk12(buf[p], wi + (size_t)min(p, JT - 1) * 64 * 24);
+    for (int u = 0; u < WCP; ++u) wcp[u] = src[threadIdx.x + u * NT];
+  }
+  const uint8_t *wi = M.wi + ((size_t)rg * JT * 64 + lane) * 24;
+  const uint2 *xg = reinterpret_cast<const uint2 *>(M.x) + lane;   // x_j, j = 64 k + lane
+  uint32_t buf[PF][6];
+  uint2 xbuf[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const int k = min(kbeg + p, JT - 1);
+    load_chunk12(buf[p], wi + (size_t)k * 64 * 24);
+    xbuf[p] = xg[k * 64];
+  }
+  {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(wc);
+#pragma unroll
+    for (int u = 0; u < WCP; ++u) dst[threadIdx.x + u * NT] = wcp[u];
+  }
   __syncthreads();
 
-  // 3. lookups: OC[j][c] = x_j . WC[c] formed per index, summed per row
+  // 2. lookups: OC[j][c] = x_j . WC[c] formed per index, summed per row
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  const uint2 *xl = reinterpret_cast<const uint2 *>(xs) + lane;
-  for (int k0 = 0; k0 < JT; k0 += PF) {
+  for (int k0 = kbeg; k0 < kend; k0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int k = k0 + p;
       uint32_t cur[6];
 #pragma unroll
       for (int q = 0; q < 6; ++q) cur[q] = buf[p][q];
-      // refill this slot with chunk k + PF (clamped: in-bounds, unused)
-      load_chunk12(buf[p], wi + (size_t)min(k + PF, JT - 1) * 64 * 24);
-      if (k < JT) wc12_chunk(acc, cur, xl[k * 64], wc);
+      const uint2 xj = xbuf[p];
+      // refill this slot with chunk k + PF (clamped: in bounds, unused)
+      const int kn = min(k + PF, JT - 1);
+      load_chunk12(buf[p], wi + (size_t)kn * 64 * 24);
+      xbuf[p] = xg[kn * 64];
+      if (k < kend) wc12_chunk(acc, cur, xj, wc);
     }
   }
 
-  // 4. rows out: lane 4r holds row r of the 16
-  const float v = wreduce_rows16(acc, lane);
-  const int row = ((int)blockIdx.x * W + wave) * 16 + ((lane >> 2) & 15);
-  if ((lane & 3) == 0 && (int)blockIdx.x * W + wave < NG && row < M.N) M.y[row] = v;
+  // 3. rows out: lane 4r holds row r of the 16 (segments added in order)
+  float v = wreduce_rows16(acc, lane);
+  if (S > 1) {
+    part[wave * 64 + lane] = v;
+    __syncthreads();
+    if (sg != 0) return;
+    v = part[wave * 64 + lane];
+    for (int t = 1; t < S; ++t) v += part[(wave + t) * 64 + lane];
+  }
+  const int row = rgw * 16 + ((lane >> 2) & 15);
+  if ((lane & 3) == 0 && rgw < NG && row < M.N) M.y[row] = v;
 }
 
 // --------------------------------------------------------------------------
@@ -318,16 +345,20 @@ static int wgrid(int64_t work, int block) {
 }
 
 constexpr int WC12_W = 4;
-constexpr int WC12_PF = 4;
+constexpr int WC12_PF = 8;
 constexpr int WC16_W = 4;
 
-int wc12_rows_per_wg() { return WC12_W * 16; }
+int wc12_rows_per_wg(int jsplit) { return WC12_W / jsplit * 16; }
+int wc12_jsplit(int J) {
+  const int JT = J / 64;
+  return JT <= 24 ? 1 : (JT <= 48 ? 2 : 4);
+}
 int wc16_rows_per_wg() { return WC16_W * 16; }
 
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
-  const size_t lds = 4096 * 8 + (size_t)max_j * 8;
+  (void)max_j;
   (void)hipGetLastError();  // report only this launch's error
-  hipLaunchKernelGGL((wc12_kernel<WC12_W, WC12_PF>), dim3(grid_x, a.count), dim3(WC12_W * 64), lds,
+  hipLaunchKernelGGL((wc12_kernel<WC12_W, WC12_PF>), dim3(grid_x, a.count), dim3(WC12_W * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }

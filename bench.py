@@ -42,7 +42,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, decimal GB/s
 METRIC = "µs/layer and effective HBM GB/s (% of peak) for VQ-GEMV at LLaMA-7B, B=1"
-KERNEL_SRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc", "vq_kernels.hip")
+CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
+# source of each workload's lookup kernel (8-bit indices: output-codebook tile
+# kernels; 12- and 16-bit indices: virtual-codebook kernels)
+KERNEL_SRC = {1: "vq_kernels.hip", 2: "vq_kernels.hip", 3: "vq_kernels_wc.hip",
+              4: "vq_kernels_wc.hip", 5: "vq_kernels.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
@@ -69,15 +73,15 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_sha(workload: int) -> str:
+    with open(os.path.join(CSRC, KERNEL_SRC[workload]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def committed_traffic(workload: int):
     """HBM bytes per launch of the lookup kernel from the committed counter
     summary of this workload, if it was taken on the current kernel source."""
-    sha = kernel_source_sha()
+    sha = kernel_source_sha(workload)
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         text = open(path).read()
         m = re.search(r"traffic-record: workload=(\d+) kernel_sha=(\w+) "
@@ -296,7 +300,7 @@ def main():
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(launch_us, 4),
                      "algorithmic_bytes_per_launch": layer_bytes,
-                     "traffic_source": traffic_src, "kernel_source_sha": kernel_source_sha()},
+                     "traffic_source": traffic_src, "kernel_source_sha": kernel_source_sha(args.workload)},
         "cpu_baseline": cpu,
         "parity": parity,
     }

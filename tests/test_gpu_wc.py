@@ -120,7 +120,8 @@ def test_gemv_12bit_shapes(K, N):
     _assert_close(y, ref, f"12-bit K={K} N={N}")
 
 
-@pytest.mark.parametrize("K,N,B", [(256, 20, 1), (256, 16, 16), (512, 100, 3), (2048, 33, 16),
+@pytest.mark.parametrize("K,N,B", [(256, 20, 1), (256, 16, 16), (512, 100, 3), (2048, 33, 16), (3072, 40, 16),
+                                   (5120, 24, 2),
                                    (1024, 7, 5)])
 def test_gemv_16bit_shapes(K, N, B):
     _say(f"gemv 16-bit K={K} N={N} B={B}")

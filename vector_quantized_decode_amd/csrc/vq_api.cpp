@@ -204,8 +204,8 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     d.N = m[i].N;
     d.B = B;
     d.ldy = m[i].N;
-    d.jsplit = (f == FMT_WC12) ? wc12_jsplit(d.J) : 1;
-    const int R = (f == FMT_WC12) ? wc12_rows_per_wg(d.jsplit) : wc16_rows_per_wg();
+    d.jsplit = (f == FMT_WC12) ? wc12_jsplit(d.J) : wc16_jsplit(d.J);
+    const int R = (f == FMT_WC12) ? wc12_rows_per_wg(d.jsplit) : wc16_rows_per_wg(d.jsplit);
     d.nwg = (m[i].N + R - 1) / R;
     if (d.nwg > max_wg) max_wg = d.nwg;
     if (d.J > max_j) max_j = d.J;

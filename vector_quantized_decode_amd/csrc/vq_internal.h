@@ -62,7 +62,8 @@ struct WcArgs {
 
 int wc12_rows_per_wg(int jsplit);
 int wc12_jsplit(int J);
-int wc16_rows_per_wg();
+int wc16_rows_per_wg(int jsplit);
+int wc16_jsplit(int J);
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
 int launch_wc16(const WcArgs &a, int grid_x, void *stream);
 int launch_repack_wi12(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);

@@ -228,14 +228,19 @@ __global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
 // of row l%16.
 template <int W>
 __global__ void __launch_bounds__(W * 64) wc16_kernel(const WcArgs args) {
+  __shared__ f32x4_t part[W * 64];
   const WcMat &M = args.mat[blockIdx.y];
   if ((int)blockIdx.x >= M.nwg) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = M.jsplit;                    // waves sharing a row group along J
+  const int rgl = wave / S, sg = wave % S;
   const int JB = M.J >> 5;
   const int NG = (M.N + 15) >> 4;
-  const int rgw = (int)blockIdx.x * W + wave;
+  const int rgw = (int)blockIdx.x * (W / S) + rgl;
   const int rg = min(rgw, NG - 1);
+  const int seg = (JB + S - 1) / S;
+  const int jb0 = min(sg * seg, JB), jb1 = min(jb0 + seg, JB);
   const int tok = lane & 15, sub = lane >> 4;
   const bool has_tok = tok < M.B;
   const int K = M.J * 8;
@@ -244,9 +249,10 @@ __global__ void __launch_bounds__(W * 64) wc16_kernel(const WcArgs args) {
   const uint8_t *wi = M.wi + ((size_t)rg * JB * 64 + lane) * 16;
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  u32x4 idx = *reinterpret_cast<const u32x4 *>(wi);
-  for (int jb = 0; jb < JB; ++jb) {
-    // gathers of this block, then the next block's indices
+  u32x4 idx = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb0, JB - 1) * 64 * 16);
+  u32x4 idx_next = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb0 + 1, JB - 1) * 64 * 16);
+  for (int jb = jb0; jb < jb1; ++jb) {
+    // gathers of this block, the block after next's indices, then the MFMAs
     half8_t b[8], a[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -260,9 +266,19 @@ __global__ void __launch_bounds__(W * 64) wc16_kernel(const WcArgs args) {
                                : u32x4{0u, 0u, 0u, 0u};
       a[q] = __builtin_bit_cast(half8_t, xv);
     }
-    idx = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb + 1, JB - 1) * 64 * 16);
+    idx = idx_next;
+    idx_next = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb + 2, JB - 1) * 64 * 16);
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[q], acc, 0, 0, 0);
+  }
+  if (S > 1) {                               // segments added in order through LDS
+    part[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (sg != 0) return;
+    for (int t = 1; t < S; ++t) {
+      const f32x4_t o = part[(wave + t) * 64 + lane];
+      acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
+    }
   }
   if (rgw < NG) {
     const int row = rgw * 16 + tok;
@@ -346,14 +362,18 @@ static int wgrid(int64_t work, int block) {
 
 constexpr int WC12_W = 4;
 constexpr int WC12_PF = 8;
-constexpr int WC16_W = 4;
+constexpr int WC16_W = 8;
 
 int wc12_rows_per_wg(int jsplit) { return WC12_W / jsplit * 16; }
 int wc12_jsplit(int J) {
   const int JT = J / 64;
   return JT <= 24 ? 1 : (JT <= 48 ? 2 : 4);
 }
-int wc16_rows_per_wg() { return WC16_W * 16; }
+int wc16_rows_per_wg(int jsplit) { return WC16_W / jsplit * 16; }
+int wc16_jsplit(int J) {
+  const int JB = J / 32;
+  return JB <= 8 ? 1 : (JB <= 16 ? 2 : 4);
+}
 
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   (void)max_j;

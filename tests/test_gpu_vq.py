@@ -79,19 +79,26 @@ def _host_wi_layout(canon, N, J):
 
 
 def _host_sign_layout(canon, N, P):
+    """chunk (tile pt, row pair rp), lane 2r + g: 16 sign bytes of row
+    32 rp + r, byte j at position 32 pt + 16 g + (j ^ (r % 16))."""
     NP = (N + 31) // 32
-    out = np.zeros((P // 32, NP, 2, 32, 16), dtype=np.uint8)
+    out = np.zeros((P // 32, NP, 32, 2, 16), dtype=np.uint8)
     for r in range(N):
-        out[:, r // 32, (r % 32) // 16, :, r % 16] = canon[r].reshape(P // 32, 32)
+        rr = r % 32
+        for g in range(2):
+            for j in range(16):
+                out[:, r // 32, rr, g, j] = canon[r].reshape(P // 32, 32)[:, 16 * g + (j ^ (rr % 16))]
     return out.reshape(-1)
 
 
 def _host_alpha_layout(canon, N, G):
+    """chunk (group pair, row pair rp), lane 2r + g: the scale of row
+    32 rp + r, group 2 (group pair) + g."""
     NP = (N + 31) // 32
-    out = np.zeros((G // 2, NP, 2, 2, 16), dtype=np.uint16)
+    out = np.zeros((G // 2, NP, 32, 2), dtype=np.uint16)
     for r in range(N):
         for g in range(G):
-            out[g // 2, r // 32, (r % 32) // 16, g % 2, r % 16] = canon[r, g]
+            out[g // 2, r // 32, r % 32, g % 2] = canon[r, g]
     return out.reshape(-1)
 
 
@@ -269,11 +276,14 @@ def test_workspace_reused_across_calls():
                                           (3584, 300, True, 0), (2048, 1031, True, 0), (768, 50, True, 0),
                                           (1024, 64, True, 64), (512, 33, True, 1), (1024, 96, True, 2),
                                           (4096, 80, True, 4096), (8192, 100, True, 8192),
-                                          (1024, 3000, True, 0), (2048, 4500, True, 0)])
+                                          (1024, 3000, True, 0), (2048, 4500, True, 0),
+                                          (20480, 64, True, 0), (33024, 64, True, 0)])
 def test_gemv_residual_shapes(K, N, rotate, h):
     # h = 0: the largest power of two dividing K.  Blocks up to 2048 are
     # rotated inside the lookup kernel (h < 256: whole blocks per tile);
-    # 4096 and 8192 go through the separate rotation kernel.
+    # 4096 and 8192 go through the separate rotation kernel.  K = 20480 takes
+    # the wider bound loads; above 127 splits (K = 33024) partial sums are
+    # handed off in float.
     _say(f"gemv_residual K={K} N={N} rotate={rotate} h={h}")
     mi = synth.small_matrix(K, N, 4, 8, seed=K * 7 + N, residual=True, had_block=h or None)
     m = _upload(mi, residual=True)

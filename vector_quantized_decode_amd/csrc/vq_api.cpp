@@ -35,7 +35,7 @@ Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count) {
     if (m[i].N > max_n) max_n = m[i].N;
     work += (int64_t)m[i].N * J;
   }
-  Lut8Shape s;
+  Lut8Shape s{};
   s.nsub = all128 ? 2 : 1;
   if (work <= (int64_t)1 << 20) {   // small layers: more, smaller workgroups
     s.waves = 4;
@@ -52,13 +52,18 @@ Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count) {
   // two 32-row steps per wave (1024 rows per workgroup) once the matrices are
   // tall enough to fill them: the per-workgroup OC tile and sign table are
   // then shared by twice the lookups
-  int64_t max_n = 0;
-  for (int i = 0; i < count; ++i)
+  int64_t max_n = 0, max_k = 0;
+  for (int i = 0; i < count; ++i) {
     if (m[i].N > max_n) max_n = m[i].N;
-  Lut8Shape s;
+    if (m[i].K > max_k) max_k = m[i].K;
+  }
+  Lut8Shape s{};
   s.nsub = 1;
   s.waves = 16;
   s.steps = max_n > 2048 ? 2 : 1;
+  // x chunks per thread for the hand-off bound: 2 cover K <= 16384, 4 cover
+  // every K that the fixed-point hand-off takes (at most 127 splits)
+  s.nbx = max_k > 16384 ? 4 : 2;
   return s;
 }
 
@@ -260,8 +265,7 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
                                                        alpha_body_bytes(m[i].N, m[i].K));
       // blocks up to 2048 are rotated inside the lookup kernel; larger ones first
       // by the rotation kernel, into the workspace
-      if (h > 2048) d.xr = reinterpret_cast<const float *>(ws + q.xrot_off);
-      else d.xr = nullptr;
+      d.fused = h <= 2048 ? 1 : 0;
     }
     d.nwg = q.nsplit * q.nrb;
     if (d.nwg > max_wg) max_wg = d.nwg;
@@ -269,7 +273,7 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
   int err;
   if (residual) {
     for (int i = 0; i < count; ++i) {
-      if (!args.mat[i].xr) continue;          // rotated inside the lookup kernel
+      if (args.mat[i].fused) continue;        // rotated inside the lookup kernel
       const int h = args.mat[i].had;
       err = launch_rht(x[i], m[i].rht_sign, B, m[i].K, h, args.mat[i].had_scale,
                        reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);

@@ -26,6 +26,7 @@ struct Lut8Mat {
   const uint32_t *alpha_hdr;  // residual: largest |alpha| (fp16 magnitude bits)
   float had_scale;        // residual: 1/sqrt(had)
   int32_t had;            // residual: Hadamard block (1: no rotation)
+  int32_t fused;          // residual: rotate x inside the lookup kernel (else xr holds it)
   int32_t J;              // subvectors per row, K/4
   int32_t N;              // output rows
   int32_t rows_pad;       // rows of the padded layout (multiple of 32)
@@ -74,6 +75,7 @@ struct Lut8Shape {
   int nsub;     // 64-subvector tiles per workgroup (1 or 2)
   int waves;    // wavefronts per workgroup
   int steps;    // row steps per wave (16 rows each, 32 for the residual kernel)
+  int nbx;      // residual: 16-byte chunks of x per thread for the bound (2 or 4)
   int rows() const { return waves * steps * 16; }
   int rows_res() const { return waves * steps * 32; }
   int jt() const { return 64 * nsub; }

@@ -104,13 +104,11 @@ __device__ __forceinline__ float reduce_rows16(float (&a)[16], int lane) {
   return v;
 }
 
-// Rows 0..15 in A, rows 16..31 in Bv, and S holding sign-residual partials
-// of rows 0..15 in lanes 0..31 and rows 16..31 in lanes 32..63.  Returns the
-// full sum of row (lane >> 1) & 31 in every lane.
-__device__ __forceinline__ float reduce_rows32(float (&A)[16], float (&Bv)[16], const float (&S)[16],
-                                               int lane) {
+// Rows 0..15 in A, rows 16..31 in Bv.  Returns the full sum of row
+// (lane >> 1) & 31 in every lane.
+__device__ __forceinline__ float reduce_rows32(float (&A)[16], float (&Bv)[16], int lane) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { swap32(A[i], Bv[i]); A[i] = A[i] + Bv[i] + S[i]; }
+  for (int i = 0; i < 16; ++i) { swap32(A[i], Bv[i]); A[i] = A[i] + Bv[i]; }
   // A[i]: row i + 16*bit5
 #pragma unroll
   for (int i = 0; i < 8; ++i) { swap16(A[i], A[i + 8]); A[i] += A[i + 8]; }
@@ -493,12 +491,16 @@ __device__ __forceinline__ float sign_of_byte(uint32_t s4, int t) {
   return (float)(int8_t)((s4 >> (8 * t)) & 0xffu);
 }
 
-template <int W, int STEPS>
+template <int W, int STEPS, int NBX>
 __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args args) {
   static_assert(W == 16, "the OC tile takes waves 0-7, the sign table waves 8-15");
   constexpr int NT = W * 64;
-  __shared__ float lds[2 * 16384 + 2 * W + 16];
-  float *bnd = lds + 2 * 16384;
+  // LDS: sign table [256 byte values][64 columns] at 0, OC tile [256
+  // centroids][64 subvectors] at 64 KiB (so the sign lookups' addresses have
+  // a zero third byte), x_rot, bound parts, hand-off flag
+  __shared__ __align__(16) float lds[2 * 16384 + 256 + 2 * W + 16];
+  float *xrs = lds + 2 * 16384;              // x_rot of the tile, 4 per subvector
+  float *bnd = xrs + 256;
   uint32_t *flag = reinterpret_cast<uint32_t *>(bnd + 2 * W);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -508,44 +510,54 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   const int sp = local % M.nsplit, rb = local / M.nsplit;
   const int NG = (M.N + 15) >> 4;
   const int NP = (M.N + 31) >> 5;
-  const int half = lane >> 5, pl = lane & 31;
+  const int pl = lane & 31;
   const uint8_t *xb = reinterpret_cast<const uint8_t *>(M.x);
-  const uint8_t *wcb = reinterpret_cast<const uint8_t *>(M.wc);
   const bool oc_wave = wave < 8;
 
-  // 1. small loads first.  Rotation inputs: sub-block u of the tile's
-  //    Hadamard block, elements 4 lane .. 4 lane + 3 (clamped, in bounds).
+  // 1. small loads first; every load here is unconditional within its wave
+  //    (a branch around a load makes the compiler wait for the whole index
+  //    stream at the join).  The vector memory pipe of a CU is shared by its
+  //    16 waves, so work that every wave would repeat is done once: wave 0
+  //    alone loads the rotation inputs, sub-block u of the tile's Hadamard
+  //    block at elements 4 lane .. 4 lane + 3 (clamped, in bounds) with their
+  //    signs (x itself stands in when there are none), or the rotated tile
+  //    the rotation kernel left in the workspace.
   const int h = M.had;                       // 1: no rotation
   const int k0 = sp * 256;
   const int QS = h > 256 ? (h >> 8) : 1;
   const int kb = h > 256 ? (k0 / h) * h : k0;
   const int qt = h > 256 ? ((k0 - kb) >> 8) : 0;
-  const bool fused = (M.xr == nullptr);
+  const bool fused = M.fused != 0;
   uint2 xq[8];
   uint32_t sq[8];
+  float4 xrw;
+  if (wave == 0) {
+    const uint8_t *rsb = M.rs ? reinterpret_cast<const uint8_t *>(M.rs) : xb;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = kb + 256 * min(u, QS - 1) + 4 * lane;
-    xq[u] = *reinterpret_cast<const uint2 *>(xb + 2 * (size_t)e);
-    sq[u] = M.rs ? *reinterpret_cast<const uint32_t *>(M.rs + e) : 0x01010101u;
+    for (int u = 0; u < 8; ++u) {
+      const int e = kb + 256 * min(u, QS - 1) + 4 * lane;
+      xq[u] = *reinterpret_cast<const uint2 *>(xb + 2 * (size_t)e);
+      sq[u] = *reinterpret_cast<const uint32_t *>(rsb + e);
+    }
+    xrw = *reinterpret_cast<const float4 *>(M.xr + k0 + 4 * lane);
   }
-  float4 xrw = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (!fused) xrw = *reinterpret_cast<const float4 *>(M.xr + k0 + 4 * lane);
-  //    OC waves: centroids 32 wave + (lane % 32) as the MFMA A operand
-  const half4_t wa = __builtin_bit_cast(
-      half4_t, reinterpret_cast<const uint2 *>(M.wc)[(oc_wave ? wave : 0) * 32 + (lane & 31)]);
-  //    bound inputs: x in 16-byte chunks t and t + NT, WC chunk t, max |alpha|
+  //    OC waves: centroids 32 wave + (lane % 32) as the MFMA A operand.  The
+  //    eight OC waves hold the whole codebook, so max |WC| is taken from them.
+  const uint2 wraw = reinterpret_cast<const uint2 *>(M.wc)[(oc_wave ? wave : 0) * 32 + (lane & 31)];
+  const half4_t wa = __builtin_bit_cast(half4_t, wraw);
+  //    bound inputs: x in 16-byte chunks t0 + u NT, max |alpha|
   const int nxc = M.J >> 1;
-  const int t0 = threadIdx.x, t1 = threadIdx.x + NT;
-  const u32x4 xb0 = load16(xb + 16 * (size_t)min(t0, nxc - 1));
-  const u32x4 xb1 = load16(xb + 16 * (size_t)min(t1, nxc - 1));
-  const u32x4 wb = load16(wcb + 16 * min(t0, 127));
+  const int t0 = threadIdx.x;
+  u32x4 xbw[NBX];
+#pragma unroll
+  for (int u = 0; u < NBX; ++u) xbw[u] = load16(xb + 16 * (size_t)min(t0 + u * NT, nxc - 1));
   const uint32_t amax_bits = *M.alpha_hdr;
   __builtin_amdgcn_s_barrier();
 
   // 2. index, sign and alpha loads: per 32-row step, two index chunks, one
-  //    sign chunk, 16 alphas
-  u32x4 va[STEPS], vb[STEPS], vs[STEPS], al0[STEPS], al1[STEPS];
+  //    sign chunk and the scale of the lane's (row, group)
+  u32x4 va[STEPS], vb[STEPS], vs[STEPS];
+  uint16_t al[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     const int rp = min((rb * STEPS + g) * W + wave, NP - 1);
@@ -556,54 +568,58 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
         reinterpret_cast<const u32x4 *>(M.wi + (((size_t)sp * NG + rgb) * 64 + lane) * 16));
     vs[g] = __builtin_nontemporal_load(
         reinterpret_cast<const u32x4 *>(M.signs + (((size_t)sp * NP + rp) * 64 + lane) * 16));
-    const uint16_t *ap = M.alpha + (((size_t)sp * NP + rp) * 4 + half * 2 + (pl >> 4)) * 16;
-    al0[g] = *reinterpret_cast<const u32x4 *>(ap);
-    al1[g] = *reinterpret_cast<const u32x4 *>(ap + 8);
+    al[g] = M.alpha[((size_t)sp * NP + rp) * 64 + lane];
   }
 
-  // 3. x_rot of subvector `lane` of this tile
-  float xr[4];
-  if (fused) {
-    float c[4] = {0.f, 0.f, 0.f, 0.f};
+  // 3. x_rot of subvector `lane` of this tile, formed by wave 0 into LDS
+  if (wave == 0) {
+    float c[4] = {xrw.x, xrw.y, xrw.z, xrw.w};
+    if (fused) {
+      c[0] = c[1] = c[2] = c[3] = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < QS) {
-        const float sg = (__builtin_popcount(qt & u) & 1) ? -1.f : 1.f;
-        const half2_t a = as_h2(xq[u].x), b = as_h2(xq[u].y);
-        c[0] += sg * sign_of_byte(sq[u], 0) * (float)a.x;
-        c[1] += sg * sign_of_byte(sq[u], 1) * (float)a.y;
-        c[2] += sg * sign_of_byte(sq[u], 2) * (float)b.x;
-        c[3] += sg * sign_of_byte(sq[u], 3) * (float)b.y;
+      for (int u = 0; u < 8; ++u) {
+        if (u < QS) {
+          if (!M.rs) sq[u] = 0x01010101u;
+          const float sg = (__builtin_popcount(qt & u) & 1) ? -1.f : 1.f;
+          const half2_t a = as_h2(xq[u].x), b = as_h2(xq[u].y);
+          c[0] += sg * sign_of_byte(sq[u], 0) * (float)a.x;
+          c[1] += sg * sign_of_byte(sq[u], 1) * (float)a.y;
+          c[2] += sg * sign_of_byte(sq[u], 2) * (float)b.x;
+          c[3] += sg * sign_of_byte(sq[u], 3) * (float)b.y;
+        }
       }
-    }
-    const int hl = h < 256 ? h : 256;
-    if (hl >= 2) {
-      const float a0 = c[0] + c[1], a1 = c[0] - c[1], a2 = c[2] + c[3], a3 = c[2] - c[3];
-      c[0] = a0; c[1] = a1; c[2] = a2; c[3] = a3;
-    }
-    if (hl >= 4) {
-      const float a0 = c[0] + c[2], a2 = c[0] - c[2], a1 = c[1] + c[3], a3 = c[1] - c[3];
-      c[0] = a0; c[1] = a1; c[2] = a2; c[3] = a3;
-    }
-    for (int m = 1; 4 * m < hl; m <<= 1) {
-      const bool upper = lane & m;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float p = __shfl_xor(c[t], m, 64);
-        c[t] = upper ? (p - c[t]) : (c[t] + p);
+      const int hl = h < 256 ? h : 256;
+      if (hl >= 2) {
+        const float a0 = c[0] + c[1], a1 = c[0] - c[1], a2 = c[2] + c[3], a3 = c[2] - c[3];
+        c[0] = a0; c[1] = a1; c[2] = a2; c[3] = a3;
       }
-    }
+      if (hl >= 4) {
+        const float a0 = c[0] + c[2], a2 = c[0] - c[2], a1 = c[1] + c[3], a3 = c[1] - c[3];
+        c[0] = a0; c[1] = a1; c[2] = a2; c[3] = a3;
+      }
+      for (int m = 1; 4 * m < hl; m <<= 1) {
+        const bool upper = lane & m;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) xr[t] = c[t] * M.had_scale;
-  } else {
-    xr[0] = xrw.x; xr[1] = xrw.y; xr[2] = xrw.z; xr[3] = xrw.w;
+        for (int t = 0; t < 4; ++t) {
+          const float p = __shfl_xor(c[t], m, 64);
+          c[t] = upper ? (p - c[t]) : (c[t] + p);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) c[t] *= M.had_scale;
+    }
+    *reinterpret_cast<float4 *>(xrs + 4 * lane) = make_float4(c[0], c[1], c[2], c[3]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
 
   if (oc_wave) {
     // 4. OC tile, centroids 32 wave .. +31, on the matrix cores.  x_rot is
     //    split into fp16 high and low parts (x = hi + lo to ~2^-22), so two
     //    fp16 MFMAs give the fp32 product; the output registers are placed as
     //    in the plain kernel (one centroid per register after the swap).
+    const float4 xv = *reinterpret_cast<const float4 *>(xrs + 4 * lane);
+    const float xr[4] = {xv.x, xv.y, xv.z, xv.w};
     half4_t xh, xl;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -614,7 +630,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     f32x32_t o = {};
     o = __builtin_amdgcn_mfma_f32_32x32x4f16(wa, xh, o, 0, 0, 0);
     o = __builtin_amdgcn_mfma_f32_32x32x4f16(wa, xl, o, 0, 0, 0);
-    float *dst = lds + (wave * 32) * 64 + lane;
+    float *dst = lds + 16384 + (wave * 32) * 64 + lane;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float a = o[i], b = o[i + 16];
@@ -624,15 +640,13 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
       dst[(m + 4) * 64] = b;
     }
   } else {
-    // 5. sign table for sign byte p = 32*sp + (lane & 31): the 8 rotated
-    //    inputs 8p .. 8p+7 live in lanes 2p (first four) and 2p+1; this wave
-    //    writes high nibbles 2 (wave - 8) and 2 (wave - 8) + 1
-    float lo4[4], hi4[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      lo4[t] = __shfl(xr[t], 2 * pl, 64);
-      hi4[t] = __shfl(xr[t], 2 * pl + 1, 64);
-    }
+    // 5. sign table for sign byte p = 32*sp + (lane & 31): its 8 rotated
+    //    inputs are x_rot 8p' .. 8p'+7 of the tile (p' = lane & 31); this
+    //    wave writes high nibbles 2 (wave - 8) and 2 (wave - 8) + 1
+    const float4 l4 = *reinterpret_cast<const float4 *>(xrs + 8 * pl);
+    const float4 h4 = *reinterpret_cast<const float4 *>(xrs + 8 * pl + 4);
+    const float lo4[4] = {l4.x, l4.y, l4.z, l4.w};
+    const float hi4[4] = {h4.x, h4.y, h4.z, h4.w};
     const float S = ((lo4[0] + lo4[1]) + (lo4[2] + lo4[3])) + ((hi4[0] + hi4[1]) + (hi4[2] + hi4[3]));
     float L[16];
     L[0] = 0.f;
@@ -644,7 +658,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
       const float H = ((hi & 1) ? hi4[0] : 0.f) + ((hi & 2) ? hi4[1] : 0.f) +
                       ((hi & 4) ? hi4[2] : 0.f) + ((hi & 8) ? hi4[3] : 0.f);
       const float c0 = 2.f * H - S;
-      float *dst = lds + 16384 + (hi * 16) * 64 + lane;
+      float *dst = lds + (hi * 16) * 64 + lane;
 #pragma unroll
       for (int lo = 0; lo < 16; ++lo) dst[lo * 64] = __builtin_fmaf(2.f, L[lo], c0);
     }
@@ -652,47 +666,66 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   // 6. per-wave parts of the bound sum_k |x_rot_k| <= sqrt(K) ||x||_2
   {
     float s2 = 0.f;
-    if (t0 < nxc) s2 += sq_sum8(xb0);
-    if (t1 < nxc) s2 += sq_sum8(xb1);
-    for (int t = t0 + 2 * NT; t < nxc; t += NT) s2 += sq_sum8(load16(xb + 16 * (size_t)t));
-    const float mw = (t0 < 128) ? abs_max8(wb) : 0.f;
+#pragma unroll
+    for (int u = 0; u < NBX; ++u)
+      if (t0 + u * NT < nxc) s2 += sq_sum8(xbw[u]);
+    if (nxc > NBX * NT) s2 = __builtin_inff();   // longer inputs take the float hand-off
+    uint32_t m = max(max(wraw.x & 0x7fffu, (wraw.x >> 16) & 0x7fffu),
+                     max(wraw.y & 0x7fffu, (wraw.y >> 16) & 0x7fffu));
+    const float mw = !oc_wave ? 0.f
+                     : m >= 0x7c00u ? __builtin_inff()
+                                    : (float)__builtin_bit_cast(_Float16, (uint16_t)m);
     const float ws = wave_sum(s2), wm = wave_max(mw);
     if (lane == 0) { bnd[wave] = ws; bnd[W + wave] = wm; }
   }
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
-  // 7. lookups
-  const uint32_t base0 = (uint32_t)lane << 2;
-  const uint32_t base1 = base0 | 0x10000u;
+  // 7. lookups.  Index chunks: lane = subvector, bytes = 16 rows.  Sign
+  //    chunk: lane L = 2r + g holds the 16 sign bytes of row r and group g of
+  //    the tile, byte j at position 16 g + (j ^ (r & 15)); its column in the
+  //    table, 32 (r >> 4) + 16 g + (j ^ (r & 15)), differs across the 64
+  //    lanes for every j.  byte0 of the address comes from bsel[j >> 2] byte
+  //    (j & 3), byte1 is the sign byte.
+  const uint32_t baseoc = ((uint32_t)lane << 2) | 0x10000u;
+  const int rr = lane >> 1, gg = lane & 1;
+  const uint32_t c0 = (uint32_t)(32 * (rr >> 4) + 16 * gg + (rr & 15));
+  uint32_t bsel[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t v = 0u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v |= (((c0 ^ (uint32_t)(4 * q + t)) << 2) & 0xffu) << (8 * t);
+    bsel[q] = v;
+  }
   float rowval[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     float A[16], Bv[16], S[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t wq = va[g][q], wbq = vb[g][q];
-      A[4 * q + 0] = lds_at(lds, lut_addr<0>(wq, base0));
-      A[4 * q + 1] = lds_at(lds, lut_addr<1>(wq, base0));
-      A[4 * q + 2] = lds_at(lds, lut_addr<2>(wq, base0));
-      A[4 * q + 3] = lds_at(lds, lut_addr<3>(wq, base0));
-      Bv[4 * q + 0] = lds_at(lds, lut_addr<0>(wbq, base0));
-      Bv[4 * q + 1] = lds_at(lds, lut_addr<1>(wbq, base0));
-      Bv[4 * q + 2] = lds_at(lds, lut_addr<2>(wbq, base0));
-      Bv[4 * q + 3] = lds_at(lds, lut_addr<3>(wbq, base0));
+      const uint32_t wq = va[g][q], wbq = vb[g][q], ws4 = vs[g][q];
+      A[4 * q + 0] = lds_at(lds, lut_addr<0>(wq, baseoc));
+      A[4 * q + 1] = lds_at(lds, lut_addr<1>(wq, baseoc));
+      A[4 * q + 2] = lds_at(lds, lut_addr<2>(wq, baseoc));
+      A[4 * q + 3] = lds_at(lds, lut_addr<3>(wq, baseoc));
+      Bv[4 * q + 0] = lds_at(lds, lut_addr<0>(wbq, baseoc));
+      Bv[4 * q + 1] = lds_at(lds, lut_addr<1>(wbq, baseoc));
+      Bv[4 * q + 2] = lds_at(lds, lut_addr<2>(wbq, baseoc));
+      Bv[4 * q + 3] = lds_at(lds, lut_addr<3>(wbq, baseoc));
+      S[4 * q + 0] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0400u));
+      S[4 * q + 1] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0501u));
+      S[4 * q + 2] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0602u));
+      S[4 * q + 3] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0703u));
     }
+    // residual of (row r, group g): alpha times the sum over its 16 sign
+    // bytes; the two groups of a row sit in lanes 2r and 2r + 1
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t ws4 = vs[g][q];
-      const uint32_t a01 = (q < 2) ? al0[g][2 * q] : al1[g][2 * q - 4];
-      const uint32_t a23 = (q < 2) ? al0[g][2 * q + 1] : al1[g][2 * q - 3];
-      const half2_t h01 = as_h2(a01), h23 = as_h2(a23);
-      S[4 * q + 0] = (float)h01.x * lds_at(lds, lut_addr<0>(ws4, base1));
-      S[4 * q + 1] = (float)h01.y * lds_at(lds, lut_addr<1>(ws4, base1));
-      S[4 * q + 2] = (float)h23.x * lds_at(lds, lut_addr<2>(ws4, base1));
-      S[4 * q + 3] = (float)h23.y * lds_at(lds, lut_addr<3>(ws4, base1));
-    }
-    rowval[g] = reduce_rows32(A, Bv, S, lane);
+    for (int i = 0; i < 8; ++i) S[i] += S[i + 8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[i] += S[i + 4];
+    const float sres = ((S[0] + S[2]) + (S[1] + S[3])) * (float)__builtin_bit_cast(_Float16, al[g]);
+    rowval[g] = reduce_rows32(A, Bv, lane) + (sres + dpp<DPP_QUAD_XOR1>(sres));
   }
 
   // 8. rows out: lane 2r holds row r of each 32-row group
@@ -754,18 +787,20 @@ int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *s
   return (int)hipErrorInvalidConfiguration;
 }
 
+template <int STEPS, int NBX>
+static int launch_residual_t(const Lut8Args &a, int grid_x, hipStream_t st) {
+  (void)hipGetLastError();  // report only this launch's error
+  hipLaunchKernelGGL((lut8_residual_kernel<16, STEPS, NBX>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
+  return (int)hipGetLastError();
+}
+
 int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (s.waves == 16 && s.steps == 1) {
-    (void)hipGetLastError();  // report only this launch's error
-    hipLaunchKernelGGL((lut8_residual_kernel<16, 1>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
-    return (int)hipGetLastError();
-  }
-  if (s.waves == 16 && s.steps == 2) {
-    (void)hipGetLastError();  // report only this launch's error
-    hipLaunchKernelGGL((lut8_residual_kernel<16, 2>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
-    return (int)hipGetLastError();
-  }
+  if (s.waves != 16) return (int)hipErrorInvalidConfiguration;
+  if (s.steps == 1 && s.nbx == 2) return launch_residual_t<1, 2>(a, grid_x, st);
+  if (s.steps == 1 && s.nbx == 4) return launch_residual_t<1, 4>(a, grid_x, st);
+  if (s.steps == 2 && s.nbx == 2) return launch_residual_t<2, 2>(a, grid_x, st);
+  if (s.steps == 2 && s.nbx == 4) return launch_residual_t<2, 4>(a, grid_x, st);
   return (int)hipErrorInvalidConfiguration;
 }
 
@@ -830,31 +865,30 @@ __global__ void repack_signs_kernel(const uint8_t *canon, int N, int P, uint8_t 
     const int64_t chunk = e >> 6;
     const int rp = (int)(chunk % NP);
     const int pt = (int)(chunk / NP);
-    const int hf = l >> 5, p = pt * 32 + (l & 31);
+    const int rr = l >> 1, gg = l & 1;
+    const int r = rp * 32 + rr;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
-    for (int i = 0; i < 16; ++i) {
-      const int r = rp * 32 + hf * 16 + i;
+    for (int j = 0; j < 16; ++j) {
+      const int p = pt * 32 + 16 * gg + (j ^ (rr & 15));
       const uint32_t b = (r < N) ? canon[(size_t)r * P + p] : 0u;
-      w[i >> 2] |= b << (8 * (i & 3));
+      w[j >> 2] |= b << (8 * (j & 3));
     }
     *reinterpret_cast<u32x4 *>(dev + e * 16) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
-// canonical alpha [N][G] fp16 -> ((g/2*NP + r/32)*4 + ((r%32)/16)*2 + g%2)*16 + r%16
+// canonical alpha [N][G] fp16 -> ((g/2*NP + r/32)*64 + 2*(r%32) + g%2)
 __global__ void repack_alpha_kernel(const uint16_t *canon, int N, int G, uint16_t *dev, uint32_t *hdr) {
   const int NP = (N + 31) >> 5;
   const int64_t total = (int64_t)((G + 1) >> 1) * NP * 64;
   uint32_t mx = 0u;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(e & 15);
-    const int gl = (int)((e >> 4) & 1);
-    const int hf = (int)((e >> 5) & 1);
+    const int l = (int)(e & 63);
     const int64_t chunk = e >> 6;
     const int rp = (int)(chunk % NP);
     const int g2 = (int)(chunk / NP);
-    const int g = g2 * 2 + gl, r = rp * 32 + hf * 16 + i;
+    const int g = g2 * 2 + (l & 1), r = rp * 32 + (l >> 1);
     const uint16_t v = (r < N && g < G) ? canon[(size_t)r * G + g] : (uint16_t)0;
     dev[e] = v;
     mx = max(mx, (uint32_t)(v & 0x7fffu));

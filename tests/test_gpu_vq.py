@@ -293,6 +293,18 @@ def test_gemv_residual_shapes(K, N, rotate, h):
     _assert_close(y, _oracle_res(mi, rotate=rotate), f"residual K={K} N={N}")
 
 
+@pytest.mark.parametrize("K,N", [(4096, 9000), (20480, 6144)])
+def test_gemv_residual_tall_sampled_rows(K, N):
+    # tall layers take 2 and 4 row steps per wave (1024 and 2048 rows per
+    # workgroup); K = 20480 also takes the wider bound loads
+    _say(f"gemv_residual K={K} N={N}, sampled rows")
+    mi = synth.small_matrix(K, N, 4, 8, seed=K + N, residual=True)
+    (y,), _ = _run_gemv([_upload(mi, residual=True)], [mi.x], residual=True)
+    rng = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([np.arange(64), rng.choice(N, 192, replace=False), np.arange(N - 64, N)]))
+    _assert_close(y[:, rows], _oracle_res(mi, rows=rows), f"residual K={K} N={N} sampled")
+
+
 def test_gemv_residual_workload5_sampled_rows():
     _say("gemv_residual workload 5 (3584->14336, 14336->3584), sampled rows")
     mis = [synth.matrix_inputs(5, m) for m in range(2)]

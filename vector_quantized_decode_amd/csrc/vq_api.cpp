@@ -26,6 +26,9 @@ static bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- shapes
+// Workgroups of the residual kernel resident at once: one per CU.
+static constexpr int64_t kResidentWorkgroups = 256;
+
 Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count) {
   bool all128 = true;
   int64_t max_n = 0, work = 0;
@@ -52,15 +55,26 @@ Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count) {
   // two 32-row steps per wave (1024 rows per workgroup) once the matrices are
   // tall enough to fill them: the per-workgroup OC tile and sign table are
   // then shared by twice the lookups
-  int64_t max_n = 0, max_k = 0;
-  for (int i = 0; i < count; ++i) {
-    if (m[i].N > max_n) max_n = m[i].N;
+  // Row steps per wave (1, 2 or 4; 512 rows per workgroup each).  One
+  // workgroup fills a CU (its LDS tables take 128 KiB), so workgroups beyond
+  // the CU count run in a second round that pays the prologue again.  Cost
+  // model: rounds x (steps + 1), one step of streaming being about as long
+  // as the prologue; ties go to fewer steps (more workgroups in flight).
+  int64_t max_k = 0;
+  for (int i = 0; i < count; ++i)
     if (m[i].K > max_k) max_k = m[i].K;
-  }
   Lut8Shape s{};
   s.nsub = 1;
   s.waves = 16;
-  s.steps = max_n > 2048 ? 2 : 1;
+  s.steps = 1;
+  int64_t best = -1;
+  for (int st = 1; st <= 4; st *= 2) {
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i)
+      wgs += (int64_t)(m[i].K / 256) * ((m[i].N + 512 * st - 1) / (512 * st));
+    const int64_t cost = (wgs + kResidentWorkgroups - 1) / kResidentWorkgroups * (st + 1);
+    if (best < 0 || cost < best) { best = cost; s.steps = st; }
+  }
   // x chunks per thread for the hand-off bound: 2 cover K <= 16384, 4 cover
   // every K that the fixed-point hand-off takes (at most 127 splits)
   s.nbx = max_k > 16384 ? 4 : 2;

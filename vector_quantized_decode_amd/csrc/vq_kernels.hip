@@ -233,11 +233,6 @@ __device__ __forceinline__ void packed_finish(uint64_t *acc, float *y, uint64_t 
     *acc = 0ull;
   }
 }
-__device__ __forceinline__ void packed_add_finish(uint64_t *acc, float *y, float p, const FixedScale &f,
-                                                  int nsplit) {
-  const uint64_t term = packed_term(p, f);
-  packed_finish(acc, y, packed_add(acc, term), term, f, nsplit);
-}
 
 // Sum and max of the magnitudes of 8 fp16 values.
 __device__ __forceinline__ float abs_sum8(u32x4 c) {
@@ -698,7 +693,21 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     for (int t = 0; t < 4; ++t) v |= (((c0 ^ (uint32_t)(4 * q + t)) << 2) & 0xffu) << (8 * t);
     bsel[q] = v;
   }
+  // the hand-off's scale (uniform): fixed point unless an input is not
+  // finite; each step's atomics are issued before the next step's lookups so
+  // their round trips overlap
+  float X2 = 0.f, Mw = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) { X2 += bnd[w]; Mw = fmaxf(Mw, bnd[W + w]); }
+  const float amax = (amax_bits & 0x7fffu) >= 0x7c00u
+                         ? __builtin_inff()
+                         : (float)__builtin_bit_cast(_Float16, (uint16_t)(amax_bits & 0x7fffu));
+  const float bound = __builtin_sqrtf((float)(M.J * 4) * X2) * (Mw + amax) * 1.0009765625f;
+  const bool packed = M.nsplit > 1 && bound <= 3.0e38f && M.nsplit <= 127;
+  const FixedScale fs = fixed_scale(bound);
+  const int rsel = (lane >> 1) & 31;
   float rowval[STEPS];
+  uint64_t term[STEPS], old[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     float A[16], Bv[16], S[16];
@@ -726,10 +735,16 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     for (int i = 0; i < 4; ++i) S[i] += S[i + 4];
     const float sres = ((S[0] + S[2]) + (S[1] + S[3])) * (float)__builtin_bit_cast(_Float16, al[g]);
     rowval[g] = reduce_rows32(A, Bv, lane) + (sres + dpp<DPP_QUAD_XOR1>(sres));
+    const int row = ((rb * STEPS + g) * W + wave) * 32 + rsel;
+    old[g] = 0ull;
+    term[g] = 0ull;
+    if (packed && (lane & 1) == 0 && row < M.N) {
+      term[g] = packed_term(rowval[g], fs);
+      old[g] = packed_add(M.acc + row, term[g]);
+    }
   }
 
   // 8. rows out: lane 2r holds row r of each 32-row group
-  const int rsel = (lane >> 1) & 31;
   if (M.nsplit == 1) {
 #pragma unroll
     for (int g = 0; g < STEPS; ++g) {
@@ -739,24 +754,18 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     }
     return;
   }
-  float X2 = 0.f, Mw = 0.f;
-#pragma unroll
-  for (int w = 0; w < W; ++w) { X2 += bnd[w]; Mw = fmaxf(Mw, bnd[W + w]); }
-  const float amax = (amax_bits & 0x7fffu) >= 0x7c00u
-                         ? __builtin_inff()
-                         : (float)__builtin_bit_cast(_Float16, (uint16_t)(amax_bits & 0x7fffu));
-  const float bound = __builtin_sqrtf((float)(M.J * 4) * X2) * (Mw + amax) * 1.0009765625f;
-  if (bound <= 3.0e38f && M.nsplit <= 127) {
-    const FixedScale fs = fixed_scale(bound);
+  if (packed) {
 #pragma unroll
     for (int g = 0; g < STEPS; ++g) {
       const int rp = (rb * STEPS + g) * W + wave;
       const int row = rp * 32 + rsel;
       if ((lane & 1) == 0 && rp < NP && row < M.N)
-        packed_add_finish(M.acc + row, M.y + row, rowval[g], fs, M.nsplit);
+        packed_finish(M.acc + row, M.y + row, old[g], term[g], fs, M.nsplit);
     }
     return;
   }
+  // non-finite inputs or more than 127 splits: float partials and a
+  // last-workgroup sum
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     const int rp = (rb * STEPS + g) * W + wave;
@@ -801,6 +810,8 @@ int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void
   if (s.steps == 1 && s.nbx == 4) return launch_residual_t<1, 4>(a, grid_x, st);
   if (s.steps == 2 && s.nbx == 2) return launch_residual_t<2, 2>(a, grid_x, st);
   if (s.steps == 2 && s.nbx == 4) return launch_residual_t<2, 4>(a, grid_x, st);
+  if (s.steps == 4 && s.nbx == 2) return launch_residual_t<4, 2>(a, grid_x, st);
+  if (s.steps == 4 && s.nbx == 4) return launch_residual_t<4, 4>(a, grid_x, st);
   return (int)hipErrorInvalidConfiguration;
 }
 

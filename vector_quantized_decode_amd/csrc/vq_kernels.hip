@@ -550,11 +550,14 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   __builtin_amdgcn_s_barrier();
 
   // 2. index, sign and alpha loads: per 32-row step, two index chunks, one
-  //    sign chunk and the scale of the lane's (row, group)
+  //    sign chunk and the scale of the lane's (row, group).  Only the first
+  //    step is loaded here; step g + 1 is issued when step g's lookups start.
+  //    With one step in flight per wave the memory queues stay short, so the
+  //    rotation inputs and each step's data come back in issue order instead
+  //    of behind every workgroup's whole stream.
   u32x4 va[STEPS], vb[STEPS], vs[STEPS];
   uint16_t al[STEPS];
-#pragma unroll
-  for (int g = 0; g < STEPS; ++g) {
+  auto load_step = [&](int g) {
     const int rp = min((rb * STEPS + g) * W + wave, NP - 1);
     const int rga = min(2 * rp, NG - 1), rgb = min(2 * rp + 1, NG - 1);
     va[g] = __builtin_nontemporal_load(
@@ -564,7 +567,8 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     vs[g] = __builtin_nontemporal_load(
         reinterpret_cast<const u32x4 *>(M.signs + (((size_t)sp * NP + rp) * 64 + lane) * 16));
     al[g] = M.alpha[((size_t)sp * NP + rp) * 64 + lane];
-  }
+  };
+  load_step(0);
 
   // 3. x_rot of subvector `lane` of this tile, formed by wave 0 into LDS
   if (wave == 0) {
@@ -710,6 +714,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   uint64_t term[STEPS], old[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
+    if (g + 1 < STEPS) load_step(g + 1);
     float A[16], Bv[16], S[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

@@ -109,6 +109,8 @@ def test_gemv_residual_validation_errors():
     assert _gemv([_m(signs=None)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
     assert _gemv([_m(group=64)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(d=4, nbits=12)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
+    # indices beyond 2 GiB: past the residual kernel's 32-bit buffer offsets
+    assert _gemv([_m(K=65536, N=131072)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(rht_sign=FAKE, had_block=3)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
     assert _gemv([_m(rht_sign=FAKE, had_block=2048)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
     assert _gemv([_m(rht_sign=FAKE, had_block=1024)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EWORKSPACE

@@ -29,6 +29,13 @@ static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workgroups of the residual kernel resident at once: one per CU.
 static constexpr int64_t kResidentWorkgroups = 256;
 
+// Row pairs per workgroup of a matrix with np pairs for a target run of T:
+// the runs of its ceil(np / T) row blocks made as even as possible.
+static int residual_pairs_per_wg(int64_t np, int T) {
+  const int64_t nrb = (np + T - 1) / T;
+  return (int)((np + nrb - 1) / nrb);
+}
+
 Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count) {
   bool all128 = true;
   int64_t max_n = 0, work = 0;
@@ -52,29 +59,35 @@ Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count) {
 }
 
 Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count) {
-  // two 32-row steps per wave (1024 rows per workgroup) once the matrices are
-  // tall enough to fill them: the per-workgroup OC tile and sign table are
-  // then shared by twice the lookups
-  // Row steps per wave (1, 2 or 4; 512 rows per workgroup each).  One
-  // workgroup fills a CU (its LDS tables take 128 KiB), so workgroups beyond
-  // the CU count run in a second round that pays the prologue again.  Cost
-  // model: rounds x (steps + 1), one step of streaming being about as long
-  // as the prologue; ties go to fewer steps (more workgroups in flight).
+  // A workgroup takes a run of 32-row pairs of one 256-input tile; wave w
+  // takes pairs w, w + 16, ... of the run.  One workgroup fills a CU (its LDS
+  // tables take 128 KiB) and the waves keep their loads in flight while they
+  // work, so the layer is best spread over one round of workgroups with equal
+  // runs: the run length T is the smallest (at least one pair per wave) for
+  // which every workgroup is resident at once, up to 8 pairs per wave.
   int64_t max_k = 0;
   for (int i = 0; i < count; ++i)
     if (m[i].K > max_k) max_k = m[i].K;
   Lut8Shape s{};
   s.nsub = 1;
   s.waves = 16;
-  s.steps = 1;
-  int64_t best = -1;
-  for (int st = 1; st <= 4; st *= 2) {
+  int T = 16;
+  for (; T < 16 * 8; ++T) {
     int64_t wgs = 0;
-    for (int i = 0; i < count; ++i)
-      wgs += (int64_t)(m[i].K / 256) * ((m[i].N + 512 * st - 1) / (512 * st));
-    const int64_t cost = (wgs + kResidentWorkgroups - 1) / kResidentWorkgroups * (st + 1);
-    if (best < 0 || cost < best) { best = cost; s.steps = st; }
+    for (int i = 0; i < count; ++i) {
+      const int64_t np = (m[i].N + 31) / 32;
+      wgs += (int64_t)(m[i].K / 256) * ((np + T - 1) / T);
+    }
+    if (wgs <= kResidentWorkgroups) break;
   }
+  s.pairs = T;
+  int max_rpw = 1;
+  for (int i = 0; i < count; ++i) {
+    const int rpw = residual_pairs_per_wg((m[i].N + 31) / 32, T);
+    if (rpw > max_rpw) max_rpw = rpw;
+  }
+  s.steps = 1;
+  while (16 * s.steps < max_rpw) s.steps *= 2;
   // x chunks per thread for the hand-off bound: 2 cover K <= 16384, 4 cover
   // every K that the fixed-point hand-off takes (at most 127 splits)
   s.nbx = max_k > 16384 ? 4 : 2;
@@ -83,7 +96,7 @@ Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count) {
 
 // ---------------------------------------------------------------- workspace
 struct MatPlan {
-  int J, nsplit, nrb, rows_pad;
+  int J, nsplit, nrb, rows_pad, rpw;
   size_t partial_off, counter_off, acc_off, xrot_off;
 };
 
@@ -96,7 +109,7 @@ struct Plan {
 
 static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residual, Plan &p) {
   p.shape = residual ? lut8_shape_residual(m, count) : lut8_shape_plain(m, count);
-  const int R = residual ? p.shape.rows_res() : p.shape.rows();
+  const int R = p.shape.rows();
   const int JT = residual ? 64 : p.shape.jt();
   size_t off = 0;
   // counters and packed accumulators first (both must start at zero and are
@@ -105,7 +118,14 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residua
     MatPlan &q = p.mp[i];
     q.J = m[i].K / m[i].d;
     q.nsplit = (q.J + JT - 1) / JT;
-    q.nrb = (m[i].N + R - 1) / R;
+    if (residual) {
+      const int64_t np = (m[i].N + 31) / 32;
+      q.rpw = residual_pairs_per_wg(np, p.shape.pairs);
+      q.nrb = (int)((np + q.rpw - 1) / q.rpw);
+    } else {
+      q.rpw = 0;
+      q.nrb = (m[i].N + R - 1) / R;
+    }
     q.rows_pad = (m[i].N + 31) / 32 * 32;
     q.counter_off = off;
     off += round_up((size_t)q.nrb * sizeof(uint32_t), 256);
@@ -159,6 +179,9 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
   if (residual) {
     if (!a.signs || !a.alpha) return VQ_EINVAL;
     if (a.group != 128) return VQ_EUNSUPPORTED;
+    // the residual kernel addresses indices, signs and scales with 32-bit
+    // buffer offsets below 2^31
+    if ((int64_t)(a.N + 31) / 32 * 32 * (a.K / 4) >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
     if (a.rht_sign) {
       if (!is_pow2(a.had_block) || a.had_block > 16384 || a.K % a.had_block) return VQ_EINVAL;
     }
@@ -269,6 +292,7 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
     d.rows_pad = q.rows_pad;
     d.nsplit = q.nsplit;
     d.nrb = q.nrb;
+    d.rpw = q.rpw;
     d.acc = reinterpret_cast<uint64_t *>(ws + q.acc_off);
     if (residual) {
       const int h = m[i].rht_sign ? m[i].had_block : 1;

@@ -27,6 +27,7 @@ struct Lut8Mat {
   float had_scale;        // residual: 1/sqrt(had)
   int32_t had;            // residual: Hadamard block (1: no rotation)
   int32_t fused;          // residual: rotate x inside the lookup kernel (else xr holds it)
+  int32_t rpw;            // residual: 32-row pairs per workgroup
   int32_t J;              // subvectors per row, K/4
   int32_t N;              // output rows
   int32_t rows_pad;       // rows of the padded layout (multiple of 32)
@@ -76,8 +77,8 @@ struct Lut8Shape {
   int waves;    // wavefronts per workgroup
   int steps;    // row steps per wave (16 rows each, 32 for the residual kernel)
   int nbx;      // residual: 16-byte chunks of x per thread for the bound (2 or 4)
+  int pairs;    // residual: target 32-row pairs per workgroup
   int rows() const { return waves * steps * 16; }
-  int rows_res() const { return waves * steps * 32; }
   int jt() const { return 64 * nsub; }
 };
 

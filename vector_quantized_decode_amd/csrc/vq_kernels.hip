@@ -133,6 +133,12 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t w, uint32_t base) {
   return __builtin_amdgcn_perm(w, base, 0x0C020000u | ((4u + K) << 8));
 }
 
+// Raw buffer descriptors (gfx9 word 3), an offset past any buffer the kernels
+// address (they stay below 2 GiB), and the nontemporal cache-policy bit.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kNontemporal = 2;
+
 __device__ __forceinline__ u32x4 load16(const uint8_t *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
@@ -557,16 +563,28 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   //    of behind every workgroup's whole stream.
   u32x4 va[STEPS], vb[STEPS], vs[STEPS];
   uint16_t al[STEPS];
+  //    Loads go through buffer descriptors: a step past the workgroup's run
+  //    gets an out-of-range offset, which returns zeros without touching
+  //    memory.  The load is still issued (a branch around it would make the
+  //    compiler wait for every load in flight) but is not looked up.
+  const __amdgpu_buffer_rsrc_t rwi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(M.wi), (short)0, M.nsplit * NG * 1024, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(M.signs), (short)0, M.nsplit * NP * 1024, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t ral = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(M.alpha), (short)0, M.nsplit * NP * 128, kBufferWord3);
   auto load_step = [&](int g) {
-    const int rp = min((rb * STEPS + g) * W + wave, NP - 1);
+    const bool mine = g * W + wave < M.rpw;
+    const int rp = min(rb * M.rpw + g * W + wave, NP - 1);
     const int rga = min(2 * rp, NG - 1), rgb = min(2 * rp + 1, NG - 1);
-    va[g] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(M.wi + (((size_t)sp * NG + rga) * 64 + lane) * 16));
-    vb[g] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(M.wi + (((size_t)sp * NG + rgb) * 64 + lane) * 16));
-    vs[g] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(M.signs + (((size_t)sp * NP + rp) * 64 + lane) * 16));
-    al[g] = M.alpha[((size_t)sp * NP + rp) * 64 + lane];
+    const uint32_t oa = mine ? (uint32_t)(((sp * NG + rga) * 64 + lane) * 16) : kOutOfRange;
+    const uint32_t ob = mine ? (uint32_t)(((sp * NG + rgb) * 64 + lane) * 16) : kOutOfRange;
+    const uint32_t os = mine ? (uint32_t)(((sp * NP + rp) * 64 + lane) * 16) : kOutOfRange;
+    const uint32_t oal = mine ? (uint32_t)(((sp * NP + rp) * 64 + lane) * 2) : kOutOfRange;
+    va[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, oa, 0, kNontemporal));
+    vb[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, ob, 0, kNontemporal));
+    vs[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, os, 0, kNontemporal));
+    al[g] = __builtin_amdgcn_raw_buffer_load_b16(ral, oal, 0, 0);
   };
   load_step(0);
 
@@ -715,6 +733,10 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
     if (g + 1 < STEPS) load_step(g + 1);
+    rowval[g] = 0.f;
+    old[g] = 0ull;
+    term[g] = 0ull;
+    if (g * W + wave >= M.rpw) continue;      // past the run: nothing to look up
     float A[16], Bv[16], S[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -740,9 +762,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     for (int i = 0; i < 4; ++i) S[i] += S[i + 4];
     const float sres = ((S[0] + S[2]) + (S[1] + S[3])) * (float)__builtin_bit_cast(_Float16, al[g]);
     rowval[g] = reduce_rows32(A, Bv, lane) + (sres + dpp<DPP_QUAD_XOR1>(sres));
-    const int row = ((rb * STEPS + g) * W + wave) * 32 + rsel;
-    old[g] = 0ull;
-    term[g] = 0ull;
+    const int row = (rb * M.rpw + g * W + wave) * 32 + rsel;
     if (packed && (lane & 1) == 0 && row < M.N) {
       term[g] = packed_term(rowval[g], fs);
       old[g] = packed_add(M.acc + row, term[g]);
@@ -753,18 +773,17 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   if (M.nsplit == 1) {
 #pragma unroll
     for (int g = 0; g < STEPS; ++g) {
-      const int rp = (rb * STEPS + g) * W + wave;
+      const int rp = rb * M.rpw + g * W + wave;
       const int row = rp * 32 + rsel;
-      if ((lane & 1) == 0 && rp < NP && row < M.N) M.y[row] = rowval[g];
+      if ((lane & 1) == 0 && g * W + wave < M.rpw && row < M.N) M.y[row] = rowval[g];
     }
     return;
   }
   if (packed) {
 #pragma unroll
     for (int g = 0; g < STEPS; ++g) {
-      const int rp = (rb * STEPS + g) * W + wave;
-      const int row = rp * 32 + rsel;
-      if ((lane & 1) == 0 && rp < NP && row < M.N)
+      const int row = (rb * M.rpw + g * W + wave) * 32 + rsel;
+      if ((lane & 1) == 0 && g * W + wave < M.rpw && row < M.N)
         packed_finish(M.acc + row, M.y + row, old[g], term[g], fs, M.nsplit);
     }
     return;
@@ -773,11 +792,11 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   // last-workgroup sum
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
-    const int rp = (rb * STEPS + g) * W + wave;
+    const int rp = rb * M.rpw + g * W + wave;
     const int row = rp * 32 + rsel;
-    if ((lane & 1) == 0 && rp < NP) store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
+    if ((lane & 1) == 0 && g * W + wave < M.rpw && rp < NP) store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
   }
-  split_finish(M, rb, STEPS * W * 32, flag);
+  split_finish(M, rb, 32 * M.rpw, flag);
 }
 
 // --------------------------------------------------------------------------
@@ -817,6 +836,8 @@ int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void
   if (s.steps == 2 && s.nbx == 4) return launch_residual_t<2, 4>(a, grid_x, st);
   if (s.steps == 4 && s.nbx == 2) return launch_residual_t<4, 2>(a, grid_x, st);
   if (s.steps == 4 && s.nbx == 4) return launch_residual_t<4, 4>(a, grid_x, st);
+  if (s.steps == 8 && s.nbx == 2) return launch_residual_t<8, 2>(a, grid_x, st);
+  if (s.steps == 8 && s.nbx == 4) return launch_residual_t<8, 4>(a, grid_x, st);
   return (int)hipErrorInvalidConfiguration;
 }
 

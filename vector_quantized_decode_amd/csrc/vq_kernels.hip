@@ -345,13 +345,15 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
   // every wave's small loads enter the memory pipeline before the index stream
   __builtin_amdgcn_s_barrier();
 
-  // 2. every index load of this workgroup, issued up front and unconditional
-  //    (branches here would make the compiler wait for all loads before the
-  //    OC build); streamed past the caches.  Row groups past the end load the
-  //    last row group instead; their sums are never written.
+  // 2. index loads, streamed past the caches: the first row step now, step
+  //    g + 1 when step g's lookups start.  One step in flight per wave keeps
+  //    the memory queues short, so the OC inputs and each step's indices come
+  //    back in issue order instead of behind every workgroup's whole stream.
+  //    Loads are unconditional (a branch around one would make the compiler
+  //    wait for every load in flight); row groups past the end load the last
+  //    row group instead and their sums are never written.
   u32x4 v[STEPS][NSUB];
-#pragma unroll
-  for (int g = 0; g < STEPS; ++g) {
+  auto load_step = [&](int g) {
     const int rg = min((rb * STEPS + g) * W + wave, NG - 1);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
@@ -359,7 +361,8 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
       v[g][s] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4 *>(M.wi + (((size_t)jt * NG + rg) * 64 + lane) * 16));
     }
-  }
+  };
+  load_step(0);
 
   // 3. OC[j][c] = x_j . WC[c] on the matrix cores: one 2-block 32x32x4 fp16
   //    MFMA per sub-tile (fp32 accumulation).  Output register r of lane l
@@ -419,6 +422,7 @@ __global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args)
   uint64_t term[STEPS], old[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
+    if (g + 1 < STEPS) load_step(g + 1);
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;

@@ -45,7 +45,7 @@ METRIC = "µs/layer and effective HBM GB/s (% of peak) for VQ-GEMV at LLaMA-7B, 
 CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
 # source of each workload's lookup kernel (8-bit indices: output-codebook tile
 # kernels; 12- and 16-bit indices: virtual-codebook kernels)
-KERNEL_SRC = {1: "vq_kernels.hip", 2: "vq_kernels.hip", 3: "vq_kernels_wc.hip",
+KERNEL_SRC = {1: "vq_kernels_wc.hip", 2: "vq_kernels_wc.hip", 3: "vq_kernels_wc.hip",
               4: "vq_kernels_wc.hip", 5: "vq_kernels.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 

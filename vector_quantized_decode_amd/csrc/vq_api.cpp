@@ -8,6 +8,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "vq_internal.h"
 
 namespace vqd {
@@ -36,28 +38,6 @@ static int residual_pairs_per_wg(int64_t np, int T) {
   return (int)((np + nrb - 1) / nrb);
 }
 
-Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count) {
-  bool all128 = true;
-  int64_t max_n = 0, work = 0;
-  for (int i = 0; i < count; ++i) {
-    const int J = m[i].K / m[i].d;
-    if (J % 128) all128 = false;
-    if (m[i].N > max_n) max_n = m[i].N;
-    work += (int64_t)m[i].N * J;
-  }
-  Lut8Shape s{};
-  s.nsub = all128 ? 2 : 1;
-  if (work <= (int64_t)1 << 20) {   // small layers: more, smaller workgroups
-    s.waves = 4;
-    s.steps = 1;
-  } else {
-    s.waves = 16;
-    s.steps = 2;
-  }
-  (void)max_n;
-  return s;
-}
-
 Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count) {
   // A workgroup takes a run of 32-row pairs of one 256-input tile; wave w
   // takes pairs w, w + 16, ... of the run.  One workgroup fills a CU (its LDS
@@ -69,7 +49,6 @@ Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count) {
   for (int i = 0; i < count; ++i)
     if (m[i].K > max_k) max_k = m[i].K;
   Lut8Shape s{};
-  s.nsub = 1;
   s.waves = 16;
   int T = 16;
   for (; T < 16 * 8; ++T) {
@@ -107,10 +86,10 @@ struct Plan {
   int64_t grid;
 };
 
-static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residual, Plan &p) {
-  p.shape = residual ? lut8_shape_residual(m, count) : lut8_shape_plain(m, count);
-  const int R = p.shape.rows();
-  const int JT = residual ? 64 : p.shape.jt();
+// Workspace plan of the residual kernel (the other kernels take none).
+static void make_plan(const vq_matrix *m, int32_t count, int32_t B, Plan &p) {
+  p.shape = lut8_shape_residual(m, count);
+  const int JT = 64;
   size_t off = 0;
   // counters and packed accumulators first (both must start at zero and are
   // left at zero by every call), then partials, then x_rot
@@ -118,14 +97,9 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residua
     MatPlan &q = p.mp[i];
     q.J = m[i].K / m[i].d;
     q.nsplit = (q.J + JT - 1) / JT;
-    if (residual) {
-      const int64_t np = (m[i].N + 31) / 32;
-      q.rpw = residual_pairs_per_wg(np, p.shape.pairs);
-      q.nrb = (int)((np + q.rpw - 1) / q.rpw);
-    } else {
-      q.rpw = 0;
-      q.nrb = (m[i].N + R - 1) / R;
-    }
+    const int64_t np = (m[i].N + 31) / 32;
+    q.rpw = residual_pairs_per_wg(np, p.shape.pairs);
+    q.nrb = (int)((np + q.rpw - 1) / q.rpw);
     q.rows_pad = (m[i].N + 31) / 32 * 32;
     q.counter_off = off;
     off += round_up((size_t)q.nrb * sizeof(uint32_t), 256);
@@ -142,7 +116,7 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, bool residua
   for (int i = 0; i < count; ++i) {
     MatPlan &q = p.mp[i];
     q.xrot_off = off;
-    if (residual) off += round_up((size_t)B * m[i].K * sizeof(float), 256);
+    off += round_up((size_t)B * m[i].K * sizeof(float), 256);
   }
   p.bytes = off;
 }
@@ -227,6 +201,9 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
   // Workgroups are dispatched in grid order, matrix by matrix; the matrices
   // with the longest rows (most work per wave) go first so they do not start
   // last and set the tail.  Results do not depend on the order.
+  int64_t indices = 0;
+  for (int i = 0; i < count; ++i) indices += (int64_t)m[i].N * (m[i].K / m[i].d);
+  const int w8 = wc8_waves(indices);
   int order[VQ_MAX_GROUP];
   for (int i = 0; i < count; ++i) order[i] = i;
   for (int a = 1; a < count; ++a)
@@ -246,30 +223,39 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     d.N = m[i].N;
     d.B = B;
     d.ldy = m[i].N;
-    d.jsplit = (f == FMT_WC12) ? wc12_jsplit(d.J) : wc16_jsplit(d.J);
-    const int R = (f == FMT_WC12) ? wc12_rows_per_wg(d.jsplit) : wc16_rows_per_wg(d.jsplit);
+    d.jsplit = (f == FMT_LUT8)   ? wc8_jsplit(m[i].N, d.J)
+               : (f == FMT_WC12) ? wc12_jsplit(d.J)
+                                 : wc16_jsplit(d.J);
+    const int R = (f == FMT_LUT8)   ? wc8_rows_per_wg(d.jsplit, w8)
+                  : (f == FMT_WC12) ? wc12_rows_per_wg(d.jsplit)
+                                    : wc16_rows_per_wg(d.jsplit);
     d.nwg = (m[i].N + R - 1) / R;
     if (d.nwg > max_wg) max_wg = d.nwg;
     if (d.J > max_j) max_j = d.J;
   }
   if (max_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
-  const int err = (f == FMT_WC12) ? launch_wc12(args, (int)max_wg, max_j, stream)
-                                  : launch_wc16(args, (int)max_wg, stream);
+  const int err = (f == FMT_LUT8)   ? launch_wc8(args, (int)max_wg, w8, stream)
+                  : (f == FMT_WC12) ? launch_wc12(args, (int)max_wg, max_j, stream)
+                                    : launch_wc16(args, (int)max_wg, stream);
   return hip_status(err);
 }
 
-static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                       float *const *y, void *workspace, size_t ws_bytes, void *stream, bool residual) {
-  int st = check_group(m, count, x, B, y, residual);
+static int gemv_plain(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                      float *const *y, void *stream) {
+  const int st = check_group(m, count, x, B, y, false);
   if (st != VQ_OK) return st;
-  if (format_of(m[0]) != FMT_LUT8) return gemv_wc(m, count, x, B, y, stream);
+  return gemv_wc(m, count, x, B, y, stream);
+}
+
+static int gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                         float *const *y, void *workspace, size_t ws_bytes, void *stream) {
+  int st = check_group(m, count, x, B, y, true);
+  if (st != VQ_OK) return st;
   Plan p;
-  make_plan(m, count, B, residual, p);
+  make_plan(m, count, B, p);
   if (p.grid > 0x7fffffff) return VQ_EUNSUPPORTED;
-  if (p.bytes > 0) {
-    if (!workspace || ws_bytes < p.bytes) return VQ_EWORKSPACE;
-    if (!aligned(workspace, 256)) return VQ_EALIGN;
-  }
+  if (!workspace || ws_bytes < p.bytes) return VQ_EWORKSPACE;
+  if (!aligned(workspace, 256)) return VQ_EALIGN;
   char *ws = static_cast<char *>(workspace);
   Lut8Args args;
   memset(&args, 0, sizeof(args));
@@ -281,9 +267,9 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
     d.wi = static_cast<const uint8_t *>(m[i].wi);
     d.wc = m[i].wc;
     d.x = x[i];
-    d.xr = residual ? reinterpret_cast<const float *>(ws + q.xrot_off) : nullptr;
-    d.signs = residual ? static_cast<const uint8_t *>(m[i].signs) : nullptr;
-    d.alpha = residual ? static_cast<const uint16_t *>(m[i].alpha) : nullptr;
+    d.xr = reinterpret_cast<const float *>(ws + q.xrot_off);
+    d.signs = static_cast<const uint8_t *>(m[i].signs);
+    d.alpha = static_cast<const uint16_t *>(m[i].alpha);
     d.y = y[i];
     d.partial = q.nsplit > 1 ? reinterpret_cast<float *>(ws + q.partial_off) : nullptr;
     d.counter = reinterpret_cast<uint32_t *>(ws + q.counter_off);
@@ -294,33 +280,27 @@ static int gemv_common(const vq_matrix *m, int32_t count, const uint16_t *const 
     d.nrb = q.nrb;
     d.rpw = q.rpw;
     d.acc = reinterpret_cast<uint64_t *>(ws + q.acc_off);
-    if (residual) {
-      const int h = m[i].rht_sign ? m[i].had_block : 1;
-      d.rs = m[i].rht_sign;
-      d.had = h;
-      d.had_scale = (float)(1.0 / sqrt((double)h));
-      d.alpha_hdr = reinterpret_cast<const uint32_t *>(static_cast<const char *>(m[i].alpha) +
-                                                       alpha_body_bytes(m[i].N, m[i].K));
-      // blocks up to 2048 are rotated inside the lookup kernel; larger ones first
-      // by the rotation kernel, into the workspace
-      d.fused = h <= 2048 ? 1 : 0;
-    }
+    const int h = m[i].rht_sign ? m[i].had_block : 1;
+    d.rs = m[i].rht_sign;
+    d.had = h;
+    d.had_scale = (float)(1.0 / sqrt((double)h));
+    d.alpha_hdr = reinterpret_cast<const uint32_t *>(static_cast<const char *>(m[i].alpha) +
+                                                     alpha_body_bytes(m[i].N, m[i].K));
+    // blocks up to 2048 are rotated inside the lookup kernel; larger ones first
+    // by the rotation kernel, into the workspace
+    d.fused = h <= 2048 ? 1 : 0;
     d.nwg = q.nsplit * q.nrb;
     if (d.nwg > max_wg) max_wg = d.nwg;
   }
   int err;
-  if (residual) {
-    for (int i = 0; i < count; ++i) {
-      if (args.mat[i].fused) continue;        // rotated inside the lookup kernel
-      const int h = args.mat[i].had;
-      err = launch_rht(x[i], m[i].rht_sign, B, m[i].K, h, args.mat[i].had_scale,
-                       reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);
-      if (err) return hip_status(err);
-    }
-    err = launch_lut8_residual(args, p.shape, max_wg, stream);
-  } else {
-    err = launch_lut8_plain(args, p.shape, max_wg, stream);
+  for (int i = 0; i < count; ++i) {
+    if (args.mat[i].fused) continue;          // rotated inside the lookup kernel
+    const int h = args.mat[i].had;
+    err = launch_rht(x[i], m[i].rht_sign, B, m[i].K, h, args.mat[i].had_scale,
+                     reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);
+    if (err) return hip_status(err);
   }
+  err = launch_lut8_residual(args, p.shape, max_wg, stream);
   return hip_status(err);
 }
 
@@ -375,9 +355,9 @@ size_t vq_workspace_bytes(const vq_matrix *m, int32_t count, int32_t B, int32_t 
     const vq_matrix &a = m[i];
     if (a.K <= 0 || a.N <= 0 || a.d <= 0 || a.K % a.d) return 0;
   }
-  if (format_of(m[0]) != FMT_LUT8) return 0;     // the virtual-OC kernels use none
+  if (!residual || format_of(m[0]) != FMT_LUT8) return 0;   // only the residual kernel takes one
   Plan p;
-  make_plan(m, count, B, residual != 0, p);
+  make_plan(m, count, B, p);
   return p.bytes;
 }
 
@@ -461,12 +441,14 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K, int32_t 
 
 int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B, float *const *y,
             void *workspace, size_t ws_bytes, void *stream) {
-  return gemv_common(m, count, x, B, y, workspace, ws_bytes, stream, false);
+  (void)workspace;   // no kernel of vq_gemv needs one (vq_workspace_bytes gives 0)
+  (void)ws_bytes;
+  return gemv_plain(m, count, x, B, y, stream);
 }
 
 int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                      float *const *y, void *workspace, size_t ws_bytes, void *stream) {
-  return gemv_common(m, count, x, B, y, workspace, ws_bytes, stream, true);
+  return gemv_residual(m, count, x, B, y, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

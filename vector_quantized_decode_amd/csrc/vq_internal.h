@@ -64,6 +64,10 @@ struct WcArgs {
 
 int wc12_rows_per_wg(int jsplit);
 int wc12_jsplit(int J);
+int wc8_waves(int64_t indices);
+int wc8_rows_per_wg(int jsplit, int waves);
+int wc8_jsplit(int N, int J);
+int launch_wc8(const WcArgs &a, int grid_x, int waves, void *stream);
 int wc16_rows_per_wg(int jsplit);
 int wc16_jsplit(int J);
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
@@ -73,23 +77,18 @@ int launch_repack_wi16(const uint8_t *canon, int N, int J, uint8_t *dev, void *s
 
 // Launch shape of one lookup-kernel variant.
 struct Lut8Shape {
-  int nsub;     // 64-subvector tiles per workgroup (1 or 2)
   int waves;    // wavefronts per workgroup
-  int steps;    // row steps per wave (16 rows each, 32 for the residual kernel)
-  int nbx;      // residual: 16-byte chunks of x per thread for the bound (2 or 4)
-  int pairs;    // residual: target 32-row pairs per workgroup
-  int rows() const { return waves * steps * 16; }
-  int jt() const { return 64 * nsub; }
+  int steps;    // 32-row steps per wave (at least the run / waves)
+  int nbx;      // 16-byte chunks of x per thread for the hand-off bound (2 or 4)
+  int pairs;    // target 32-row pairs per workgroup
 };
 
 // Variant selection (shared by workspace sizing and launch).
-Lut8Shape lut8_shape_plain(const vq_matrix *m, int32_t count);
 Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count);
 
 // Kernel launchers: return a hipError_t value (0 = success).
 // Lookup kernels: grid (grid_x, a.count), grid_x = the most workgroups any
 // matrix of the call needs.
-int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream);
 int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream);
 int launch_pack(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, void *stream);
 int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out, void *stream);

@@ -13,25 +13,34 @@
 //          Hadamard rotation, 1-bit sign residual with one fp16 scale per
 //          group of 128 weights, LUT inference with bit operations).
 //
-// How the lookup GEMV maps onto a CDNA4 compute unit (d = 4, n = 8, B = 1):
-//   * A workgroup owns a tile of 64*NSUB subvectors (j) and a block of rows.
-//     It builds the OC tile for its subvectors in LDS, fp32, laid out as
-//     word((s*256 + c)*64 + l) for subvector j = 64 s + l and centroid c, so
-//     the LDS bank of an entry depends only on l.  Lane l of every wavefront
-//     always works on subvector l: the 64 lanes of one LDS read hit 64
-//     different banks whatever the indices are -- the conflict-free lookup
-//     of [EVA 2.A] expressed as a bank layout.
+// This file holds the lookup GEMV with a materialized output-codebook tile
+// (used for the rotated 8-bit matrices with a 1-bit sign residual), the
+// rotation kernel for large Hadamard blocks, the explicit OC build, and the
+// packing / layout helpers.  The plain GEMVs (no residual) keep the output
+// codebook virtual: vq_kernels_wc.hip.
+//
+// How the residual lookup GEMV maps onto a CDNA4 compute unit (d = 4, n = 8,
+// B = 1):
+//   * A workgroup owns one tile of 64 subvectors (256 inputs) and a run of
+//     32-row pairs.  It builds the OC tile for its subvectors in LDS, fp32,
+//     laid out as word(c*64 + l) for subvector l of the tile and centroid c,
+//     so the LDS bank of an entry depends only on l.  Lane l of every
+//     wavefront always works on subvector l: the 64 lanes of one LDS read hit
+//     64 different banks whatever the indices are -- the conflict-free lookup
+//     of [EVA 2.A] expressed as a bank layout.  The OC entries come from the
+//     matrix cores: OC = x_rot . WC^T is a (64 x 4) x (4 x 256) product.
 //   * Indices stream from HBM in 1 KiB chunks (16 rows x 64 subvectors, one
-//     16-byte load per lane, fully coalesced), read once.
+//     16-byte load per lane, fully coalesced), read once, one row step in
+//     flight per wave.
 //   * One v_perm_b32 turns an index byte into the LDS byte address
 //     (lane*4 | c<<8 | region<<16): one VALU op, one LDS read and one add per
 //     lookup.
-//   * Each lane accumulates 16 rows; the cross-lane "adder tree" of
+//   * Each lane accumulates 32 rows; the cross-lane "adder tree" of
 //     [EVA 2.B] is a transposing butterfly built from gfx950 permlane swaps
-//     and DPP moves that leaves row r of the 16 in lanes 4r..4r+3.
-//   * Workgroups that share a row block (a split along J) write fp32 partial
-//     sums; the last one to finish (an atomic counter) adds them in fixed
-//     split order and writes y, so results are bitwise reproducible.
+//     and DPP moves.
+//   * Workgroups that share rows (a split along K) hand their partial sums
+//     over with one 64-bit fixed-point atomic per row, so y does not depend
+//     on the order in which they arrive (bitwise reproducible).
 #include <hip/hip_runtime.h>
 
 #include "vq_internal.h"
@@ -82,26 +91,6 @@ __device__ __forceinline__ float tstage(float lo, float hi, bool bit) {
   float send = bit ? lo : hi;
   float keep = bit ? hi : lo;
   return keep + dpp<CTRL>(send);
-}
-
-// a[0..15] hold per-lane partial sums of rows 0..15.  Returns the full sum
-// over the 64 lanes of row (lane >> 2) & 15 in every lane.
-__device__ __forceinline__ float reduce_rows16(float (&a)[16], int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { swap32(a[i], a[i + 8]); a[i] += a[i + 8]; }
-  // a[i], i < 8: row i + 8*bit5
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { swap16(a[i], a[i + 4]); a[i] += a[i + 4]; }
-  // a[i], i < 4: row i + 4*bit4 + 8*bit5
-  const bool b3 = lane & 8, b2 = lane & 4;
-  a[0] = tstage<DPP_ROW_ROR8>(a[0], a[2], b3);
-  a[1] = tstage<DPP_ROW_ROR8>(a[1], a[3], b3);
-  // a[i], i < 2: row i + 2*bit3 + 4*bit4 + 8*bit5
-  float v = tstage<DPP_ROW_HALF_MIRROR>(a[0], a[1], b2);
-  // v: row bit2 + 2*bit3 + ..., partial over lanes {i, 7-i} of each 8 lanes
-  v += dpp<DPP_QUAD_XOR1>(v);
-  v += dpp<DPP_QUAD_XOR2>(v);
-  return v;
 }
 
 // Rows 0..15 in A, rows 16..31 in Bv.  Returns the full sum of row
@@ -240,16 +229,6 @@ __device__ __forceinline__ void packed_finish(uint64_t *acc, float *y, uint64_t 
   }
 }
 
-// Sum and max of the magnitudes of 8 fp16 values.
-__device__ __forceinline__ float abs_sum8(u32x4 c) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const half2_t h = as_h2(c[i] & 0x7fff7fffu);
-    s += (float)h.x + (float)h.y;
-  }
-  return s;
-}
 // Sum of squares of 8 fp16 values (fp32).
 __device__ __forceinline__ float sq_sum8(u32x4 c) {
   float s = 0.f;
@@ -260,16 +239,6 @@ __device__ __forceinline__ float sq_sum8(u32x4 c) {
     s = __builtin_fmaf((float)h.y, (float)h.y, s);
   }
   return s;
-}
-
-// Largest magnitude of 8 fp16 values, compared as integer bits so that an
-// infinity or NaN gives +inf (the caller then leaves the fixed-point path).
-__device__ __forceinline__ float abs_max8(u32x4 c) {
-  uint32_t m = 0u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m = max(m, max(c[i] & 0x7fffu, (c[i] >> 16) & 0x7fffu));
-  if (m >= 0x7c00u) return __builtin_inff();
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)m);
 }
 
 // Wave-wide sum and max: quad and row butterflies with DPP, then 16- and
@@ -303,194 +272,22 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // --------------------------------------------------------------------------
-// Plain lookup GEMV: y[r] = sum_j OC[j, WI[r, j]]   [EVA 2.A, 2.B]
-// --------------------------------------------------------------------------
-template <int NSUB, int W, int STEPS>
-__global__ void __launch_bounds__(W * 64) lut8_plain_kernel(const Lut8Args args) {
-  constexpr int NT = W * 64;
-  constexpr int TASKS = NSUB * 8;                  // OC sub-tiles: 64 subvectors x 32 centroids
-  constexpr int TPW = (TASKS + W - 1) / W;         // sub-tiles per wave
-  __shared__ float lds[NSUB * 16384 + 2 * W + 16];
-  float *bnd = lds + NSUB * 16384;                 // per-wave bound parts
-  uint32_t *flag = reinterpret_cast<uint32_t *>(bnd + 2 * W);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Lut8Mat &M = args.mat[blockIdx.y];
-  if ((int)blockIdx.x >= M.nwg) return;
-  const int local = blockIdx.x;
-  const int sp = local % M.nsplit, rb = local / M.nsplit;
-  const int NG = (M.N + 15) >> 4;
-  const uint8_t *xb = reinterpret_cast<const uint8_t *>(M.x);
-  const uint8_t *wcb = reinterpret_cast<const uint8_t *>(M.wc);
-
-  // 1. inputs of the output-codebook tile.  Sub-tile t = (s, cb) covers
-  //    subvectors 64 (sp NSUB + s) + l and centroids 32 cb + (l % 32); lane l
-  //    holds x_j and WC[c] as four fp16 each (the host picks NSUB so that
-  //    64*NSUB divides J: every subvector exists).
-  half4_t xa[TPW], wa[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = min(wave + u * W, TASKS - 1);
-    const int s = t >> 3, cb = t & 7;
-    xa[u] = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(xb + 8 * ((size_t)(sp * NSUB + s) * 64 + lane)));
-    wa[u] = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(wcb + 8 * (cb * 32 + (lane & 31))));
-  }
-  //    inputs of the bound |partial| <= sum_k |x_k| * max |WC| used by the
-  //    fixed-point hand-off: x in 16-byte chunks t and t + NT, WC chunk t
-  const int nxc = M.J >> 1;                        // 16-byte chunks of x
-  const int t0 = threadIdx.x, t1 = threadIdx.x + NT;
-  const u32x4 xb0 = load16(xb + 16 * (size_t)min(t0, nxc - 1));
-  const u32x4 xb1 = load16(xb + 16 * (size_t)min(t1, nxc - 1));
-  const u32x4 wb = load16(wcb + 16 * min(t0, 127));
-  // every wave's small loads enter the memory pipeline before the index stream
-  __builtin_amdgcn_s_barrier();
-
-  // 2. index loads, streamed past the caches: the first row step now, step
-  //    g + 1 when step g's lookups start.  One step in flight per wave keeps
-  //    the memory queues short, so the OC inputs and each step's indices come
-  //    back in issue order instead of behind every workgroup's whole stream.
-  //    Loads are unconditional (a branch around one would make the compiler
-  //    wait for every load in flight); row groups past the end load the last
-  //    row group instead and their sums are never written.
-  u32x4 v[STEPS][NSUB];
-  auto load_step = [&](int g) {
-    const int rg = min((rb * STEPS + g) * W + wave, NG - 1);
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int jt = sp * NSUB + s;
-      v[g][s] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4 *>(M.wi + (((size_t)jt * NG + rg) * 64 + lane) * 16));
-    }
-  };
-  load_step(0);
-
-  // 3. OC[j][c] = x_j . WC[c] on the matrix cores: one 2-block 32x32x4 fp16
-  //    MFMA per sub-tile (fp32 accumulation).  Output register r of lane l
-  //    holds block r/16, centroid row m = ((r%16)/4) 8 + (l/32) 4 + r%4 and
-  //    subvector column l%32; swapping the upper lanes of register i with the
-  //    lower lanes of register i+16 leaves one centroid per register with
-  //    subvector 64 s + l in lane l, so each LDS store hits 64 banks.
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = wave + u * W;
-    if (t < TASKS) {
-      const int s = t >> 3, cb = t & 7;
-      f32x32_t o = {};
-      o = __builtin_amdgcn_mfma_f32_32x32x4f16(wa[u], xa[u], o, 0, 0, 0);
-      float *dst = lds + (s * 256 + cb * 32) * 64 + lane;
-      const int mhi = (lane >> 5) * 4;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float a = o[i], b = o[i + 16];
-        swap32(a, b);
-        const int m = (i >> 2) * 8 + (i & 3);    // centroid row of a (lanes < 32 half)
-        dst[(m) * 64] = a;                        // centroid 32 cb + m
-        dst[(m + 4) * 64] = b;                    // centroid 32 cb + m + 4
-      }
-      (void)mhi;
-    }
-  }
-  //    per-wave parts of the bound
-  {
-    float sx = 0.f;
-    if (t0 < nxc) sx += abs_sum8(xb0);
-    if (t1 < nxc) sx += abs_sum8(xb1);
-    for (int t = t0 + 2 * NT; t < nxc; t += NT)   // inputs longer than 16*NT halves
-      sx += abs_sum8(load16(xb + 16 * (size_t)t));
-    const float mw = (t0 < 128) ? abs_max8(wb) : 0.f;
-    const float ws = wave_sum(sx), wm = wave_max(mw);
-    if (lane == 0) { bnd[wave] = ws; bnd[W + wave] = wm; }
-  }
-  // keep index-dependent work out of the OC build (it would wait for loads)
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-
-  // 4. the hand-off's scale (uniform): fixed point unless an input is not finite
-  float S = 0.f, Mw = 0.f;
-#pragma unroll
-  for (int w = 0; w < W; ++w) { S += bnd[w]; Mw = fmaxf(Mw, bnd[W + w]); }
-  const float bound = S * Mw * 1.0009765625f;     // margin for fp32 rounding
-  const bool packed = M.nsplit > 1 && bound <= 3.0e38f && M.nsplit <= 127;
-  const FixedScale fs = fixed_scale(bound);
-  const int rsel = (lane >> 2) & 15;
-
-  // 5. conflict-free lookups and the cross-lane adder tree; with the
-  //    fixed-point hand-off a step's atomics are issued before the next
-  //    step's lookups so their round trips overlap
-  const uint32_t base0 = (uint32_t)lane << 2;
-  float rowval[STEPS];
-  uint64_t term[STEPS], old[STEPS];
-#pragma unroll
-  for (int g = 0; g < STEPS; ++g) {
-    if (g + 1 < STEPS) load_step(g + 1);
-    float acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const uint32_t base = base0 | ((uint32_t)s << 16);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w = v[g][s][q];
-        acc[4 * q + 0] += lds_at(lds, lut_addr<0>(w, base));
-        acc[4 * q + 1] += lds_at(lds, lut_addr<1>(w, base));
-        acc[4 * q + 2] += lds_at(lds, lut_addr<2>(w, base));
-        acc[4 * q + 3] += lds_at(lds, lut_addr<3>(w, base));
-      }
-    }
-    rowval[g] = reduce_rows16(acc, lane);
-    const int row = ((rb * STEPS + g) * W + wave) * 16 + rsel;
-    old[g] = 0ull;
-    term[g] = 0ull;
-    if (packed && (lane & 3) == 0 && row < M.N) {
-      term[g] = packed_term(rowval[g], fs);
-      old[g] = packed_add(M.acc + row, term[g]);
-    }
-  }
-
-  // 6. rows out (lane 4r holds row r of its 16-row group)
-  if (M.nsplit == 1) {
-#pragma unroll
-    for (int g = 0; g < STEPS; ++g) {
-      const int row = ((rb * STEPS + g) * W + wave) * 16 + rsel;
-      if ((lane & 3) == 0 && row < M.N) M.y[row] = rowval[g];
-    }
-    return;
-  }
-  if (packed) {
-#pragma unroll
-    for (int g = 0; g < STEPS; ++g) {
-      const int row = ((rb * STEPS + g) * W + wave) * 16 + rsel;
-      if ((lane & 3) == 0 && row < M.N) packed_finish(M.acc + row, M.y + row, old[g], term[g], fs, M.nsplit);
-    }
-    return;
-  }
-  // non-finite inputs: float partials and a last-workgroup sum
-#pragma unroll
-  for (int g = 0; g < STEPS; ++g) {
-    const int rg = (rb * STEPS + g) * W + wave;
-    const int row = rg * 16 + rsel;
-    if ((lane & 3) == 0 && rg < NG) store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
-  }
-  split_finish(M, rb, STEPS * W * 16, flag);
-}
-
-// --------------------------------------------------------------------------
 // Rotated lookup GEMV + 1-bit sign residual   [EDGE section details]
-// Region 0 of LDS: OC tile of 64 subvectors (from x_rot).  Region 1: for the
-// 32 sign bytes of the same 256 weights, T[v][p] = sum_i (bit_i(v) ? +1 : -1)
-// * x_rot[8p + i], stored twice (lanes p and p + 32) so that region 1 has the
-// same lane -> bank layout as region 0.
+// LDS: the sign table at 0 and the OC tile of the workgroup's 64 subvectors
+// (from x_rot) at 64 KiB.  For the 32 sign bytes of the same 256 weights the
+// table holds T[v][p] = sum_i (bit_i(v) ? +1 : -1) * x_rot[8p + i] in columns
+// p and p + 32, so that a lane can always find its position in a column no
+// other lane of its half-wave reads.
 //
 // The rotation is fused for Hadamard blocks h <= 2048.  In Sylvester (natural)
 // order H_h = H_{h/256} (x) H_256 for h >= 256, so the 256 rotated inputs of a
 // tile, which sit in sub-block q of their block, are the 256-point transform
-// of sum_{q'} (-1)^popcount(q & q') (s (.) x)[sub-block q'].  Every wave forms
+// of sum_{q'} (-1)^popcount(q & q') (s (.) x)[sub-block q'].  Wave 0 forms
 // that combination and the 256-point butterfly in registers (lane l holds
-// elements 4l .. 4l+3, partners across lanes by xor shuffles), ending with
-// x_rot of subvector l in lane l -- no LDS and no barrier.  For h < 256 the
-// tile holds whole blocks and only the butterfly stages below h run.  Larger
-// blocks are rotated by rht_kernel into the workspace first (M.xr).
+// elements 4l .. 4l+3, partners across lanes by xor shuffles) and leaves
+// x_rot of the tile in LDS for the other waves.  For h < 256 the tile holds
+// whole blocks and only the butterfly stages below h run.  Larger blocks are
+// rotated by rht_kernel into the workspace first (M.xr).
 // --------------------------------------------------------------------------
 __device__ __forceinline__ float sign_of_byte(uint32_t s4, int t) {
   return (float)(int8_t)((s4 >> (8 * t)) & 0xffu);
@@ -806,24 +603,6 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
 // --------------------------------------------------------------------------
 // launchers of the lookup kernels
 // --------------------------------------------------------------------------
-template <int NSUB, int W, int STEPS>
-static int launch_plain_t(const Lut8Args &a, int grid_x, hipStream_t st) {
-  (void)hipGetLastError();  // report only this launch's error
-  hipLaunchKernelGGL((lut8_plain_kernel<NSUB, W, STEPS>), dim3(grid_x, a.count), dim3(W * 64), 0, st, a);
-  return (int)hipGetLastError();
-}
-
-int launch_lut8_plain(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream) {
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (s.nsub == 2 && s.waves == 16 && s.steps == 2) return launch_plain_t<2, 16, 2>(a, grid_x, st);
-  if (s.nsub == 2 && s.waves == 16 && s.steps == 1) return launch_plain_t<2, 16, 1>(a, grid_x, st);
-  if (s.nsub == 2 && s.waves == 4 && s.steps == 1) return launch_plain_t<2, 4, 1>(a, grid_x, st);
-  if (s.nsub == 1 && s.waves == 16 && s.steps == 2) return launch_plain_t<1, 16, 2>(a, grid_x, st);
-  if (s.nsub == 1 && s.waves == 16 && s.steps == 1) return launch_plain_t<1, 16, 1>(a, grid_x, st);
-  if (s.nsub == 1 && s.waves == 4 && s.steps == 1) return launch_plain_t<1, 4, 1>(a, grid_x, st);
-  return (int)hipErrorInvalidConfiguration;
-}
-
 template <int STEPS, int NBX>
 static int launch_residual_t(const Lut8Args &a, int grid_x, hipStream_t st) {
   (void)hipGetLastError();  // report only this launch's error

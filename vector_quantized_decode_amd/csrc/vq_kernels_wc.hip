@@ -217,6 +217,113 @@ __global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
 }
 
 // --------------------------------------------------------------------------
+// d = 4, n = 8, one token
+// --------------------------------------------------------------------------
+// Same walk as wc12_kernel over the 8-bit tile layout of vq_kernels.hip
+// (chunk (jt, rg): lane l = subvector 64 jt + l, byte i = row 16 rg + i).
+// The codebook (256 x 4 fp16, 2 KiB) is small enough to keep 32 copies in
+// LDS: entry c of copy k at byte 256 c + 8 k.  Lane l reads copy l % 32, so
+// the 16 lanes the LDS serves per cycle of an 8-byte read hit 16 different
+// bank pairs whatever their indices, and the address is one byte permute
+// (byte 1 = the index, byte 0 = 8 (l % 32)).  No partial sums leave the
+// workgroup: there is no hand-off, no workspace and no bound.
+template <int K>
+__device__ __forceinline__ uint32_t wc8_addr(uint32_t w, uint32_t base) {
+  return __builtin_amdgcn_perm(w, base, 0x0C0C0000u | ((4u + K) << 8));
+}
+
+__device__ __forceinline__ void wc8_chunk(float (&acc)[16], const u32x4 &w, uint2 xj, const char *wcr,
+                                          uint32_t base) {
+#define WC8_ONE(R, Q, B)                                                   \
+  {                                                                        \
+    const uint2 e = lds_u2(wcr, wc8_addr<B>(w[Q], base));                  \
+    acc[R] = __builtin_amdgcn_fdot2(h2(xj.x), h2(e.x), acc[R], false);     \
+    acc[R] = __builtin_amdgcn_fdot2(h2(xj.y), h2(e.y), acc[R], false);     \
+  }
+  WC8_ONE(0, 0, 0) WC8_ONE(1, 0, 1) WC8_ONE(2, 0, 2) WC8_ONE(3, 0, 3)
+  WC8_ONE(4, 1, 0) WC8_ONE(5, 1, 1) WC8_ONE(6, 1, 2) WC8_ONE(7, 1, 3)
+  WC8_ONE(8, 2, 0) WC8_ONE(9, 2, 1) WC8_ONE(10, 2, 2) WC8_ONE(11, 2, 3)
+  WC8_ONE(12, 3, 0) WC8_ONE(13, 3, 1) WC8_ONE(14, 3, 2) WC8_ONE(15, 3, 3)
+#undef WC8_ONE
+}
+
+template <int W, int PF>
+__global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
+  constexpr int NT = W * 64;
+  constexpr int RP = 4096 / NT;               // 16-byte replica stores per thread
+  __shared__ __align__(16) char wcr[256 * 256];
+  __shared__ float part[W * 64];
+  const WcMat &M = args.mat[blockIdx.y];
+  if ((int)blockIdx.x >= M.nwg) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = M.jsplit;
+  const int rgl = wave / S, sg = wave % S;
+  const int JT = M.J >> 6;
+  const int NG = (M.N + 15) >> 4;
+  const int rgw = (int)blockIdx.x * (W / S) + rgl;
+  const int rg = min(rgw, NG - 1);
+  const int seg = (JT + S - 1) / S;
+  const int kbeg = min(sg * seg, JT), kend = min(kbeg + seg, JT);
+
+  // 1. codebook entries for the replicas, then the first PF index chunks and
+  //    x slices: every load is issued before the first wait
+  uint2 ent[RP];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 4];
+  const uint8_t *wi = M.wi + (size_t)lane * 16;
+  const size_t kstride = (size_t)NG * 1024;   // one 64-subvector tile of all row groups
+  const uint8_t *wrg = wi + (size_t)rg * 1024;
+  const uint2 *xg = reinterpret_cast<const uint2 *>(M.x) + lane;   // x_j, j = 64 k + lane
+  u32x4 buf[PF];
+  uint2 xbuf[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const int k = min(kbeg + p, JT - 1);
+    buf[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrg + (size_t)k * kstride));
+    xbuf[p] = xg[k * 64];
+  }
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int s = threadIdx.x + u * NT;       // entry s >> 4, copies 2 (s & 15) and + 1
+    *reinterpret_cast<u32x4 *>(wcr + (s >> 4) * 256 + (s & 15) * 16) =
+        u32x4{ent[u].x, ent[u].y, ent[u].x, ent[u].y};
+  }
+  __syncthreads();
+
+  // 2. lookups: OC[j][c] = x_j . WC[c] formed per index, summed per row
+  const uint32_t base = (uint32_t)(lane & 31) << 3;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int k0 = kbeg; k0 < kend; k0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int k = k0 + p;
+      const u32x4 cur = buf[p];
+      const uint2 xj = xbuf[p];
+      // refill this slot with chunk k + PF (clamped: in bounds, unused)
+      const int kn = min(k + PF, JT - 1);
+      buf[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrg + (size_t)kn * kstride));
+      xbuf[p] = xg[kn * 64];
+      if (k < kend) wc8_chunk(acc, cur, xj, wcr, base);
+    }
+  }
+
+  // 3. rows out: lane 4r holds row r of the 16 (segments added in order)
+  float v = wreduce_rows16(acc, lane);
+  if (S > 1) {
+    part[wave * 64 + lane] = v;
+    __syncthreads();
+    if (sg != 0) return;
+    v = part[wave * 64 + lane];
+    for (int t = 1; t < S; ++t) v += part[(wave + t) * 64 + lane];
+  }
+  const int row = rgw * 16 + ((lane >> 2) & 15);
+  if ((lane & 3) == 0 && rgw < NG && row < M.N) M.y[row] = v;
+}
+
+// --------------------------------------------------------------------------
 // d = 8, n = 16, up to 16 tokens
 // --------------------------------------------------------------------------
 // Wave = 16 rows x all tokens x all J subvectors.  Index chunk (row group rg,
@@ -369,6 +476,23 @@ int wc12_jsplit(int J) {
   const int JT = J / 64;
   return JT <= 24 ? 1 : (JT <= 48 ? 2 : 4);
 }
+// Waves of the 8-bit kernel: 8 per workgroup with two index chunks in flight
+// each for layers of more than 2^20 indices, 4 with one in flight below.
+// Fewer loads in flight let the codebook reach LDS early; on small layers
+// more, smaller workgroups start sooner.
+int wc8_waves(int64_t indices) { return indices > ((int64_t)1 << 20) ? 8 : 4; }
+int wc8_rows_per_wg(int jsplit, int waves) { return waves / jsplit * 16; }
+// Waves per row group along J: the smallest power of two (at most 4 and the
+// row's 64-subvector tiles) that gives the matrix 64 workgroups of 8 waves.
+// It depends on the matrix alone, so a matrix sums in the same order alone
+// or in a group, with either wave count.
+int wc8_jsplit(int N, int J) {
+  const int64_t ng = (N + 15) / 16;
+  const int jt = J / 64;
+  int s = 1;
+  while (2 * s <= 4 && 2 * s <= jt && (ng * s + 7) / 8 < 64) s *= 2;
+  return s;
+}
 int wc16_rows_per_wg(int jsplit) { return WC16_W / jsplit * 16; }
 int wc16_jsplit(int J) {
   const int JB = J / 32;
@@ -380,6 +504,15 @@ int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL((wc12_kernel<WC12_W, WC12_PF>), dim3(grid_x, a.count), dim3(WC12_W * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+int launch_wc8(const WcArgs &a, int grid_x, int waves, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // report only this launch's error
+  if (waves == 8) hipLaunchKernelGGL((wc8_kernel<8, 2>), dim3(grid_x, a.count), dim3(8 * 64), 0, st, a);
+  else if (waves == 4) hipLaunchKernelGGL((wc8_kernel<4, 1>), dim3(grid_x, a.count), dim3(4 * 64), 0, st, a);
+  else return (int)hipErrorInvalidConfiguration;
   return (int)hipGetLastError();
 }
 

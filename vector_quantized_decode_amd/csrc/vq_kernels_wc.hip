@@ -221,12 +221,13 @@ __global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
 // --------------------------------------------------------------------------
 // Same walk as wc12_kernel over the 8-bit tile layout of vq_kernels.hip
 // (chunk (jt, rg): lane l = subvector 64 jt + l, byte i = row 16 rg + i).
-// The codebook (256 x 4 fp16, 2 KiB) is small enough to keep 32 copies in
-// LDS: entry c of copy k at byte 256 c + 8 k.  Lane l reads copy l % 32, so
+// The codebook (256 x 4 fp16, 2 KiB) is small enough to keep 16 copies in
+// LDS: entry c of copy k at byte 256 c + 8 k.  Lane l reads copy l % 16, so
 // the 16 lanes the LDS serves per cycle of an 8-byte read hit 16 different
-// bank pairs whatever their indices, and the address is one byte permute
-// (byte 1 = the index, byte 0 = 8 (l % 32)).  No partial sums leave the
-// workgroup: there is no hand-off, no workspace and no bound.
+// bank pairs whatever their indices (measured: no slower than 32 copies),
+// and the address is one byte permute (byte 1 = the index, byte 0 =
+// 8 (l % 16)).  No partial sums leave the workgroup: there is no hand-off,
+// no workspace and no bound.
 template <int K>
 __device__ __forceinline__ uint32_t wc8_addr(uint32_t w, uint32_t base) {
   return __builtin_amdgcn_perm(w, base, 0x0C0C0000u | ((4u + K) << 8));
@@ -250,7 +251,7 @@ __device__ __forceinline__ void wc8_chunk(float (&acc)[16], const u32x4 &w, uint
 template <int W, int PF>
 __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   constexpr int NT = W * 64;
-  constexpr int RP = 4096 / NT;               // 16-byte replica stores per thread
+  constexpr int RP = 2048 / NT;               // 16-byte replica stores per thread
   __shared__ __align__(16) char wcr[256 * 256];
   __shared__ float part[W * 64];
   const WcMat &M = args.mat[blockIdx.y];
@@ -270,7 +271,7 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   //    x slices: every load is issued before the first wait
   uint2 ent[RP];
 #pragma unroll
-  for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 4];
+  for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
   const uint8_t *wi = M.wi + (size_t)lane * 16;
   const size_t kstride = (size_t)NG * 1024;   // one 64-subvector tile of all row groups
   const uint8_t *wrg = wi + (size_t)rg * 1024;
@@ -285,14 +286,14 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   }
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
-    const int s = threadIdx.x + u * NT;       // entry s >> 4, copies 2 (s & 15) and + 1
-    *reinterpret_cast<u32x4 *>(wcr + (s >> 4) * 256 + (s & 15) * 16) =
+    const int s = threadIdx.x + u * NT;       // entry s >> 3, copies 2 (s & 7) and + 1
+    *reinterpret_cast<u32x4 *>(wcr + (s >> 3) * 256 + (s & 7) * 16) =
         u32x4{ent[u].x, ent[u].y, ent[u].x, ent[u].y};
   }
   __syncthreads();
 
   // 2. lookups: OC[j][c] = x_j . WC[c] formed per index, summed per row
-  const uint32_t base = (uint32_t)(lane & 31) << 3;
+  const uint32_t base = (uint32_t)(lane & 15) << 3;
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;

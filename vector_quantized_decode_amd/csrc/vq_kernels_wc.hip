@@ -469,13 +469,16 @@ static int wgrid(int64_t work, int block) {
 }
 
 constexpr int WC12_W = 4;
-constexpr int WC12_PF = 8;
+constexpr int WC12_PF = 2;
 constexpr int WC16_W = 8;
 
 int wc12_rows_per_wg(int jsplit) { return WC12_W / jsplit * 16; }
+// Waves per row group along J for the 12-bit kernel.  Two chunks in flight
+// per wave and short segments measured fastest: with fewer loads queued the
+// codebook and each wave's first chunks come back sooner.
 int wc12_jsplit(int J) {
   const int JT = J / 64;
-  return JT <= 24 ? 1 : (JT <= 48 ? 2 : 4);
+  return JT <= 12 ? 1 : (JT <= 24 ? 2 : 4);
 }
 // Waves of the 8-bit kernel: 8 per workgroup with two index chunks in flight
 // each for layers of more than 2^20 indices, 4 with one in flight below.

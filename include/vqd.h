@@ -64,17 +64,24 @@ typedef enum { VQ_F16 = 0, VQ_F32 = 1 } vq_dtype;
 /*
  * One quantized matrix.  A host struct, read only during the call.
  *   K, N      input and output features.
- *   d, nbits  supported pairs: (4, 8).  K must be a multiple of 64*d.
+ *   d, nbits  supported pairs: (4, 8), (4, 12) and (8, 16); K must be a
+ *             multiple of 256.  All matrices of one call share (d, nbits).
  *   wi        packed indices in the DEVICE layout made by vq_repack_wi
  *             (16-byte aligned).
  *   wc        fp16 codebook [2^nbits][d] (16-byte aligned).
- *   Residual fields (vq_gemv_residual only; ignored by vq_gemv):
- *   signs     sign bits in the DEVICE layout made by vq_repack_signs.
- *   alpha     fp16 scales in the DEVICE layout made by vq_repack_alpha.
+ *   Residual fields (vq_gemv_residual only, (d, nbits) = (4, 8); ignored
+ *   by vq_gemv):
+ *   signs     sign bits in the DEVICE layout made by vq_repack_signs
+ *             (16-byte aligned).
+ *   alpha     fp16 scales in the DEVICE layout made by vq_repack_alpha,
+ *             header included (32-byte aligned).
  *   group     residual group size along K; must be 128.
- *   rht_sign  int8 [K] of +1/-1 for the randomized Hadamard rotation of x,
- *             or NULL when x is already rotated.
+ *   rht_sign  int8 [K] of +1/-1 for the randomized Hadamard rotation of x
+ *             (4-byte aligned), or NULL when x is already rotated.
  *   had_block Hadamard block size h: a power of two dividing K, <= 16384.
+ *   A residual matrix must stay below 2^31 bytes of device indices
+ *   ((N rounded up to 32) * K/4 < 2^31): its kernel addresses them with
+ *   32-bit buffer offsets.
  */
 typedef struct {
   int32_t K, N, d, nbits;
@@ -99,39 +106,59 @@ const char *vq_last_error(void);
 
 /*
  * Bytes of the device layouts.  Zero means the shape is unsupported.
+ * Rows are padded with zero indices to NG = ceil(N/16) groups of 16.
  *
- * WI device layout for nbits = 8 ("tile-16x64"): rows are padded with zero
- * indices to NG = ceil(N/16) groups of 16; index (r, j) of the canonical
- * matrix sits at byte ((j/64 * NG + r/16) * 64 + j%64) * 16 + r%16.  One
- * 1 KiB chunk holds 16 rows x 64 subvectors; lane l of a wavefront reads the
- * 16 bytes of subvector l, so a lane always works on one subvector and one
- * output-codebook column [EVA 2.A conflict-free lookup].
+ * WI device layout for (4, 8) ("tile-16x64", K/4 % 64 == 0): index (r, j)
+ * of the canonical matrix sits at byte
+ * ((j/64 * NG + r/16) * 64 + j%64) * 16 + r%16.  One 1 KiB chunk holds 16
+ * rows x 64 subvectors; lane l of a wavefront reads the 16 bytes of
+ * subvector l, so a lane always works on one subvector: one x slice and,
+ * with an output-codebook tile, one OC column [EVA 2.A conflict-free
+ * lookup].
+ *
+ * (4, 12) ("tile-16x64-12", K/4 % 64 == 0): chunk (row group rg, subvector
+ * tile jt), ordered row group first, is 1536 bytes; lane l's 24 bytes hold
+ * the indices of rows 16 rg + i at subvector 64 jt + l, index i in bits
+ * [12 i, 12 i + 12) of a little-endian 192-bit word.
+ *
+ * (8, 16) ("tile-16x32-16", K/8 % 32 == 0): chunk (rg, subvector block jb
+ * of 32), ordered row group first, is 1 KiB; lane l holds 8 little-endian
+ * uint16, the q-th the index of row 16 rg + l%16 at subvector
+ * 32 jb + l/16 + 4 q.
  */
 size_t vq_wi_device_bytes(int32_t N, int32_t K, int32_t d, int32_t nbits);
 
 /*
- * Sign-bit device layout ("tile-32x32"): P = K/8 sign bytes per row,
- * NP = ceil(N/32) groups of 32 rows.  Sign byte p of row r (bits of weights
- * 8p .. 8p+7, canonical [N][K/8], bit k%8 = weight k, 1 means +1) sits at
- * byte ((p/32 * NP + r/32) * 64 + ((r%32)/16) * 32 + p%32) * 16 + r%16.
+ * Sign-bit device layout ("tile-32x32-skew"): NP = ceil(N/32) pairs of 16
+ * row groups.  Canonical sign byte p of row r holds the bits of weights
+ * 8p .. 8p+7 (canonical [N][K/8], bit k%8 = weight k, 1 means +1).  Chunk
+ * (tile pt = p/32, pair rp = r/32) is 1 KiB, ordered tile first; within it
+ * lane L = 2 (r%32) + g (g = (p%32)/16, the 128-weight group of the tile)
+ * holds 16 bytes, byte j being sign byte 32 pt + 16 g + (j ^ (r%16)) of row
+ * r.  Padding rows are zero.
  */
 size_t vq_signs_device_bytes(int32_t N, int32_t K);
 
 /*
  * Alpha device layout: fp16 scale (r, g) of the canonical [N][K/128] sits at
- * element ((g/2 * NP + r/32) * 4 + ((r%32)/16) * 2 + g%2) * 16 + r%16,
- * NP = ceil(N/32); padding is zero.
+ * element ((g/2 * NP + r/32) * 64 + 2 * (r%32) + g%2), NP = ceil(N/32),
+ * padding zero -- one scale per lane of the matching sign chunk.  After the
+ * scales a 256-byte header follows; its first 32-bit word is the largest
+ * |alpha| as fp16 magnitude bits (written by vq_repack_alpha).  The returned
+ * size includes the header.
  */
 size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group);
 
 /*
  * Workspace bytes needed by vq_gemv (residual = 0) or vq_gemv_residual
- * (residual = 1) for these matrices and B tokens: split-K partial sums,
- * completion counters and, for the residual call, the rotated inputs.
- * Returns 0 on invalid arguments.  The workspace must be set up once with
- * vq_workspace_init before its first use; every call that completes leaves
- * it ready for the next one.  Calls sharing one workspace must be ordered
- * (same stream or explicit dependencies).
+ * (residual = 1) for these matrices and B tokens.  vq_gemv takes none
+ * (0); the residual call needs its split-K accumulators, completion
+ * counters, float partials for non-finite inputs and the rotated inputs of
+ * Hadamard blocks above 2048.  Returns 0 on invalid arguments too.  The
+ * workspace must be set up once with vq_workspace_init before its first
+ * use; every call that completes leaves it ready for the next one.  Calls
+ * sharing one workspace must be ordered (same stream or explicit
+ * dependencies).
  */
 size_t vq_workspace_bytes(const vq_matrix *m, int32_t count, int32_t B,
                           int32_t residual);
@@ -167,8 +194,8 @@ int vq_repack_wi(const uint8_t *canonical, int32_t N, int32_t K, int32_t d,
 int vq_repack_signs(const uint8_t *canonical, int32_t N, int32_t K,
                     void *device_layout, void *stream);
 
-/* Canonical fp16 alpha [N][K/group] -> alpha device layout (group == 128,
- * K % 256 == 0). */
+/* Canonical fp16 alpha [N][K/group] -> alpha device layout and header
+ * (group == 128, K % 256 == 0). */
 int vq_repack_alpha(const uint16_t *canonical, int32_t N, int32_t K,
                     int32_t group, void *device_layout, void *stream);
 
@@ -195,16 +222,19 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K,
 
 /*
  * VQ GEMV [EVA 2.A, 2.B]: for each of `count` matrices m,
- * y[m][b][r] = sum_j OC_m[b*K/d + j][WI_m[r][j]], OC built from x[m].
+ * y[m][b][r] = sum_j OC_m[b*K/d + j][WI_m[r][j]], OC of x[m].  Each OC
+ * entry x_j . WC[c] is formed when an index asks for it, from a codebook
+ * held on chip; a workgroup covers whole rows.
  *   m        host array of `count` matrix descriptors.
  *   x        host array of `count` device pointers, fp16 [B][K_m] each
  *            (16-byte aligned).
  *   y        host array of `count` device pointers, fp32 [B][N_m] each
  *            (4-byte aligned), overwritten.
- *   workspace / ws_bytes  at least vq_workspace_bytes(m, count, B, 0)
- *            bytes, 256-byte aligned, set up by vq_workspace_init.
- * All matrices are served by one kernel launch.  Supported: B == 1,
- * (d, nbits) == (4, 8), 1 <= count <= VQ_MAX_GROUP.
+ *   workspace / ws_bytes  unused (vq_workspace_bytes gives 0); any value.
+ * All matrices are served by one kernel launch.  Supported:
+ * (d, nbits) = (4, 8) or (4, 12) with B == 1, (8, 16) with 1 <= B <= 16;
+ * 1 <= count <= VQ_MAX_GROUP.  A matrix sums in the same order alone or in
+ * a group.
  */
 int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x,
             int32_t B, float *const *y, void *workspace, size_t ws_bytes,
@@ -215,8 +245,12 @@ int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x,
  * x_rot = rotation of x[m] (or x[m] itself when rht_sign is NULL),
  * y[m][b][r] = sum_j OC(x_rot)[b*K/d + j][WI[r][j]]
  *            + sum_g alpha[r][g] * sum_{k in g} s[r][k] * x_rot[b][k].
- * Same arguments and support as vq_gemv plus the residual fields of each
- * vq_matrix; workspace from vq_workspace_bytes(m, count, B, 1).
+ * Each workgroup builds an output-codebook tile of 64 subvectors in LDS
+ * [EVA 2.A] and workgroups sharing rows meet in one fixed-point atomic per
+ * row.  Arguments as vq_gemv plus the residual fields of each vq_matrix;
+ * workspace / ws_bytes at least vq_workspace_bytes(m, count, B, 1) bytes,
+ * 256-byte aligned, set up by vq_workspace_init (VQ_EWORKSPACE or
+ * VQ_EALIGN otherwise).  Supported: (d, nbits) = (4, 8), B == 1.
  */
 int vq_gemv_residual(const vq_matrix *m, int32_t count,
                      const uint16_t *const *x, int32_t B, float *const *y,

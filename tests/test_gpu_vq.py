@@ -367,6 +367,43 @@ def test_gemv_nonfinite_input_propagates_like_oracle(bad):
     _assert_close(y2, _oracle_plain(mi2), "after non-finite call")
 
 
+def test_gemv_residual_zero_input_gives_exact_zero():
+    # K = 3584 splits each row over 14 workgroups (fixed-point hand-off)
+    _say("gemv_residual x = 0")
+    mi = synth.small_matrix(3584, 300, 4, 8, seed=78, residual=True)
+    mi.x = np.zeros_like(mi.x)
+    (y,), _ = _run_gemv([_upload(mi, residual=True)], [mi.x], residual=True)
+    assert np.array_equal(y, np.zeros_like(y))
+
+
+@pytest.mark.parametrize("bad", ["inf", "nan"])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_gemv_residual_nonfinite_input_propagates_like_oracle(bad, rotate):
+    # a non-finite input makes the hand-off bound non-finite: float partials
+    # and the last-workgroup sum instead; every output's class (NaN, +inf,
+    # -inf, finite) matches the oracle, and the workspace is left ready
+    _say(f"gemv_residual non-finite input: {bad}, rotate={rotate}")
+    mi = synth.small_matrix(3584, 200, 4, 8, seed=79, residual=True)
+    x = mi.x.copy()
+    x[0, 1234] = np.float16(np.inf if bad == "inf" else np.nan)
+    mi.x = x
+    m = _upload(mi, residual=True)
+    if not rotate:
+        m.rht_sign = None
+    (y,), _ = _run_gemv([m], [mi.x], residual=True)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = _oracle_res(mi, rotate=rotate)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(y), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    if fin.any():
+        _assert_close(y[fin], ref[fin], "finite rows")
+    mi2 = synth.small_matrix(3584, 200, 4, 8, seed=80, residual=True)
+    (y2,), _ = _run_gemv([_upload(mi2, residual=True)], [mi2.x], residual=True)
+    _assert_close(y2, _oracle_res(mi2), "after non-finite call")
+
+
 def test_gemv_residual_large_magnitudes():
     _say("gemv_residual with large x and alpha")
     mi = synth.small_matrix(3584, 200, 4, 8, seed=77, residual=True)

@@ -443,7 +443,8 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     for (int t = 0; t < 4; ++t) {
       const _Float16 hi = (_Float16)xr[t];
       xh[t] = hi;
-      xl[t] = (_Float16)(xr[t] - (float)hi);
+      // the low part of an infinite input is zero, not inf - inf
+      xl[t] = __builtin_isfinite(xr[t]) ? (_Float16)(xr[t] - (float)hi) : (_Float16)0.f;
     }
     f32x32_t o = {};
     o = __builtin_amdgcn_mfma_f32_32x32x4f16(wa, xh, o, 0, 0, 0);
@@ -465,20 +466,19 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     const float4 h4 = *reinterpret_cast<const float4 *>(xrs + 8 * pl + 4);
     const float lo4[4] = {l4.x, l4.y, l4.z, l4.w};
     const float hi4[4] = {h4.x, h4.y, h4.z, h4.w};
-    const float S = ((lo4[0] + lo4[1]) + (lo4[2] + lo4[3])) + ((hi4[0] + hi4[1]) + (hi4[2] + hi4[3]));
-    float L[16];
-    L[0] = 0.f;
-#pragma unroll
-    for (int lo = 1; lo < 16; ++lo) L[lo] = L[lo & (lo - 1)] + lo4[__builtin_ctz(lo)];
+    // T = sum_i (+-1) x_i formed from signed pairs, never as 2 (sum of the
+    // set inputs) - (sum of all): no cancellation, so an infinite input
+    // gives an infinite entry as the sum itself does
+    const float pa[4] = {-(lo4[0] + lo4[1]), lo4[0] - lo4[1], lo4[1] - lo4[0], lo4[0] + lo4[1]};
+    const float pb[4] = {-(lo4[2] + lo4[3]), lo4[2] - lo4[3], lo4[3] - lo4[2], lo4[2] + lo4[3]};
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int hi = 2 * (wave - 8) + e;
-      const float H = ((hi & 1) ? hi4[0] : 0.f) + ((hi & 2) ? hi4[1] : 0.f) +
-                      ((hi & 4) ? hi4[2] : 0.f) + ((hi & 8) ? hi4[3] : 0.f);
-      const float c0 = 2.f * H - S;
+      const float H = (((hi & 1) ? hi4[0] : -hi4[0]) + ((hi & 2) ? hi4[1] : -hi4[1])) +
+                      (((hi & 4) ? hi4[2] : -hi4[2]) + ((hi & 8) ? hi4[3] : -hi4[3]));
       float *dst = lds + (hi * 16) * 64 + lane;
 #pragma unroll
-      for (int lo = 0; lo < 16; ++lo) dst[lo * 64] = __builtin_fmaf(2.f, L[lo], c0);
+      for (int lo = 0; lo < 16; ++lo) dst[lo * 64] = (pa[lo & 3] + pb[lo >> 2]) + H;
     }
   }
   // 6. per-wave parts of the bound sum_k |x_rot_k| <= sqrt(K) ||x||_2

@@ -358,10 +358,11 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
 
   // 2. index, sign and alpha loads: per 32-row step, two index chunks, one
   //    sign chunk and the scale of the lane's (row, group).  Only the first
-  //    step is loaded here; step g + 1 is issued when step g's lookups start.
-  //    With one step in flight per wave the memory queues stay short, so the
-  //    rotation inputs and each step's data come back in issue order instead
-  //    of behind every workgroup's whole stream.
+  //    step is loaded here, the second after the OC tile is built, and step
+  //    g + 2 when step g's lookups start.  With few steps in flight per wave
+  //    the memory queues stay short, so the rotation inputs and each step's
+  //    data come back in issue order instead of behind every workgroup's
+  //    whole stream.
   u32x4 va[STEPS], vb[STEPS], vs[STEPS];
   uint16_t al[STEPS];
   //    Loads go through buffer descriptors: a step past the workgroup's run
@@ -481,6 +482,9 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
       for (int lo = 0; lo < 16; ++lo) dst[lo * 64] = (pa[lo & 3] + pb[lo >> 2]) + H;
     }
   }
+  // the second row step goes out once the tables are written (the OC inputs
+  // are in by then); from here on two steps are in flight per wave
+  if (STEPS > 1) load_step(1);
   // 6. per-wave parts of the bound sum_k |x_rot_k| <= sqrt(K) ||x||_2
   {
     float s2 = 0.f;
@@ -533,7 +537,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   uint64_t term[STEPS], old[STEPS];
 #pragma unroll
   for (int g = 0; g < STEPS; ++g) {
-    if (g + 1 < STEPS) load_step(g + 1);
+    if (g + 2 < STEPS) load_step(g + 2);
     rowval[g] = 0.f;
     old[g] = 0ull;
     term[g] = 0ull;

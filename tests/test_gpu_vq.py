@@ -226,7 +226,7 @@ def test_gemv_workload1_single_matrix():
 
 
 @pytest.mark.parametrize("K,N", [(256, 1), (256, 17), (512, 100), (768, 333), (1024, 4103),
-                                 (2048, 48), (4096, 513)])
+                                 (2048, 48), (4096, 513), (8192, 77), (8448, 50)])
 def test_gemv_shapes_with_ragged_rows(K, N):
     _say(f"gemv K={K} N={N}")
     mi = synth.small_matrix(K, N, 4, 8, seed=K + N)
@@ -247,6 +247,20 @@ def test_gemv_workload2_grouped_and_deterministic():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     (y1,), _ = _run_gemv([mats[2]], [mis[2].x])
     assert np.array_equal(y1.view(np.uint32), ys[2].view(np.uint32))
+
+
+def test_gemv_long_rows_share_the_short_row_sums():
+    # rows of more than 32 chunks of 64 subvectors are streamed; a short-row
+    # matrix grouped with them is streamed too and must give bitwise the
+    # result it gets alone (where all of its chunks are requested at once)
+    _say("gemv long and short rows in one launch")
+    mis = [synth.small_matrix(12288, 100, 4, 8, seed=21), synth.small_matrix(4096, 700, 4, 8, seed=22)]
+    mats = [_upload(mi) for mi in mis]
+    ys, _ = _run_gemv(mats, [mi.x for mi in mis])
+    for i, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _oracle_plain(mi), f"long/short {i}")
+    (y1,), _ = _run_gemv([mats[1]], [mis[1].x])
+    assert np.array_equal(y1.view(np.uint32), ys[1].view(np.uint32))
 
 
 def test_gemv_mixed_group():

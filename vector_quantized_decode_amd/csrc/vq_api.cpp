@@ -198,12 +198,12 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
   args.count = count;
   int64_t max_wg = 0;
   int max_j = 0;
+  bool burst = true;   // 8-bit: every row short enough for the burst kernel
+  int64_t indices = 0;
+  int max_split = 1;
   // Workgroups are dispatched in grid order, matrix by matrix; the matrices
   // with the longest rows (most work per wave) go first so they do not start
   // last and set the tail.  Results do not depend on the order.
-  int64_t indices = 0;
-  for (int i = 0; i < count; ++i) indices += (int64_t)m[i].N * (m[i].K / m[i].d);
-  const int w8 = wc8_waves(indices);
   int order[VQ_MAX_GROUP];
   for (int i = 0; i < count; ++i) order[i] = i;
   for (int a = 1; a < count; ++a)
@@ -226,15 +226,24 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     d.jsplit = (f == FMT_LUT8)   ? wc8_jsplit(m[i].N, d.J)
                : (f == FMT_WC12) ? wc12_jsplit(d.J)
                                  : wc16_jsplit(d.J);
+    if (f == FMT_LUT8) {
+      if (!wc8_burst_fits(d.N, d.J, d.jsplit)) burst = false;
+      indices += (int64_t)d.N * d.J;
+      if (d.jsplit > max_split) max_split = d.jsplit;
+    }
+    if (d.J > max_j) max_j = d.J;
+  }
+  const int w8 = (f == FMT_LUT8) ? wc8_waves(indices, max_split) : 0;
+  for (int s = 0; s < count; ++s) {
+    WcMat &d = args.mat[s];
     const int R = (f == FMT_LUT8)   ? wc8_rows_per_wg(d.jsplit, w8)
                   : (f == FMT_WC12) ? wc12_rows_per_wg(d.jsplit)
                                     : wc16_rows_per_wg(d.jsplit);
-    d.nwg = (m[i].N + R - 1) / R;
+    d.nwg = (d.N + R - 1) / R;
     if (d.nwg > max_wg) max_wg = d.nwg;
-    if (d.J > max_j) max_j = d.J;
   }
   if (max_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
-  const int err = (f == FMT_LUT8)   ? launch_wc8(args, (int)max_wg, w8, stream)
+  const int err = (f == FMT_LUT8)   ? launch_wc8(args, (int)max_wg, w8, burst, stream)
                   : (f == FMT_WC12) ? launch_wc12(args, (int)max_wg, max_j, stream)
                                     : launch_wc16(args, (int)max_wg, stream);
   return hip_status(err);

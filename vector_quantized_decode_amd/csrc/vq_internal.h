@@ -64,10 +64,11 @@ struct WcArgs {
 
 int wc12_rows_per_wg(int jsplit);
 int wc12_jsplit(int J);
-int wc8_waves(int64_t indices);
+int wc8_waves(int64_t indices, int max_split);
 int wc8_rows_per_wg(int jsplit, int waves);
 int wc8_jsplit(int N, int J);
-int launch_wc8(const WcArgs &a, int grid_x, int waves, void *stream);
+bool wc8_burst_fits(int N, int J, int jsplit);
+int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, void *stream);
 int wc16_rows_per_wg(int jsplit);
 int wc16_jsplit(int J);
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);

@@ -83,6 +83,28 @@ __device__ __forceinline__ float wreduce_rows16(float (&a)[16], int lane) {
   return v;
 }
 
+// The descriptor of this workgroup's matrix.  Every field is read from the
+// kernel arguments before the first one is used, so the scalar loads share
+// one round trip instead of one per dependent use (the early exit, then the
+// split, then the pointers), which the first vector loads would wait for.
+__device__ __forceinline__ WcMat load_wcmat(const WcArgs &args) {
+  const WcMat &R = args.mat[blockIdx.y];
+  WcMat M;
+  M.wi = R.wi;
+  M.wc = R.wc;
+  M.x = R.x;
+  M.y = R.y;
+  M.J = R.J;
+  M.N = R.N;
+  M.B = R.B;
+  M.ldy = R.ldy;
+  M.nwg = R.nwg;
+  M.jsplit = R.jsplit;
+  __asm__ volatile("" ::"s"(M.wi), "s"(M.wc), "s"(M.x), "s"(M.y), "s"(M.J), "s"(M.N), "s"(M.B),
+                   "s"(M.ldy), "s"(M.nwg), "s"(M.jsplit));
+  return M;
+}
+
 // --------------------------------------------------------------------------
 // d = 4, n = 12, one token
 // --------------------------------------------------------------------------
@@ -145,7 +167,7 @@ __global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
   constexpr int WCP = 2048 / NT;              // 16-byte codebook pieces per thread
   __shared__ __align__(16) char wc[4096 * 8];
   __shared__ float part[W * 64];
-  const WcMat &M = args.mat[blockIdx.y];
+  const WcMat M = load_wcmat(args);
   if ((int)blockIdx.x >= M.nwg) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -254,7 +276,7 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   constexpr int RP = 2048 / NT;               // 16-byte replica stores per thread
   __shared__ __align__(16) char wcr[256 * 256];
   __shared__ float part[W * 64];
-  const WcMat &M = args.mat[blockIdx.y];
+  const WcMat M = load_wcmat(args);
   if ((int)blockIdx.x >= M.nwg) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -324,6 +346,101 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   if ((lane & 3) == 0 && rgw < NG && row < M.N) M.y[row] = v;
 }
 
+// Raw buffer descriptors (gfx9 word 3), an offset past any buffer the
+// kernels address, and the nontemporal cache-policy bit.
+constexpr uint32_t kWcOutOfRange = 0x80000000u;
+constexpr int kWcBufferWord3 = 0x00020000;
+constexpr int kWcNontemporal = 2;
+
+// The same walk for rows of at most 4 S chunks (K <= 8192 at S = 8): a wave's
+// whole segment is requested at once, in two parts.  The codebook, the x
+// slices and the first two chunks go out first; the other chunks only once
+// the codebook has arrived and been written to LDS.  Issued together with
+// the codebook, the whole layer's index stream held the codebook back
+// behind it; issued one chunk per lookup pass, too little was in flight
+// while the codebook was on its way.  Chunks past the segment load through
+// a buffer descriptor with an out-of-range offset (zeros, no memory access)
+// and are not looked up.  Sums are formed in the same order as wc8_kernel,
+// so the two kernels give bitwise the same y for the same split.
+template <int W, int NCH, int PF0>
+__global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
+  constexpr int NT = W * 64;
+  constexpr int RP = 2048 / NT;               // 16-byte replica stores per thread
+  __shared__ __align__(16) char wcr[256 * 256];
+  __shared__ float part[W * 64];
+  const WcMat M = load_wcmat(args);
+  if ((int)blockIdx.x >= M.nwg) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lS = 31 - __builtin_clz((unsigned)M.jsplit);   // the split is a power of two
+  const int S = 1 << lS;
+  const int rgl = wave >> lS, sg = wave & (S - 1);
+  const int JT = M.J >> 6;
+  const int NG = (M.N + 15) >> 4;
+  const int rgw = (int)blockIdx.x * (W >> lS) + rgl;
+  const int rg = min(rgw, NG - 1);
+  const int seg = (JT + S - 1) >> lS;
+  const int kbeg = min(sg * seg, JT), kend = min(kbeg + seg, JT);
+  const uint32_t kstride = (uint32_t)NG * 1024u;   // one 64-subvector tile of all row groups
+  const __amdgpu_buffer_rsrc_t rwi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(M.wi + (size_t)rg * 1024), (short)0, (int)(kstride * (uint32_t)JT),
+      kWcBufferWord3);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(M.x), (short)0, M.J * 8, kWcBufferWord3);
+  auto wi_off = [&](int k) -> uint32_t {
+    return k < kend ? (uint32_t)k * kstride + (uint32_t)lane * 16u : kWcOutOfRange;
+  };
+  auto x_off = [&](int k) -> uint32_t {
+    return k < kend ? (uint32_t)(k * 64 + lane) * 8u : kWcOutOfRange;
+  };
+
+  // 1. codebook entries for the replicas, the x slices, the first PF0 chunks
+  uint2 ent[RP];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
+  u32x4 buf[NCH];
+  uint2 xbuf[NCH];
+#pragma unroll
+  for (int p = 0; p < NCH; ++p)
+    xbuf[p] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, x_off(kbeg + p), 0, 0));
+#pragma unroll
+  for (int p = 0; p < PF0; ++p)
+    buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, wi_off(kbeg + p), 0, kWcNontemporal));
+  // 2. replicas into LDS (waits for the codebook), then the rest of the segment
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int s = threadIdx.x + u * NT;       // entry s >> 3, copies 2 (s & 7) and + 1
+    *reinterpret_cast<u32x4 *>(wcr + (s >> 3) * 256 + (s & 7) * 16) =
+        u32x4{ent[u].x, ent[u].y, ent[u].x, ent[u].y};
+  }
+  __builtin_amdgcn_sched_barrier(0);          // keep the remaining loads after the codebook wait
+#pragma unroll
+  for (int p = PF0; p < NCH; ++p)
+    buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, wi_off(kbeg + p), 0, kWcNontemporal));
+  __syncthreads();
+
+  // 3. lookups in chunk order, each as soon as its indices arrive
+  const uint32_t base = (uint32_t)(lane & 15) << 3;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int p = 0; p < NCH; ++p)
+    if (kbeg + p < kend) wc8_chunk(acc, buf[p], xbuf[p], wcr, base);
+
+  // 4. rows out: lane 4r holds row r of the 16 (segments added in order)
+  float v = wreduce_rows16(acc, lane);
+  if (S > 1) {
+    part[wave * 64 + lane] = v;
+    __syncthreads();
+    if (sg != 0) return;
+    v = part[wave * 64 + lane];
+    for (int t = 1; t < S; ++t) v += part[(wave + t) * 64 + lane];
+  }
+  const int row = rgw * 16 + ((lane >> 2) & 15);
+  if ((lane & 3) == 0 && rgw < NG && row < M.N) M.y[row] = v;
+}
+
 // --------------------------------------------------------------------------
 // d = 8, n = 16, up to 16 tokens
 // --------------------------------------------------------------------------
@@ -337,7 +454,7 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
 template <int W>
 __global__ void __launch_bounds__(W * 64) wc16_kernel(const WcArgs args) {
   __shared__ f32x4_t part[W * 64];
-  const WcMat &M = args.mat[blockIdx.y];
+  const WcMat M = load_wcmat(args);
   if ((int)blockIdx.x >= M.nwg) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -471,6 +588,8 @@ static int wgrid(int64_t work, int block) {
 constexpr int WC12_W = 4;
 constexpr int WC12_PF = 2;
 constexpr int WC16_W = 8;
+constexpr int WC8_W = 8;       // waves per workgroup, 8-bit kernels
+constexpr int WC8_NCH = 4;     // chunks per wave of the burst kernel
 
 int wc12_rows_per_wg(int jsplit) { return WC12_W / jsplit * 16; }
 // Waves per row group along J for the 12-bit kernel.  Two chunks in flight
@@ -480,22 +599,32 @@ int wc12_jsplit(int J) {
   const int JT = J / 64;
   return JT <= 12 ? 1 : (JT <= 24 ? 2 : 4);
 }
-// Waves of the 8-bit kernel: 8 per workgroup with two index chunks in flight
-// each for layers of more than 2^20 indices, 4 with one in flight below.
-// Fewer loads in flight let the codebook reach LDS early; on small layers
-// more, smaller workgroups start sooner.
-int wc8_waves(int64_t indices) { return indices > ((int64_t)1 << 20) ? 8 : 4; }
-int wc8_rows_per_wg(int jsplit, int waves) { return waves / jsplit * 16; }
-// Waves per row group along J: the smallest power of two (at most 4 and the
-// row's 64-subvector tiles) that gives the matrix 64 workgroups of 8 waves.
-// It depends on the matrix alone, so a matrix sums in the same order alone
-// or in a group, with either wave count.
+// Waves per row group along J for the 8-bit kernels: the smallest power of
+// two (at most 8) that leaves each wave at most four 64-subvector chunks,
+// doubled while the matrix has fewer than 64 workgroups of 8 waves and the
+// row has chunks to spare.  It depends on the matrix alone, so a matrix sums
+// in the same order alone or in a group, whichever kernel serves the group.
 int wc8_jsplit(int N, int J) {
   const int64_t ng = (N + 15) / 16;
   const int jt = J / 64;
   int s = 1;
-  while (2 * s <= 4 && 2 * s <= jt && (ng * s + 7) / 8 < 64) s *= 2;
+  while (s < WC8_W && (jt + s - 1) / s > WC8_NCH) s *= 2;
+  while (2 * s <= WC8_W && 2 * s <= jt && (ng * s + WC8_W - 1) / WC8_W < 64) s *= 2;
   return s;
+}
+// Waves per workgroup: 8, or 4 for calls of at most 2^20 indices whose splits
+// allow it (there more, smaller workgroups start sooner; measured 2.7 against
+// 3.1 us for one 512 x 512 matrix).  Only the number of row groups per
+// workgroup changes, not the order of any sum.
+int wc8_waves(int64_t indices, int max_split) {
+  return (indices <= ((int64_t)1 << 20) && max_split <= 4) ? 4 : WC8_W;
+}
+int wc8_rows_per_wg(int jsplit, int waves) { return waves / jsplit * 16; }
+// The burst kernel serves a call when every row fits in its waves' chunks
+// and the matrix's indices lie within one 32-bit buffer offset.
+bool wc8_burst_fits(int N, int J, int jsplit) {
+  const int64_t bytes = (int64_t)((N + 15) / 16) * 1024 * (J / 64);
+  return (J / 64 + jsplit - 1) / jsplit <= WC8_NCH && bytes < ((int64_t)1 << 31);
 }
 int wc16_rows_per_wg(int jsplit) { return WC16_W / jsplit * 16; }
 int wc16_jsplit(int J) {
@@ -511,12 +640,15 @@ int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   return (int)hipGetLastError();
 }
 
-int launch_wc8(const WcArgs &a, int grid_x, int waves, void *stream) {
+int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error
-  if (waves == 8) hipLaunchKernelGGL((wc8_kernel<8, 2>), dim3(grid_x, a.count), dim3(8 * 64), 0, st, a);
-  else if (waves == 4) hipLaunchKernelGGL((wc8_kernel<4, 1>), dim3(grid_x, a.count), dim3(4 * 64), 0, st, a);
-  else return (int)hipErrorInvalidConfiguration;
+  if (waves == 4)
+    hipLaunchKernelGGL((wc8_kernel<4, 1>), dim3(grid_x, a.count), dim3(4 * 64), 0, st, a);
+  else if (burst)
+    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((wc8_kernel<WC8_W, 2>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
   return (int)hipGetLastError();
 }
 

@@ -263,6 +263,37 @@ def test_gemv_long_rows_share_the_short_row_sums():
     assert np.array_equal(y1.view(np.uint32), ys[1].view(np.uint32))
 
 
+def test_gemv_small_call_matches_its_grouped_sums():
+    # alone, a 512 x 512 matrix is a call of few indices (4-wave workgroups);
+    # grouped with a 4096 x 4096 matrix it takes the 8-wave burst kernel: the
+    # same sums in the same order either way
+    _say("gemv small matrix alone and in a group")
+    mis = [synth.matrix_inputs(1, 0), synth.small_matrix(4096, 4096, 4, 8, seed=23)]
+    mats = [_upload(mi) for mi in mis]
+    ys, _ = _run_gemv(mats, [mi.x for mi in mis])
+    for i, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _oracle_plain(mi), f"small/large {i}")
+    (y0,), _ = _run_gemv([mats[0]], [mis[0].x])
+    assert np.array_equal(y0.view(np.uint32), ys[0].view(np.uint32))
+
+
+def test_gemv_largest_group():
+    # VQ_MAX_GROUP matrices of mixed shapes in one launch, each checked against
+    # the oracle and against its own single-matrix call
+    _say("gemv 16 matrices in one launch")
+    shapes = [(256, 7), (512, 300), (768, 64), (1024, 1000), (1280, 33), (2048, 515),
+              (2304, 128), (4096, 256), (3072, 96), (512, 2049), (1536, 17), (256, 4000),
+              (1024, 1), (2560, 200), (8192, 40), (9216, 24)]
+    assert len(shapes) == vq.VQ_MAX_GROUP
+    mis = [synth.small_matrix(K, N, 4, 8, seed=100 + i) for i, (K, N) in enumerate(shapes)]
+    mats = [_upload(mi) for mi in mis]
+    ys, _ = _run_gemv(mats, [mi.x for mi in mis])
+    for i, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _oracle_plain(mi), f"group of 16, matrix {i}")
+        (y1,), _ = _run_gemv([mats[i]], [mi.x])
+        assert np.array_equal(y1.view(np.uint32), y.view(np.uint32)), f"matrix {i}"
+
+
 def test_gemv_mixed_group():
     _say("gemv mixed shapes in one launch")
     mis = [synth.small_matrix(1024, 300, 4, 8, seed=1), synth.small_matrix(512, 2000, 4, 8, seed=2),

@@ -15,8 +15,9 @@ events on the launch stream bracket the timed replays.
 Prints one JSON line:
   value            effective weight-byte throughput (GB/s) of back-to-back
                    layer calls, launch gaps included; us_per_layer beside it
-  roofline         the lookup kernel (one launch per call): algorithmic bytes
-                   per launch over its average launch duration in the timed
+  roofline         the lookup kernel (one launch per call; 16-bit indices add a
+                   pre-pass launch, counted in): algorithmic bytes per call
+                   over the average call period in the timed
                    region; traffic = HBM bytes per launch from the committed
                    rocprofv3 counter summary, when it was taken on the
                    current kernel source (else null)
@@ -219,9 +220,10 @@ def main():
     print(f"# timed {done} steps in {ms:.2f} ms: {us_per_layer:.3f} us/layer, {gbs:.1f} GB/s",
           file=sys.stderr, flush=True)
 
-    # One call is one launch of the lookup kernel, so the timed region's
-    # average launch period is that kernel's average duration back to back
-    # (rocprofv3's kernel trace of the same command reports the same figure).
+    # One call is one launch of the lookup kernel (the 16-bit format adds a
+    # pre-pass launch), so the timed region's average call period is that
+    # kernel's average duration back to back, plus the pre-pass where there
+    # is one (rocprofv3's kernel trace of the same command reports both).
     launch_us = us_per_layer
     kernel_gbs = gbs
 
@@ -299,6 +301,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(launch_us, 4),
+                     "launches_per_call": 2 if wl.nbits == 16 else 1,
                      "algorithmic_bytes_per_launch": layer_bytes,
                      "traffic_source": traffic_src, "kernel_source_sha": kernel_source_sha(args.workload)},
         "cpu_baseline": cpu,

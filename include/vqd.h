@@ -151,8 +151,9 @@ size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group);
 
 /*
  * Workspace bytes needed by vq_gemv (residual = 0) or vq_gemv_residual
- * (residual = 1) for these matrices and B tokens.  vq_gemv takes none
- * (0); the residual call needs its split-K accumulators, completion
+ * (residual = 1) for these matrices and B tokens.  vq_gemv takes none (0)
+ * except for (d, nbits) = (8, 16): 1 MiB + B*K*2 bytes (each rounded up to
+ * 256) per matrix; the residual call needs its split-K accumulators, completion
  * counters, float partials for non-finite inputs and the rotated inputs of
  * Hadamard blocks above 2048.  Returns 0 on invalid arguments too.  The
  * workspace must be set up once with vq_workspace_init before its first
@@ -224,17 +225,23 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K,
  * VQ GEMV [EVA 2.A, 2.B]: for each of `count` matrices m,
  * y[m][b][r] = sum_j OC_m[b*K/d + j][WI_m[r][j]], OC of x[m].  Each OC
  * entry x_j . WC[c] is formed when an index asks for it, from a codebook
- * held on chip; a workgroup covers whole rows.
+ * held on chip (for (8, 16), one dimension of it at a time); a workgroup
+ * covers whole rows.
  *   m        host array of `count` matrix descriptors.
  *   x        host array of `count` device pointers, fp16 [B][K_m] each
  *            (16-byte aligned).
  *   y        host array of `count` device pointers, fp32 [B][N_m] each
  *            (4-byte aligned), overwritten.
- *   workspace / ws_bytes  unused (vq_workspace_bytes gives 0); any value.
- * All matrices are served by one kernel launch.  Supported:
- * (d, nbits) = (4, 8) or (4, 12) with B == 1, (8, 16) with 1 <= B <= 16;
- * 1 <= count <= VQ_MAX_GROUP.  A matrix sums in the same order alone or in
- * a group.
+ *   workspace / ws_bytes  (d, nbits) = (8, 16): at least
+ *            vq_workspace_bytes(m, count, B, 0) bytes, 256-byte aligned
+ *            (VQ_EWORKSPACE / VQ_EALIGN otherwise): per matrix the codebook
+ *            by dimension and x by dimension, rewritten by every call.
+ *            Other formats: unused (vq_workspace_bytes gives 0); any value.
+ * All matrices are served by one kernel launch ((8, 16): a pre-pass that
+ * fills the workspace, then the lookup kernel).  Supported:
+ * (d, nbits) = (4, 8) or (4, 12) with B == 1, (8, 16) with 1 <= B <= 16 and
+ * K <= 65536; 1 <= count <= VQ_MAX_GROUP.  A matrix sums in the same order
+ * alone or in a group.
  */
 int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x,
             int32_t B, float *const *y, void *workspace, size_t ws_bytes,

@@ -88,9 +88,16 @@ def test_gemv_validation_errors():
     assert _gemv([_m(d=8, nbits=16)], ok_x, 17, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # <= 16 tokens
     # one kernel per call: every matrix of a group has the same (d, nbits)
     assert _gemv([_m(), _m(d=4, nbits=12)], ok_x * 2, 1, ok_y * 2, None, 0) == vq.VQ_EUNSUPPORTED
-    # the virtual-codebook formats take no workspace
+    # the 12-bit format takes no workspace; the 16-bit one 1 MiB (the codebook
+    # by dimension) plus B*K*2 bytes (x by dimension) per matrix
     assert vq.vq_workspace_bytes([_m(d=4, nbits=12)], 1) == 0
-    assert vq.vq_workspace_bytes([_m(d=8, nbits=16)], 16) == 0
+    assert vq.vq_workspace_bytes([_m(d=8, nbits=16)], 16) == (1 << 20) + 16 * 1024 * 2
+    assert vq.vq_workspace_bytes([_m(d=8, nbits=16, K=1280)] * 2, 3) == 2 * ((1 << 20) + 7680)
+    need16 = vq.vq_workspace_bytes([_m(d=8, nbits=16)], 4)
+    assert _gemv([_m(d=8, nbits=16)], ok_x, 4, ok_y, None, 0) == vq.VQ_EWORKSPACE
+    assert _gemv([_m(d=8, nbits=16)], ok_x, 4, ok_y, FAKE, need16 - 1) == vq.VQ_EWORKSPACE
+    assert _gemv([_m(d=8, nbits=16)], ok_x, 4, ok_y, FAKE + 16, need16) == vq.VQ_EALIGN
+    assert _gemv([_m(d=8, nbits=16, K=65792)], ok_x, 1, ok_y, FAKE, 1 << 30) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(K=1088)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # K % 256
     assert _gemv([_m()], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED        # B = 2
     assert _gemv([_m(wi=FAKE + 8)], ok_x, 1, ok_y, None, 0) == vq.VQ_EALIGN

@@ -163,7 +163,10 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
   switch (format_of(a)) {
     case FMT_LUT8: if (B != 1) return VQ_EUNSUPPORTED; break;
     case FMT_WC12: if (residual || B != 1) return VQ_EUNSUPPORTED; break;
-    case FMT_WC16: if (residual || B > 16) return VQ_EUNSUPPORTED; break;
+    case FMT_WC16:
+      if (residual || B > 16) return VQ_EUNSUPPORTED;
+      if (!wc16t_fits(a.N, a.K / a.d, wc16t_jsplit(a.K / a.d))) return VQ_EUNSUPPORTED;
+      break;
     default: return VQ_EUNSUPPORTED;
   }
   if (a.K % 256) return VQ_EUNSUPPORTED;
@@ -190,8 +193,15 @@ static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const 
 }
 
 // Virtual-OC kernels: whole rows per workgroup, no workspace.
+// Workspace of the 16-bit kernel: per matrix the codebook split by
+// dimension (1 MiB) and x's values by dimension (B K fp16), 256-byte aligned.
+static size_t wc16_ws_bytes(const vq_matrix &a, int32_t B) {
+  const size_t xb = ((size_t)B * a.K * 2 + 255) / 256 * 256;
+  return ((size_t)1 << 20) + xb;
+}
+
 static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                   float *const *y, void *stream) {
+                   float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   const Format f = format_of(m[0]);
   WcArgs args;
   memset(&args, 0, sizeof(args));
@@ -225,7 +235,7 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     d.ldy = m[i].N;
     d.jsplit = (f == FMT_LUT8)   ? wc8_jsplit(m[i].N, d.J)
                : (f == FMT_WC12) ? wc12_jsplit(d.J)
-                                 : wc16_jsplit(d.J);
+                                 : wc16t_jsplit(d.J);
     if (f == FMT_LUT8) {
       if (!wc8_burst_fits(d.N, d.J, d.jsplit)) burst = false;
       indices += (int64_t)d.N * d.J;
@@ -238,22 +248,41 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     WcMat &d = args.mat[s];
     const int R = (f == FMT_LUT8)   ? wc8_rows_per_wg(d.jsplit, w8)
                   : (f == FMT_WC12) ? wc12_rows_per_wg(d.jsplit)
-                                    : wc16_rows_per_wg(d.jsplit);
+                                    : wc16t_rows_per_wg(d.jsplit);
     d.nwg = (d.N + R - 1) / R;
     if (d.nwg > max_wg) max_wg = d.nwg;
   }
   if (max_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
+  if (f == FMT_WC16) {
+    Wc16tArgs t;
+    memset(&t, 0, sizeof(t));
+    t.a = args;
+    size_t need = 0;
+    int64_t maxbj = 0;
+    for (int s = 0; s < count; ++s) need += wc16_ws_bytes(m[order[s]], B);
+    if (!workspace || ws_bytes < need) return VQ_EWORKSPACE;
+    if (!aligned(workspace, 256)) return VQ_EALIGN;
+    char *w = static_cast<char *>(workspace);
+    for (int s = 0; s < count; ++s) {
+      const vq_matrix &a = m[order[s]];
+      t.wct[s] = reinterpret_cast<uint16_t *>(w);
+      t.xt[s] = reinterpret_cast<uint16_t *>(w + ((size_t)1 << 20));
+      w += wc16_ws_bytes(a, B);
+      maxbj = std::max<int64_t>(maxbj, (int64_t)B * (a.K / a.d));
+    }
+    const int prep_blocks = (int)std::min<int64_t>((65536 + maxbj + 255) / 256, 4096);
+    return hip_status(launch_wc16t(t, (int)max_wg, prep_blocks, stream));
+  }
   const int err = (f == FMT_LUT8)   ? launch_wc8(args, (int)max_wg, w8, burst, stream)
-                  : (f == FMT_WC12) ? launch_wc12(args, (int)max_wg, max_j, stream)
-                                    : launch_wc16(args, (int)max_wg, stream);
+                                    : launch_wc12(args, (int)max_wg, max_j, stream);
   return hip_status(err);
 }
 
 static int gemv_plain(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                      float *const *y, void *stream) {
+                      float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   const int st = check_group(m, count, x, B, y, false);
   if (st != VQ_OK) return st;
-  return gemv_wc(m, count, x, B, y, stream);
+  return gemv_wc(m, count, x, B, y, workspace, ws_bytes, stream);
 }
 
 static int gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
@@ -364,6 +393,11 @@ size_t vq_workspace_bytes(const vq_matrix *m, int32_t count, int32_t B, int32_t 
     const vq_matrix &a = m[i];
     if (a.K <= 0 || a.N <= 0 || a.d <= 0 || a.K % a.d) return 0;
   }
+  if (!residual && format_of(m[0]) == FMT_WC16) {
+    size_t n = 0;
+    for (int i = 0; i < count; ++i) n += wc16_ws_bytes(m[i], B);
+    return n;
+  }
   if (!residual || format_of(m[0]) != FMT_LUT8) return 0;   // only the residual kernel takes one
   Plan p;
   make_plan(m, count, B, p);
@@ -450,9 +484,7 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K, int32_t 
 
 int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B, float *const *y,
             void *workspace, size_t ws_bytes, void *stream) {
-  (void)workspace;   // no kernel of vq_gemv needs one (vq_workspace_bytes gives 0)
-  (void)ws_bytes;
-  return gemv_plain(m, count, x, B, y, stream);
+  return gemv_plain(m, count, x, B, y, workspace, ws_bytes, stream);
 }
 
 int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,

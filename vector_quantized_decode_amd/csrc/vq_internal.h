@@ -62,6 +62,14 @@ struct WcArgs {
   int32_t count;
 };
 
+// The 16-bit kernel's per-matrix scratch (in the caller's workspace): the
+// codebook split by dimension and x's values in the order the kernel reads.
+struct Wc16tArgs {
+  WcArgs a;
+  uint16_t *wct[VQ_MAX_GROUP];   // [8][65536] fp16
+  uint16_t *xt[VQ_MAX_GROUP];    // [8][B][K/8] fp16
+};
+
 int wc12_rows_per_wg(int jsplit);
 int wc12_jsplit(int J);
 int wc8_waves(int64_t indices, int max_split);
@@ -69,10 +77,11 @@ int wc8_rows_per_wg(int jsplit, int waves);
 int wc8_jsplit(int N, int J);
 bool wc8_burst_fits(int N, int J, int jsplit);
 int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, void *stream);
-int wc16_rows_per_wg(int jsplit);
-int wc16_jsplit(int J);
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
-int launch_wc16(const WcArgs &a, int grid_x, void *stream);
+int wc16t_jsplit(int J);
+int wc16t_rows_per_wg(int jsplit);
+bool wc16t_fits(int N, int J, int jsplit);
+int launch_wc16t(const Wc16tArgs &a, int grid_x, int prep_blocks, void *stream);
 int launch_repack_wi12(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
 int launch_repack_wi16(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
 

@@ -21,11 +21,14 @@
 //     in LDS; a lane owns one subvector j, reads WC[c] (8 bytes) for each
 //     index and adds x_j . WC[c] with two packed fp16 dot products into fp32.
 //     Each workgroup covers whole rows: no partial sums leave it.
-//   * wc16_kernel (d = 8, n = 16, up to 16 tokens): the codebook (65536 x 8
-//     fp16, 1 MiB) does not fit in LDS and is gathered from the caches; the
-//     16-token contraction sum_j x_b,j . WC[c_rj] runs on the matrix cores,
-//     one v_mfma_f32_16x16x32_f16 per 16 rows x 4 subvectors, where a lane's
-//     gathered codebook row is exactly its 8-element slice of the B operand.
+//   * wc16t_kernel (d = 8, n = 16, up to 16 tokens): the codebook (65536 x 8
+//     fp16, 1 MiB) does not fit in LDS, but one of its dimensions does
+//     (65536 fp16, 128 KiB).  The kernel makes eight passes, one per
+//     dimension t, with that dimension's table in LDS; the 16-token
+//     contraction sum_j x_b,8j+t WC[c_rj][t] runs on the matrix cores (one
+//     v_mfma_f32_16x16x32_f16 per 16 rows x 32 subvectors) with x's
+//     dimension-t values as A and the looked-up table values as B.  The
+//     wave's indices stay in registers across the passes.
 #include <hip/hip_runtime.h>
 
 #include "vq_internal.h"
@@ -442,66 +445,110 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
 }
 
 // --------------------------------------------------------------------------
-// d = 8, n = 16, up to 16 tokens
+// d = 8, n = 16, up to 16 tokens: the codebook split by dimension
 // --------------------------------------------------------------------------
-// Wave = 16 rows x all tokens x all J subvectors.  Index chunk (row group rg,
-// subvector block jb of 32): lane l holds 8 uint16 indices, the q-th of row
-// 16 rg + l%16 at subvector 32 jb + l/16 + 4 q.  MFMA q of the block contracts
-// subvectors 32 jb + 4 q .. + 3: lane l's A slice is x[token l%16] at those
-// subvectors' 8 inputs (l/16 picks the subvector), its B slice the gathered
-// WC row of its own index.  D[token][row]: lane l holds tokens 4(l/16) .. +3
-// of row l%16.
-template <int W>
-__global__ void __launch_bounds__(W * 64) wc16_kernel(const WcArgs args) {
-  __shared__ f32x4_t part[W * 64];
-  const WcMat M = load_wcmat(args);
+// y[b][r] = sum_t sum_j x[b][8 j + t] WC[c_rj][t]: for each dimension t the
+// table WC[.][t] (65536 fp16, 128 KiB) fits in LDS, and the contraction over
+// j runs on the matrix cores with x's dimension-t values as A and the looked-
+// up table values as B.  A pre-pass writes the tables (dimension-major) and
+// x's dimension-t values in the order the A operand reads them.
+//   wct[t][c]                      = WC[c][t]
+//   xt[t][b][jb][s][i] (16 B runs) = x[b][8 (32 jb + s + 4 i) + t]
+__global__ void wc16_prep_kernel(const Wc16tArgs args) {
+  const WcMat &M = args.a.mat[blockIdx.y];
+  uint16_t *wct = args.wct[blockIdx.y];
+  uint16_t *xt = args.xt[blockIdx.y];
+  const int J = M.J, JB = J >> 5;
+  const int64_t nx = (int64_t)M.B * J;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < 65536 + nx;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    if (e < 65536) {
+      const u32x4 v = reinterpret_cast<const u32x4 *>(M.wc)[e];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) wct[(size_t)t * 65536 + e] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
+    } else {
+      const int64_t f = e - 65536;
+      const int b = (int)(f / J), j = (int)(f % J);
+      const u32x4 v = reinterpret_cast<const u32x4 *>(M.x + (size_t)b * J * 8)[j];
+      const int jb = j >> 5, r = j & 31, sub = r & 3, i = r >> 2;
+      const size_t pos = ((size_t)b * JB + jb) * 32 + sub * 8 + i;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        xt[(size_t)t * M.B * J + pos] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
+    }
+  }
+}
+
+template <int W, int NBLK>
+__global__ void __launch_bounds__(W * 64) wc16t_kernel(const Wc16tArgs args) {
+  constexpr int NT = W * 64;
+  __shared__ __align__(16) _Float16 tbl[65536];
+  const WcMat M = load_wcmat(args.a);
   if ((int)blockIdx.x >= M.nwg) return;
+  const uint16_t *wct = args.wct[blockIdx.y];
+  const uint16_t *xt = args.xt[blockIdx.y];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int S = M.jsplit;                    // waves sharing a row group along J
-  const int rgl = wave / S, sg = wave % S;
+  const int lS = 31 - __builtin_clz((unsigned)M.jsplit);
+  const int S = 1 << lS;
+  const int rgl = wave >> lS, sg = wave & (S - 1);
   const int JB = M.J >> 5;
   const int NG = (M.N + 15) >> 4;
-  const int rgw = (int)blockIdx.x * (W / S) + rgl;
+  const int rgw = (int)blockIdx.x * (W >> lS) + rgl;
   const int rg = min(rgw, NG - 1);
-  const int seg = (JB + S - 1) / S;
-  const int jb0 = min(sg * seg, JB), jb1 = min(jb0 + seg, JB);
+  const int seg = (JB + S - 1) >> lS;
+  const int kbeg = min(sg * seg, JB), kend = min(kbeg + seg, JB);
   const int tok = lane & 15, sub = lane >> 4;
   const bool has_tok = tok < M.B;
-  const int K = M.J * 8;
-  const uint8_t *xrow = reinterpret_cast<const uint8_t *>(M.x) + (size_t)(has_tok ? tok : 0) * K * 2;
-  const uint8_t *wcb = reinterpret_cast<const uint8_t *>(M.wc);
-  const uint8_t *wi = M.wi + ((size_t)rg * JB * 64 + lane) * 16;
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  u32x4 idx = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb0, JB - 1) * 64 * 16);
-  u32x4 idx_next = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb0 + 1, JB - 1) * 64 * 16);
-  for (int jb = jb0; jb < jb1; ++jb) {
-    // gathers of this block, the block after next's indices, then the MFMAs
-    half8_t b[8], a[8];
+  // the wave's index blocks, all in registers for the eight passes
+  const __amdgpu_buffer_rsrc_t rwi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(M.wi + (size_t)rg * JB * 1024), (short)0, JB * 1024, kWcBufferWord3);
+  u32x4 ib[NBLK];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t c = (idx[q >> 1] >> ((q & 1) * 16)) & 0xffffu;
-      b[q] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4 *>(wcb + (size_t)c * 16));
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = jb * 32 + 4 * q + sub;
-      const u32x4 xv = has_tok ? *reinterpret_cast<const u32x4 *>(xrow + (size_t)j * 16)
-                               : u32x4{0u, 0u, 0u, 0u};
-      a[q] = __builtin_bit_cast(half8_t, xv);
-    }
-    idx = idx_next;
-    idx_next = *reinterpret_cast<const u32x4 *>(wi + (size_t)min(jb + 2, JB - 1) * 64 * 16);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[q], acc, 0, 0, 0);
+  for (int p = 0; p < NBLK; ++p) {
+    const uint32_t off = kbeg + p < kend ? (uint32_t)(kbeg + p) * 1024u + (uint32_t)lane * 16u : kWcOutOfRange;
+    ib[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, off, 0, kWcNontemporal));
   }
-  if (S > 1) {                               // segments added in order through LDS
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const size_t xplane = (size_t)M.B * M.J;          // fp16 values per dimension plane of xt
+  const uint16_t *xrow = xt + ((size_t)(has_tok ? tok : 0) * JB) * 32 + sub * 8;
+  for (int t = 0; t < 8; ++t) {
+    __syncthreads();                                 // the previous table is no longer read
+    {
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(wct + (size_t)t * 65536);
+      u32x4 *dst = reinterpret_cast<u32x4 *>(tbl);
+#pragma unroll
+      for (int u = 0; u < 8192 / NT; ++u) dst[threadIdx.x + u * NT] = src[threadIdx.x + u * NT];
+    }
+    __syncthreads();
+    const uint16_t *xp = xrow + (size_t)t * xplane;
+    // an opaque zero per pass keeps the 8 NBLK table addresses from being
+    // computed once before the passes and held in registers
+    uint32_t z;
+    __asm__ volatile("s_mov_b32 %0, 0" : "=s"(z));
+    const char *tb = reinterpret_cast<const char *>(tbl);
+#pragma unroll
+    for (int p = 0; p < NBLK; ++p) {
+      if (kbeg + p < kend) {
+        const u32x4 xv = has_tok ? *reinterpret_cast<const u32x4 *>(xp + (size_t)(kbeg + p) * 32)
+                                 : u32x4{0u, 0u, 0u, 0u};
+        half8_t b;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          b[i] = *reinterpret_cast<const _Float16 *>(tb + 2 * (((ib[p][i >> 1] | z) >> (16 * (i & 1))) & 0xffffu));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xv), b, acc, 0, 0, 0);
+      }
+    }
+  }
+  if (S > 1) {                                       // segments added in order through LDS
+    __syncthreads();
+    f32x4_t *part = reinterpret_cast<f32x4_t *>(tbl);
     part[wave * 64 + lane] = acc;
     __syncthreads();
     if (sg != 0) return;
-    for (int t = 1; t < S; ++t) {
-      const f32x4_t o = part[(wave + t) * 64 + lane];
+    for (int q = 1; q < S; ++q) {
+      const f32x4_t o = part[(wave + q) * 64 + lane];
       acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
     }
   }
@@ -509,8 +556,8 @@ __global__ void __launch_bounds__(W * 64) wc16_kernel(const WcArgs args) {
     const int row = rgw * 16 + tok;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = sub * 4 + i;
-      if (t < M.B && row < M.N) M.y[(size_t)t * M.ldy + row] = acc[i];
+      const int tt = sub * 4 + i;
+      if (tt < M.B && row < M.N) M.y[(size_t)tt * M.ldy + row] = acc[i];
     }
   }
 }
@@ -554,7 +601,8 @@ __global__ void repack_wi12_kernel(const uint8_t *canon, int N, int J, uint8_t *
 
 // canonical 16-bit rows (little-endian uint16, [N][J]) -> tile-16x32-16:
 // chunk (rg, jb), lane l holds the indices of row 16 rg + l%16 at subvectors
-// 32 jb + l/16 + 4 q, q < 8
+// 32 jb + l/16 + 4 q, q < 8 (the q-th is the lane's B-operand value at
+// k = 8 (l/16) + q of the block's MFMA)
 __global__ void repack_wi16_kernel(const uint8_t *canon, int N, int J, uint8_t *dev) {
   const int NG = (N + 15) >> 4, JB = J >> 5;
   const int64_t total = (int64_t)NG * JB * 64;
@@ -587,7 +635,6 @@ static int wgrid(int64_t work, int block) {
 
 constexpr int WC12_W = 4;
 constexpr int WC12_PF = 2;
-constexpr int WC16_W = 8;
 constexpr int WC8_W = 8;       // waves per workgroup, 8-bit kernels
 constexpr int WC8_NCH = 4;     // chunks per wave of the burst kernel
 
@@ -626,11 +673,6 @@ bool wc8_burst_fits(int N, int J, int jsplit) {
   const int64_t bytes = (int64_t)((N + 15) / 16) * 1024 * (J / 64);
   return (J / 64 + jsplit - 1) / jsplit <= WC8_NCH && bytes < ((int64_t)1 << 31);
 }
-int wc16_rows_per_wg(int jsplit) { return WC16_W / jsplit * 16; }
-int wc16_jsplit(int J) {
-  const int JB = J / 32;
-  return JB <= 8 ? 1 : (JB <= 16 ? 2 : 4);
-}
 
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   (void)max_j;
@@ -652,12 +694,28 @@ int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, void *stream)
   return (int)hipGetLastError();
 }
 
-int launch_wc16(const WcArgs &a, int grid_x, void *stream) {
+// Waves per row group along J for the 16-bit kernel: the smallest power of
+// two (at most 16) that leaves each wave at most 16 blocks of 32 subvectors
+// (its indices stay in registers for the eight passes).
+int wc16t_jsplit(int J) {
+  const int JB = J / 32;
+  int s = 1;
+  while (s < 16 && (JB + s - 1) / s > 16) s *= 2;
+  return s;
+}
+int wc16t_rows_per_wg(int jsplit) { return 16 / jsplit * 16; }
+// Rows of at most 256 blocks (K <= 65536), indices within 32-bit offsets.
+bool wc16t_fits(int N, int J, int jsplit) {
+  return (J / 32 + jsplit - 1) / jsplit <= 16 && (int64_t)((N + 15) / 16) * (J / 32) * 1024 < ((int64_t)1 << 31);
+}
+int launch_wc16t(const Wc16tArgs &a, int grid_x, int prep_blocks, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error
-  hipLaunchKernelGGL((wc16_kernel<WC16_W>), dim3(grid_x, a.count), dim3(WC16_W * 64), 0,
-                     reinterpret_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(wc16_prep_kernel, dim3(prep_blocks, a.a.count), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((wc16t_kernel<16, 16>), dim3(grid_x, a.a.count), dim3(16 * 64), 0, st, a);
   return (int)hipGetLastError();
 }
+
 
 int launch_repack_wi12(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream) {
   const int64_t total = (int64_t)((N + 15) >> 4) * (J >> 6) * 64;

@@ -192,7 +192,6 @@ static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const 
   return VQ_OK;
 }
 
-// Virtual-OC kernels: whole rows per workgroup, no workspace.
 // Workspace of the 16-bit kernel: per matrix the codebook split by
 // dimension (1 MiB) and x's values by dimension (B K fp16), 256-byte aligned.
 static size_t wc16_ws_bytes(const vq_matrix &a, int32_t B) {
@@ -200,6 +199,8 @@ static size_t wc16_ws_bytes(const vq_matrix &a, int32_t B) {
   return ((size_t)1 << 20) + xb;
 }
 
+// Virtual-OC kernels: whole rows per workgroup; only the 16-bit kernel takes
+// a workspace.
 static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                    float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   const Format f = format_of(m[0]);

@@ -15,6 +15,11 @@ Workloads (matrix shapes follow LLaMA-7B / LLaMA-13B / Gemma-2-9B linears):
   5  3584->14336, 14336->3584, d=4, n=8, B=1, plus randomized Hadamard
      rotation of x and a 1-bit sign residual with an fp16 scale per group of
      128 weights
+  6  mixture-of-experts decode shaped like Qwen3-30B-A3B (hidden 2048, expert
+     width 768, 8 routed experts per token): the gate and up projections of
+     the 8 experts, 16 matrices 2048->768, each with its own codebook,
+     d=4, n=8, B=1
+  7  the same experts' down projections, 8 matrices 768->2048, d=4, n=8, B=1
 
 Distributions: x ~ N(0, 1), codebook ~ N(0, 0.02) (0.02 is the standard
 deviation), indices uniform over [0, 2^n), residual sign bits Bernoulli(0.5),
@@ -81,6 +86,11 @@ WORKLOADS = {
                 4, 8, 1, [MatrixSpec("up", 3584, 14336),
                           MatrixSpec("down", 14336, 3584)],
                 residual=True, group=128),
+    6: Workload(6, "MoE decode (Qwen3-30B-A3B-shaped), gate+up of 8 routed experts, 2 bits/weight",
+                4, 8, 1, [MatrixSpec(f"e{e}.{p}", 2048, 768) for e in range(8)
+                          for p in ("gate", "up")]),
+    7: Workload(7, "MoE decode (Qwen3-30B-A3B-shaped), down of 8 routed experts, 2 bits/weight",
+                4, 8, 1, [MatrixSpec(f"e{e}.down", 768, 2048) for e in range(8)]),
 }
 
 

@@ -294,6 +294,23 @@ def test_gemv_largest_group():
         assert np.array_equal(y1.view(np.uint32), y.view(np.uint32)), f"matrix {i}"
 
 
+@pytest.mark.parametrize("wl", [6, 7])
+def test_gemv_moe_expert_groups(wl):
+    # mixture-of-experts decode: the routed experts' projections (16 gate/up
+    # matrices, or 8 down matrices), each with its own codebook, in one
+    # launch; every matrix in full against the oracle, and grouped equal to
+    # alone bitwise
+    _say(f"gemv MoE expert group (workload {wl}) in one launch")
+    w = synth.workload(wl)
+    mis = [synth.matrix_inputs(wl, m) for m in range(w.count)]
+    mats = [_upload(mi) for mi in mis]
+    ys, _ = _run_gemv(mats, [mi.x for mi in mis])
+    for i, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _oracle_plain(mi), f"workload {wl} matrix {i}")
+    (y1,), _ = _run_gemv([mats[3]], [mis[3].x])
+    assert np.array_equal(y1.view(np.uint32), ys[3].view(np.uint32))
+
+
 def test_gemv_mixed_group():
     _say("gemv mixed shapes in one launch")
     mis = [synth.small_matrix(1024, 300, 4, 8, seed=1), synth.small_matrix(512, 2000, 4, 8, seed=2),

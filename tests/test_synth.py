@@ -60,3 +60,7 @@ def test_weight_bytes_per_layer():
     assert synth.weight_bytes(3) == 76120064
     assert synth.weight_bytes(4) == 45088768
     assert synth.weight_bytes(5) == 40144896
+    # MoE experts: 16 x (768 rows x 512 subvectors + 2 KiB), 8 x (2048 x 192 + 2 KiB)
+    assert synth.weight_bytes(6) == 16 * (768 * 512 + 2048)
+    assert synth.weight_bytes(7) == 8 * (2048 * 192 + 2048)
+    assert synth.workload(6).count == 16 and synth.workload(7).count == 8

@@ -656,7 +656,9 @@ int wc8_jsplit(int N, int J) {
   const int jt = J / 64;
   int s = 1;
   while (s < WC8_W && (jt + s - 1) / s > WC8_NCH) s *= 2;
-  while (2 * s <= WC8_W && 2 * s <= jt && (ng * s + WC8_W - 1) / WC8_W < 64) s *= 2;
+  while (2 * s <= WC8_W && 2 * s <= jt && (ng * s + WC8_W - 1) / WC8_W < 64 &&
+         (jt <= 2 || (jt + 2 * s - 1) / (2 * s) >= 2))
+    s *= 2;
   return s;
 }
 // Waves per workgroup: 8, or 4 for calls of at most 2^20 indices whose splits

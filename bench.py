@@ -48,7 +48,7 @@ CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
 # kernels; 12- and 16-bit indices: virtual-codebook kernels)
 KERNEL_SRC = {1: "vq_kernels_wc.hip", 2: "vq_kernels_wc.hip", 3: "vq_kernels_wc.hip",
               4: "vq_kernels_wc.hip", 5: "vq_kernels.hip", 6: "vq_kernels_wc.hip",
-              7: "vq_kernels_wc.hip"}
+              7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
@@ -57,7 +57,8 @@ WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
                   4: "llama13b-shaped-batched-decode-2bit-d8-b16",
                   5: "gemma2-9b-mlp-rotated-vq-residual-3.125bit-b1",
                  6: "qwen3-30b-a3b-moe-8-experts-gate-up-2bit-b1",
-                 7: "qwen3-30b-a3b-moe-8-experts-down-2bit-b1"}
+                 7: "qwen3-30b-a3b-moe-8-experts-down-2bit-b1",
+                 8: "llama7b-attn-qkvo-4096x4096-2bit-b4"}
 
 
 def parse():

@@ -20,6 +20,7 @@ Workloads (matrix shapes follow LLaMA-7B / LLaMA-13B / Gemma-2-9B linears):
      the 8 experts, 16 matrices 2048->768, each with its own codebook,
      d=4, n=8, B=1
   7  the same experts' down projections, 8 matrices 768->2048, d=4, n=8, B=1
+  8  workload 2 for 4 tokens per call (batched or speculative decode), B=4
 
 Distributions: x ~ N(0, 1), codebook ~ N(0, 0.02) (0.02 is the standard
 deviation), indices uniform over [0, 2^n), residual sign bits Bernoulli(0.5),
@@ -91,6 +92,8 @@ WORKLOADS = {
                           for p in ("gate", "up")]),
     7: Workload(7, "MoE decode (Qwen3-30B-A3B-shaped), down of 8 routed experts, 2 bits/weight",
                 4, 8, 1, [MatrixSpec(f"e{e}.down", 768, 2048) for e in range(8)]),
+    8: Workload(8, "LLaMA-7B attention projections q/k/v/o, 4 tokens, 2 bits/weight",
+                4, 8, 4, list(_LLAMA7B_ATTN)),
 }
 
 

@@ -99,7 +99,8 @@ def test_gemv_validation_errors():
     assert _gemv([_m(d=8, nbits=16)], ok_x, 4, ok_y, FAKE + 16, need16) == vq.VQ_EALIGN
     assert _gemv([_m(d=8, nbits=16, K=65792)], ok_x, 1, ok_y, FAKE, 1 << 30) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(K=1088)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # K % 256
-    assert _gemv([_m()], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED        # B = 2
+    assert _gemv([_m()], ok_x, 5, ok_y, None, 0) == vq.VQ_EUNSUPPORTED        # 8-bit: B <= 4
+    assert _gemv([_m(K=12288)], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # long rows: B = 1
     assert _gemv([_m(wi=FAKE + 8)], ok_x, 1, ok_y, None, 0) == vq.VQ_EALIGN
     assert _gemv([_m()], [FAKE + 2], 1, ok_y, None, 0) == vq.VQ_EALIGN
     assert _gemv([_m()], ok_x, 1, [FAKE + 1], None, 0) == vq.VQ_EALIGN
@@ -116,6 +117,7 @@ def test_gemv_validation_errors():
 def test_gemv_residual_validation_errors():
     ok_x, ok_y = [FAKE], [FAKE]
     assert _gemv([_m(signs=None)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL
+    assert _gemv([_m()], ok_x, 2, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED   # one token
     assert _gemv([_m(group=64)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(d=4, nbits=12)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EUNSUPPORTED
     # indices beyond 2 GiB: past the residual kernel's 32-bit buffer offsets

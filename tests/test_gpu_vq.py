@@ -311,6 +311,35 @@ def test_gemv_moe_expert_groups(wl):
     assert np.array_equal(y1.view(np.uint32), ys[3].view(np.uint32))
 
 
+@pytest.mark.parametrize("K,N,B", [(256, 17, 2), (1024, 333, 3), (2048, 1000, 4), (4096, 513, 2),
+                                   (8192, 77, 4), (768, 2048, 3)])
+def test_gemv_several_tokens(K, N, B):
+    # 2 to 4 tokens per call: each codebook entry looked up once serves every
+    # token; every token within tolerance, bitwise equal alone and grouped
+    _say(f"gemv K={K} N={N} B={B}")
+    mi = synth.small_matrix(K, N, 4, 8, B=B, seed=K + N + B)
+    other = synth.small_matrix(1024, 700, 4, 8, B=B, seed=99)
+    mats = [_upload(mi), _upload(other)]
+    ys, _ = _run_gemv(mats, [mi.x, other.x], B=B)
+    _assert_close(ys[0], _oracle_plain(mi), f"K={K} N={N} B={B}")
+    _assert_close(ys[1], _oracle_plain(other), f"grouped companion B={B}")
+    (y1,), _ = _run_gemv([mats[0]], [mi.x], B=B)
+    assert np.array_equal(y1.view(np.uint32), ys[0].view(np.uint32))
+
+
+def test_gemv_workload8_four_tokens_sampled():
+    # LLaMA-7B q/k/v/o for 4 tokens in one launch, in the launch bench.py times
+    _say("gemv workload 8 (4 x 4096x4096, 4 tokens, one launch)")
+    w = synth.workload(8)
+    mis = [synth.matrix_inputs(8, m) for m in range(w.count)]
+    ys, _ = _run_gemv([_upload(mi) for mi in mis], [mi.x for mi in mis], B=4)
+    rng = np.random.default_rng(8)
+    for m, (mi, y) in enumerate(zip(mis, ys)):
+        rows = np.sort(rng.choice(mi.N, size=256, replace=False))
+        ref = oracle.vq_gemv(mi.x, mi.wc, oracle.pack_rows(mi.idx[rows], 8), rows.size, mi.K, 4, 8)
+        _assert_close(y[:, rows], ref, f"workload 8 matrix {m}")
+
+
 def test_gemv_mixed_group():
     _say("gemv mixed shapes in one launch")
     mis = [synth.small_matrix(1024, 300, 4, 8, seed=1), synth.small_matrix(512, 2000, 4, 8, seed=2),

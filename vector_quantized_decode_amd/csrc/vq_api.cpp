@@ -161,7 +161,11 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
     }
   }
   switch (format_of(a)) {
-    case FMT_LUT8: if (B != 1) return VQ_EUNSUPPORTED; break;
+    case FMT_LUT8:
+      // several tokens: plain GEMV only, and rows the burst kernel takes whole
+      if (B > 1 && (residual || B > 4 || !wc8_burst_fits(a.N, a.K / a.d, wc8_jsplit(a.N, a.K / a.d))))
+        return VQ_EUNSUPPORTED;
+      break;
     case FMT_WC12: if (residual || B != 1) return VQ_EUNSUPPORTED; break;
     case FMT_WC16:
       if (residual || B > 16) return VQ_EUNSUPPORTED;
@@ -244,7 +248,7 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     }
     if (d.J > max_j) max_j = d.J;
   }
-  const int w8 = (f == FMT_LUT8) ? wc8_waves(indices, max_split) : 0;
+  const int w8 = (f == FMT_LUT8) ? wc8_waves(indices, max_split, B) : 0;
   for (int s = 0; s < count; ++s) {
     WcMat &d = args.mat[s];
     const int R = (f == FMT_LUT8)   ? wc8_rows_per_wg(d.jsplit, w8)
@@ -274,7 +278,7 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     const int prep_blocks = (int)std::min<int64_t>((65536 + maxbj + 255) / 256, 4096);
     return hip_status(launch_wc16t(t, (int)max_wg, prep_blocks, stream));
   }
-  const int err = (f == FMT_LUT8)   ? launch_wc8(args, (int)max_wg, w8, burst, stream)
+  const int err = (f == FMT_LUT8)   ? launch_wc8(args, (int)max_wg, w8, burst, B, stream)
                                     : launch_wc12(args, (int)max_wg, max_j, stream);
   return hip_status(err);
 }

@@ -72,11 +72,11 @@ struct Wc16tArgs {
 
 int wc12_rows_per_wg(int jsplit);
 int wc12_jsplit(int J);
-int wc8_waves(int64_t indices, int max_split);
+int wc8_waves(int64_t indices, int max_split, int B);
 int wc8_rows_per_wg(int jsplit, int waves);
 int wc8_jsplit(int N, int J);
 bool wc8_burst_fits(int N, int J, int jsplit);
-int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, void *stream);
+int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, int B, void *stream);
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
 int wc16t_jsplit(int J);
 int wc16t_rows_per_wg(int jsplit);

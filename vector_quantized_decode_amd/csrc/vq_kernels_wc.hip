@@ -365,12 +365,35 @@ constexpr int kWcNontemporal = 2;
 // a buffer descriptor with an out-of-range offset (zeros, no memory access)
 // and are not looked up.  Sums are formed in the same order as wc8_kernel,
 // so the two kernels give bitwise the same y for the same split.
-template <int W, int NCH, int PF0>
+// One chunk for TB tokens: each codebook entry read from LDS serves every
+// token (two dot2 per token).  TB = 1 is wc8_chunk.
+template <int TB>
+__device__ __forceinline__ void wc8_chunk_tb(float (&acc)[TB][16], const u32x4 &w,
+                                             const uint2 (&xj)[TB], const char *wcr, uint32_t base) {
+#define WC8TB_ONE(R, Q, K)                                                   \
+  {                                                                          \
+    const uint2 e = lds_u2(wcr, wc8_addr<K>(w[Q], base));                    \
+    _Pragma("unroll") for (int b = 0; b < TB; ++b) {                         \
+      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].x), h2(e.x), acc[b][R], false); \
+      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].y), h2(e.y), acc[b][R], false); \
+    }                                                                        \
+  }
+  WC8TB_ONE(0, 0, 0) WC8TB_ONE(1, 0, 1) WC8TB_ONE(2, 0, 2) WC8TB_ONE(3, 0, 3)
+  WC8TB_ONE(4, 1, 0) WC8TB_ONE(5, 1, 1) WC8TB_ONE(6, 1, 2) WC8TB_ONE(7, 1, 3)
+  WC8TB_ONE(8, 2, 0) WC8TB_ONE(9, 2, 1) WC8TB_ONE(10, 2, 2) WC8TB_ONE(11, 2, 3)
+  WC8TB_ONE(12, 3, 0) WC8TB_ONE(13, 3, 1) WC8TB_ONE(14, 3, 2) WC8TB_ONE(15, 3, 3)
+#undef WC8TB_ONE
+}
+
+// TB: tokens per call the kernel is built for (1, 2 or 4; the call's B <= TB,
+// tokens past B read zeros and are not stored).  Every token's sums are
+// formed in the same order as for one token.
+template <int W, int NCH, int PF0, int TB>
 __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
   constexpr int NT = W * 64;
   constexpr int RP = 2048 / NT;               // 16-byte replica stores per thread
   __shared__ __align__(16) char wcr[256 * 256];
-  __shared__ float part[W * 64];
+  __shared__ float part[TB][W * 64];
   const WcMat M = load_wcmat(args);
   if ((int)blockIdx.x >= M.nwg) return;
   const int lane = threadIdx.x & 63;
@@ -389,12 +412,12 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
       const_cast<uint8_t *>(M.wi + (size_t)rg * 1024), (short)0, (int)(kstride * (uint32_t)JT),
       kWcBufferWord3);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(M.x), (short)0, M.J * 8, kWcBufferWord3);
+      const_cast<uint16_t *>(M.x), (short)0, M.B * M.J * 8, kWcBufferWord3);
   auto wi_off = [&](int k) -> uint32_t {
     return k < kend ? (uint32_t)k * kstride + (uint32_t)lane * 16u : kWcOutOfRange;
   };
-  auto x_off = [&](int k) -> uint32_t {
-    return k < kend ? (uint32_t)(k * 64 + lane) * 8u : kWcOutOfRange;
+  auto x_off = [&](int k, int b) -> uint32_t {
+    return (k < kend && b < M.B) ? (uint32_t)(b * M.J + k * 64 + lane) * 8u : kWcOutOfRange;
   };
 
   // 1. codebook entries for the replicas, the x slices, the first PF0 chunks
@@ -402,10 +425,12 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
 #pragma unroll
   for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
   u32x4 buf[NCH];
-  uint2 xbuf[NCH];
+  uint2 xbuf[NCH][TB];
 #pragma unroll
   for (int p = 0; p < NCH; ++p)
-    xbuf[p] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, x_off(kbeg + p), 0, 0));
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      xbuf[p][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, x_off(kbeg + p, b), 0, 0));
 #pragma unroll
   for (int p = 0; p < PF0; ++p)
     buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, wi_off(kbeg + p), 0, kWcNontemporal));
@@ -424,24 +449,36 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
 
   // 3. lookups in chunk order, each as soon as its indices arrive
   const uint32_t base = (uint32_t)(lane & 15) << 3;
-  float acc[16];
+  float acc[TB][16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
 #pragma unroll
   for (int p = 0; p < NCH; ++p)
-    if (kbeg + p < kend) wc8_chunk(acc, buf[p], xbuf[p], wcr, base);
+    if (kbeg + p < kend) wc8_chunk_tb<TB>(acc, buf[p], xbuf[p], wcr, base);
 
   // 4. rows out: lane 4r holds row r of the 16 (segments added in order)
-  float v = wreduce_rows16(acc, lane);
+  float v[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) v[b] = wreduce_rows16(acc[b], lane);
   if (S > 1) {
-    part[wave * 64 + lane] = v;
+#pragma unroll
+    for (int b = 0; b < TB; ++b) part[b][wave * 64 + lane] = v[b];
     __syncthreads();
     if (sg != 0) return;
-    v = part[wave * 64 + lane];
-    for (int t = 1; t < S; ++t) v += part[(wave + t) * 64 + lane];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      v[b] = part[b][wave * 64 + lane];
+      for (int t = 1; t < S; ++t) v[b] += part[b][(wave + t) * 64 + lane];
+    }
   }
   const int row = rgw * 16 + ((lane >> 2) & 15);
-  if ((lane & 3) == 0 && rgw < NG && row < M.N) M.y[row] = v;
+  if ((lane & 3) == 0 && rgw < NG && row < M.N) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      if (b < M.B) M.y[(size_t)b * M.ldy + row] = v[b];
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -661,12 +698,12 @@ int wc8_jsplit(int N, int J) {
     s *= 2;
   return s;
 }
-// Waves per workgroup: 8, or 4 for calls of at most 2^20 indices whose splits
-// allow it (there more, smaller workgroups start sooner; measured 2.7 against
+// Waves per workgroup: 8, or 4 for one-token calls of at most 2^20 indices
+// whose splits allow it (there more, smaller workgroups start sooner; measured 2.7 against
 // 3.1 us for one 512 x 512 matrix).  Only the number of row groups per
 // workgroup changes, not the order of any sum.
-int wc8_waves(int64_t indices, int max_split) {
-  return (indices <= ((int64_t)1 << 20) && max_split <= 4) ? 4 : WC8_W;
+int wc8_waves(int64_t indices, int max_split, int B) {
+  return (B == 1 && indices <= ((int64_t)1 << 20) && max_split <= 4) ? 4 : WC8_W;
 }
 int wc8_rows_per_wg(int jsplit, int waves) { return waves / jsplit * 16; }
 // The burst kernel serves a call when every row fits in its waves' chunks
@@ -684,13 +721,18 @@ int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   return (int)hipGetLastError();
 }
 
-int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, void *stream) {
+int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, int B, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error
-  if (waves == 4)
+  if (B > 4 || (B > 1 && !burst)) return (int)hipErrorInvalidConfiguration;
+  if (waves == 4 && B == 1)
     hipLaunchKernelGGL((wc8_kernel<4, 1>), dim3(grid_x, a.count), dim3(4 * 64), 0, st, a);
+  else if (burst && B == 1)
+    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 1>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
+  else if (burst && B == 2)
+    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 2>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
   else if (burst)
-    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
+    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 4>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
   else
     hipLaunchKernelGGL((wc8_kernel<WC8_W, 2>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
   return (int)hipGetLastError();

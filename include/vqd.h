@@ -239,8 +239,7 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K,
  *            Other formats: unused (vq_workspace_bytes gives 0); any value.
  * All matrices are served by one kernel launch ((8, 16): a pre-pass that
  * fills the workspace, then the lookup kernel).  Supported:
- * (d, nbits) = (4, 8) with 1 <= B <= 4 (B > 1: K/d <= 256 * S, S the
- * matrix's split, i.e. K <= 8192 at most), (4, 12) with B == 1, (8, 16) with
+ * (d, nbits) = (4, 8) with 1 <= B <= 4, (4, 12) with B == 1, (8, 16) with
  * 1 <= B <= 16 and K <= 65536; 1 <= count <= VQ_MAX_GROUP.  A matrix sums in
  * the same order alone or in a group.
  */

@@ -100,7 +100,6 @@ def test_gemv_validation_errors():
     assert _gemv([_m(d=8, nbits=16, K=65792)], ok_x, 1, ok_y, FAKE, 1 << 30) == vq.VQ_EUNSUPPORTED
     assert _gemv([_m(K=1088)], ok_x, 1, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # K % 256
     assert _gemv([_m()], ok_x, 5, ok_y, None, 0) == vq.VQ_EUNSUPPORTED        # 8-bit: B <= 4
-    assert _gemv([_m(K=12288)], ok_x, 2, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # long rows: B = 1
     assert _gemv([_m(wi=FAKE + 8)], ok_x, 1, ok_y, None, 0) == vq.VQ_EALIGN
     assert _gemv([_m()], [FAKE + 2], 1, ok_y, None, 0) == vq.VQ_EALIGN
     assert _gemv([_m()], ok_x, 1, [FAKE + 1], None, 0) == vq.VQ_EALIGN

@@ -312,10 +312,11 @@ def test_gemv_moe_expert_groups(wl):
 
 
 @pytest.mark.parametrize("K,N,B", [(256, 17, 2), (1024, 333, 3), (2048, 1000, 4), (4096, 513, 2),
-                                   (8192, 77, 4), (768, 2048, 3)])
+                                   (8192, 77, 4), (768, 2048, 3), (8448, 50, 2), (12288, 100, 3)])
 def test_gemv_several_tokens(K, N, B):
     # 2 to 4 tokens per call: each codebook entry looked up once serves every
     # token; every token within tolerance, bitwise equal alone and grouped
+    # (rows of more than 32 chunks are streamed, with their group)
     _say(f"gemv K={K} N={N} B={B}")
     mi = synth.small_matrix(K, N, 4, 8, B=B, seed=K + N + B)
     other = synth.small_matrix(1024, 700, 4, 8, B=B, seed=99)

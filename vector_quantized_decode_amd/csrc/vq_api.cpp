@@ -162,9 +162,7 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
   }
   switch (format_of(a)) {
     case FMT_LUT8:
-      // several tokens: plain GEMV only, and rows the burst kernel takes whole
-      if (B > 1 && (residual || B > 4 || !wc8_burst_fits(a.N, a.K / a.d, wc8_jsplit(a.N, a.K / a.d))))
-        return VQ_EUNSUPPORTED;
+      if (B > 1 && (residual || B > 4)) return VQ_EUNSUPPORTED;   // several tokens: plain only
       break;
     case FMT_WC12: if (residual || B != 1) return VQ_EUNSUPPORTED; break;
     case FMT_WC16:

@@ -273,12 +273,34 @@ __device__ __forceinline__ void wc8_chunk(float (&acc)[16], const u32x4 &w, uint
 #undef WC8_ONE
 }
 
-template <int W, int PF>
+// One chunk for TB tokens: each codebook entry read from LDS serves every
+// token (two dot2 per token).  TB = 1 is wc8_chunk.
+template <int TB>
+__device__ __forceinline__ void wc8_chunk_tb(float (&acc)[TB][16], const u32x4 &w,
+                                             const uint2 (&xj)[TB], const char *wcr, uint32_t base) {
+#define WC8TB_ONE(R, Q, K)                                                   \
+  {                                                                          \
+    const uint2 e = lds_u2(wcr, wc8_addr<K>(w[Q], base));                    \
+    _Pragma("unroll") for (int b = 0; b < TB; ++b) {                         \
+      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].x), h2(e.x), acc[b][R], false); \
+      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].y), h2(e.y), acc[b][R], false); \
+    }                                                                        \
+  }
+  WC8TB_ONE(0, 0, 0) WC8TB_ONE(1, 0, 1) WC8TB_ONE(2, 0, 2) WC8TB_ONE(3, 0, 3)
+  WC8TB_ONE(4, 1, 0) WC8TB_ONE(5, 1, 1) WC8TB_ONE(6, 1, 2) WC8TB_ONE(7, 1, 3)
+  WC8TB_ONE(8, 2, 0) WC8TB_ONE(9, 2, 1) WC8TB_ONE(10, 2, 2) WC8TB_ONE(11, 2, 3)
+  WC8TB_ONE(12, 3, 0) WC8TB_ONE(13, 3, 1) WC8TB_ONE(14, 3, 2) WC8TB_ONE(15, 3, 3)
+#undef WC8TB_ONE
+}
+
+// TB: tokens per call the kernel is built for (1, 2 or 4; B <= TB).  A token
+// past B loads the last token's x (in bounds) and is not stored.
+template <int W, int PF, int TB>
 __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   constexpr int NT = W * 64;
   constexpr int RP = 2048 / NT;               // 16-byte replica stores per thread
   __shared__ __align__(16) char wcr[256 * 256];
-  __shared__ float part[W * 64];
+  __shared__ float part[TB][W * 64];
   const WcMat M = load_wcmat(args);
   if ((int)blockIdx.x >= M.nwg) return;
   const int lane = threadIdx.x & 63;
@@ -301,13 +323,17 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   const size_t kstride = (size_t)NG * 1024;   // one 64-subvector tile of all row groups
   const uint8_t *wrg = wi + (size_t)rg * 1024;
   const uint2 *xg = reinterpret_cast<const uint2 *>(M.x) + lane;   // x_j, j = 64 k + lane
+  size_t xt[TB];                              // token rows of x, in uint2 units
+#pragma unroll
+  for (int b = 0; b < TB; ++b) xt[b] = (size_t)min(b, M.B - 1) * M.J;
   u32x4 buf[PF];
-  uint2 xbuf[PF];
+  uint2 xbuf[PF][TB];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     const int k = min(kbeg + p, JT - 1);
     buf[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrg + (size_t)k * kstride));
-    xbuf[p] = xg[k * 64];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) xbuf[p][b] = xg[xt[b] + k * 64];
   }
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
@@ -319,34 +345,49 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
 
   // 2. lookups: OC[j][c] = x_j . WC[c] formed per index, summed per row
   const uint32_t base = (uint32_t)(lane & 15) << 3;
-  float acc[16];
+  float acc[TB][16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
   for (int k0 = kbeg; k0 < kend; k0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int k = k0 + p;
       const u32x4 cur = buf[p];
-      const uint2 xj = xbuf[p];
+      uint2 xj[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) xj[b] = xbuf[p][b];
       // refill this slot with chunk k + PF (clamped: in bounds, unused)
       const int kn = min(k + PF, JT - 1);
       buf[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrg + (size_t)kn * kstride));
-      xbuf[p] = xg[kn * 64];
-      if (k < kend) wc8_chunk(acc, cur, xj, wcr, base);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) xbuf[p][b] = xg[xt[b] + kn * 64];
+      if (k < kend) wc8_chunk_tb<TB>(acc, cur, xj, wcr, base);
     }
   }
 
   // 3. rows out: lane 4r holds row r of the 16 (segments added in order)
-  float v = wreduce_rows16(acc, lane);
+  float v[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) v[b] = wreduce_rows16(acc[b], lane);
   if (S > 1) {
-    part[wave * 64 + lane] = v;
+#pragma unroll
+    for (int b = 0; b < TB; ++b) part[b][wave * 64 + lane] = v[b];
     __syncthreads();
     if (sg != 0) return;
-    v = part[wave * 64 + lane];
-    for (int t = 1; t < S; ++t) v += part[(wave + t) * 64 + lane];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      v[b] = part[b][wave * 64 + lane];
+      for (int t = 1; t < S; ++t) v[b] += part[b][(wave + t) * 64 + lane];
+    }
   }
   const int row = rgw * 16 + ((lane >> 2) & 15);
-  if ((lane & 3) == 0 && rgw < NG && row < M.N) M.y[row] = v;
+  if ((lane & 3) == 0 && rgw < NG && row < M.N) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      if (b < M.B) M.y[(size_t)b * M.ldy + row] = v[b];
+  }
 }
 
 // Raw buffer descriptors (gfx9 word 3), an offset past any buffer the
@@ -365,26 +406,6 @@ constexpr int kWcNontemporal = 2;
 // a buffer descriptor with an out-of-range offset (zeros, no memory access)
 // and are not looked up.  Sums are formed in the same order as wc8_kernel,
 // so the two kernels give bitwise the same y for the same split.
-// One chunk for TB tokens: each codebook entry read from LDS serves every
-// token (two dot2 per token).  TB = 1 is wc8_chunk.
-template <int TB>
-__device__ __forceinline__ void wc8_chunk_tb(float (&acc)[TB][16], const u32x4 &w,
-                                             const uint2 (&xj)[TB], const char *wcr, uint32_t base) {
-#define WC8TB_ONE(R, Q, K)                                                   \
-  {                                                                          \
-    const uint2 e = lds_u2(wcr, wc8_addr<K>(w[Q], base));                    \
-    _Pragma("unroll") for (int b = 0; b < TB; ++b) {                         \
-      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].x), h2(e.x), acc[b][R], false); \
-      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].y), h2(e.y), acc[b][R], false); \
-    }                                                                        \
-  }
-  WC8TB_ONE(0, 0, 0) WC8TB_ONE(1, 0, 1) WC8TB_ONE(2, 0, 2) WC8TB_ONE(3, 0, 3)
-  WC8TB_ONE(4, 1, 0) WC8TB_ONE(5, 1, 1) WC8TB_ONE(6, 1, 2) WC8TB_ONE(7, 1, 3)
-  WC8TB_ONE(8, 2, 0) WC8TB_ONE(9, 2, 1) WC8TB_ONE(10, 2, 2) WC8TB_ONE(11, 2, 3)
-  WC8TB_ONE(12, 3, 0) WC8TB_ONE(13, 3, 1) WC8TB_ONE(14, 3, 2) WC8TB_ONE(15, 3, 3)
-#undef WC8TB_ONE
-}
-
 // TB: tokens per call the kernel is built for (1, 2 or 4; the call's B <= TB,
 // tokens past B read zeros and are not stored).  Every token's sums are
 // formed in the same order as for one token.
@@ -724,17 +745,22 @@ int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
 int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, int B, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error
-  if (B > 4 || (B > 1 && !burst)) return (int)hipErrorInvalidConfiguration;
+  if (B < 1 || B > 4) return (int)hipErrorInvalidConfiguration;
+  const dim3 grid(grid_x, a.count), block(WC8_W * 64);
   if (waves == 4 && B == 1)
-    hipLaunchKernelGGL((wc8_kernel<4, 1>), dim3(grid_x, a.count), dim3(4 * 64), 0, st, a);
+    hipLaunchKernelGGL((wc8_kernel<4, 1, 1>), grid, dim3(4 * 64), 0, st, a);
   else if (burst && B == 1)
-    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 1>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
+    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 1>), grid, block, 0, st, a);
   else if (burst && B == 2)
-    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 2>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
+    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 2>), grid, block, 0, st, a);
   else if (burst)
-    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 4>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
+    hipLaunchKernelGGL((wc8_burst_kernel<WC8_W, WC8_NCH, 2, 4>), grid, block, 0, st, a);
+  else if (B == 1)
+    hipLaunchKernelGGL((wc8_kernel<WC8_W, 2, 1>), grid, block, 0, st, a);
+  else if (B == 2)
+    hipLaunchKernelGGL((wc8_kernel<WC8_W, 2, 2>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((wc8_kernel<WC8_W, 2>), dim3(grid_x, a.count), dim3(WC8_W * 64), 0, st, a);
+    hipLaunchKernelGGL((wc8_kernel<WC8_W, 2, 4>), grid, block, 0, st, a);
   return (int)hipGetLastError();
 }
 

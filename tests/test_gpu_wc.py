@@ -131,6 +131,21 @@ def test_gemv_16bit_shapes(K, N, B):
     _assert_close(y, ref, f"16-bit K={K} N={N} B={B}")
 
 
+@pytest.mark.parametrize("d,nbits,B", [(4, 8, 1), (4, 8, 4), (4, 12, 1), (8, 16, 1), (8, 16, 16)])
+def test_gemv_longest_supported_rows(d, nbits, B):
+    # K = 65536, the longest row each 16-bit call takes (16 waves x 16 blocks
+    # of 32 subvectors); the 8- and 12-bit kernels stream it
+    K, N = 65536, 24
+    _say(f"gemv K={K} N={N} d={d} n={nbits} B={B}")
+    mi = synth.small_matrix(K, N, d, nbits, B=B, seed=4242 + nbits + B)
+    (y,) = _run([_up(mi)], [mi.x], B)
+    # the dequantize-then-GEMV form (pinned equal to the lookup form by the
+    # oracle tests): the lookup form would build a 65536-column codebook
+    # product for every subvector
+    ref = oracle.dequant_gemv(mi.x, mi.wc, oracle.pack_rows(mi.idx, nbits), N, K, d, nbits)
+    _assert_close(y, ref, f"K={K} d={d} n={nbits} B={B}")
+
+
 def _sample_rows(N, rng, n=192):
     return np.unique(np.concatenate([np.arange(32), rng.choice(N, n, replace=False),
                                      np.arange(N - 32, N)]))

@@ -459,6 +459,24 @@ def test_gemv_nonfinite_input_propagates_like_oracle(bad):
     _assert_close(y2, _oracle_plain(mi2), "after non-finite call")
 
 
+def test_gemv_residual_on_quantizer_output():
+    # the offline quantizer's artifacts (non-uniform, K-means indices; signs
+    # and scales of a real residual) decoded on the GPU against the oracle
+    from vector_quantized_decode_amd import quantize
+    _say("residual GEMV on quantizer output")
+    N, K = 96, 1024
+    rng = np.random.default_rng(12)
+    W = rng.standard_normal((N, K)) * 0.02
+    q = quantize.quantize_rotated_residual(W, seed=2, iters=6)
+    x = rng.standard_normal((1, K)).astype(np.float16)
+    m = vq.upload_matrix(q.idx, q.wc, K, N, 4, 8, sign_bits=q.sign_bits, alpha=q.alpha, group=128,
+                         rht_sign=q.rht_sign, had_block=q.had_block, device=DEV)
+    (y,), _ = _run_gemv([m], [x], residual=True)
+    ref = oracle.vq_gemv_residual(x, q.wc, oracle.pack_rows(q.idx, 8), oracle.pack_rows(q.sign_bits, 1),
+                                  q.alpha, q.rht_sign, q.had_block, N, K, 4, 8, 128)
+    _assert_close(y, ref, "quantizer output")
+
+
 def test_gemv_residual_zero_input_gives_exact_zero():
     # K = 3584 splits each row over 14 workgroups (fixed-point hand-off)
     _say("gemv_residual x = 0")

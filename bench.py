@@ -48,7 +48,7 @@ CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
 # kernels; 12- and 16-bit indices: virtual-codebook kernels)
 KERNEL_SRC = {1: "vq_kernels_wc.hip", 2: "vq_kernels_wc.hip", 3: "vq_kernels_wc.hip",
               4: "vq_kernels_wc.hip", 5: "vq_kernels.hip", 6: "vq_kernels_wc.hip",
-              7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip"}
+              7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip", 9: "vq_kernels_wc.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
@@ -58,7 +58,8 @@ WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
                   5: "gemma2-9b-mlp-rotated-vq-residual-3.125bit-b1",
                  6: "qwen3-30b-a3b-moe-8-experts-gate-up-2bit-b1",
                  7: "qwen3-30b-a3b-moe-8-experts-down-2bit-b1",
-                 8: "llama7b-attn-qkvo-4096x4096-2bit-b4"}
+                 8: "llama7b-attn-qkvo-4096x4096-2bit-b4",
+                 9: "llama7b-mlp-gate-up-silu-fused-2bit-b1"}
 
 
 def parse():
@@ -148,6 +149,10 @@ def main():
     ys = [torch.empty((wl.B, m.N), dtype=torch.float32, device=dev) for m in base]
     ws = vq.alloc_workspace(base, wl.B, residual=residual, device=dev)
     call = vq.vq_gemv_residual if residual else vq.vq_gemv
+    if wl.gated_pairs:
+        # gate/up pairs share the gate's x and write one gated output per pair
+        def call(lay, xs_, B_, ys_, ws_, n_, stream=None):
+            vq.vq_gemv_swiglu(lay[0::2], lay[1::2], xs_[0::2], B_, ys_[0::2], ws_, n_, stream=stream)
     torch.cuda.synchronize()
     print(f"# setup: {copies} copies x {layer_bytes} B in {time.time() - t0:.1f} s",
           file=sys.stderr, flush=True)
@@ -161,9 +166,18 @@ def main():
         rng = np.random.default_rng(7)
         worst = 0.0
         ok = True
-        for mi, y in zip(mis, ys):
+        for k, (mi, y) in enumerate(zip(mis, ys)):
             rows = np.sort(rng.choice(mi.N, size=min(256, mi.N), replace=False))
-            if residual:
+            if wl.gated_pairs:
+                if k % 2:
+                    continue                                  # the up matrix of a pair
+                up = mis[k + 1]
+                g = oracle.vq_gemv(mi.x, mi.wc, oracle.pack_rows(mi.idx[rows], 8), rows.size,
+                                   mi.K, mi.d, mi.nbits)
+                u = oracle.vq_gemv(mi.x, up.wc, oracle.pack_rows(up.idx[rows], 8), rows.size,
+                                   mi.K, mi.d, mi.nbits)
+                ref = oracle.silu_gated(g, u)
+            elif residual:
                 ref = oracle.vq_gemv_residual(mi.x, mi.wc, oracle.pack_rows(mi.idx[rows], 8),
                                               oracle.pack_rows(mi.sign_bits[rows], 1),
                                               mi.alpha[rows], mi.rht_sign, mi.had_block,
@@ -254,6 +268,13 @@ def main():
             packed.append((pw, ps))
 
         def one_layer():
+            if wl.gated_pairs:
+                for k in range(0, len(mis), 2):
+                    g, u = mis[k], mis[k + 1]
+                    oracle.silu_gated(oracle.vq_gemv(g.x, g.wc, packed[k][0], g.N, g.K, g.d, g.nbits),
+                                      oracle.vq_gemv(g.x, u.wc, packed[k + 1][0], g.N, g.K, g.d,
+                                                     g.nbits))
+                return
             for mi, (pw, ps) in zip(mis, packed):
                 if residual:
                     oracle.vq_gemv_residual(mi.x, mi.wc, pw, ps, mi.alpha, mi.rht_sign,

@@ -263,6 +263,22 @@ int vq_gemv_residual(const vq_matrix *m, int32_t count,
                      const uint16_t *const *x, int32_t B, float *const *y,
                      void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Gate and up projections of a SiLU-gated MLP with the gating fused (the
+ * LLaMA, Mixtral and Qwen3 models the EVA page evaluates use it): for each of
+ * `count` pairs i, y[i][b][r] = silu(g)[r] * u[r], silu(z) = z / (1 + e^-z),
+ * where g and u are vq_gemv of gate[i] and up[i] on the shared x[i]
+ * [EVA 2.A, 2.B].  gate[i] and up[i] must have the same K, N and format;
+ * one workgroup looks up both for the same rows, so the two products never
+ * leave it.  Supported: (d, nbits) = (4, 8), 1 <= B <= 2, rows of at most
+ * 4 * S chunks of 64 subvectors (S the split of the row, at most 8, i.e.
+ * K <= 8192), VQ_EUNSUPPORTED otherwise.  workspace / ws_bytes unused.
+ * Arguments otherwise as vq_gemv.
+ */
+int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
+                   const uint16_t *const *x, int32_t B, float *const *y,
+                   void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,7 +56,7 @@ import numpy as np
 __all__ = [
     "pack_bits", "unpack_bits", "pack_rows", "unpack_rows",
     "sylvester_hadamard", "rht", "output_codebook", "lookup_sum",
-    "vq_gemv", "dequant_gemv", "residual_term", "vq_gemv_residual", "compare",
+    "vq_gemv", "dequant_gemv", "residual_term", "vq_gemv_residual", "silu_gated", "compare",
     "within_tolerance", "REL_L2_TOL", "MAX_ERR_RMS_TOL",
 ]
 
@@ -259,6 +259,15 @@ def vq_gemv_residual(x: np.ndarray, wc: np.ndarray, wi_packed: np.ndarray,
     xr = xf if rht_sign is None else rht(xf, rht_sign, had_block)
     y = vq_gemv(xr, wc, wi_packed, N, K, d, nbits)
     return y + residual_term(xr, signs_packed, alpha, N, K, group)
+
+
+def silu_gated(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """silu(g) * u with silu(z) = z / (1 + exp(-z)): the gating of a SiLU-
+    gated MLP (the LLaMA, Mixtral and Qwen3 models the EVA page evaluates)
+    applied to the gate and up projections' outputs, in float64."""
+    gf = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return gf / (1.0 + np.exp(-gf)) * np.asarray(u, dtype=np.float64)
 
 
 # --------------------------------------------------------------------------

@@ -21,6 +21,9 @@ Workloads (matrix shapes follow LLaMA-7B / LLaMA-13B / Gemma-2-9B linears):
      d=4, n=8, B=1
   7  the same experts' down projections, 8 matrices 768->2048, d=4, n=8, B=1
   8  workload 2 for 4 tokens per call (batched or speculative decode), B=4
+  9  LLaMA-7B MLP gate and up projections (2 x 4096->11008), d=4, n=8, B=1,
+     called as one gate/up pair with the SiLU gating fused (both use the
+     gate's x)
 
 Distributions: x ~ N(0, 1), codebook ~ N(0, 0.02) (0.02 is the standard
 deviation), indices uniform over [0, 2^n), residual sign bits Bernoulli(0.5),
@@ -61,6 +64,7 @@ class Workload:
     group: int = 128            # residual scale group (weights along K)
     outlier_frac: float = 0.0   # fraction of input channels scaled
     outlier_scale: float = 1.0
+    gated_pairs: bool = False   # matrices 2i, 2i+1 are a gate/up pair (SiLU gating fused)
 
     @property
     def count(self) -> int:
@@ -94,6 +98,9 @@ WORKLOADS = {
                 4, 8, 1, [MatrixSpec(f"e{e}.down", 768, 2048) for e in range(8)]),
     8: Workload(8, "LLaMA-7B attention projections q/k/v/o, 4 tokens, 2 bits/weight",
                 4, 8, 4, list(_LLAMA7B_ATTN)),
+    9: Workload(9, "LLaMA-7B MLP gate and up, SiLU gating fused, 2 bits/weight",
+                4, 8, 1, [MatrixSpec("gate", 4096, 11008), MatrixSpec("up", 4096, 11008)],
+                gated_pairs=True),
 }
 
 

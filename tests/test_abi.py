@@ -113,6 +113,19 @@ def test_gemv_validation_errors():
     assert _gemv([_m()] * 17, ok_x * 17, 1, ok_y * 17, FAKE, 1 << 30) == vq.VQ_EINVAL
 
 
+def test_gemv_swiglu_validation_errors():
+    c = vq._c["vq_gemv_swiglu"]
+    arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)
+    ptrs = lambda n, v=FAKE: (ctypes.c_void_p * n)(*([v] * n))
+    assert c(arr([_m()]), None, 1, ptrs(1), 1, ptrs(1), None, 0, None) == vq.VQ_EINVAL       # no up
+    assert c(arr([_m()]), arr([_m(N=65)]), 1, ptrs(1), 1, ptrs(1), None, 0, None) == vq.VQ_EINVAL
+    assert c(arr([_m()]), arr([_m()]), 1, ptrs(1), 3, ptrs(1), None, 0, None) == vq.VQ_EUNSUPPORTED
+    assert c(arr([_m(K=12288)]), arr([_m(K=12288)]), 1, ptrs(1), 1, ptrs(1), None, 0,
+             None) == vq.VQ_EUNSUPPORTED                                                   # long rows
+    assert c(arr([_m(d=4, nbits=12)]), arr([_m(d=4, nbits=12)]), 1, ptrs(1), 1, ptrs(1), None, 0,
+             None) == vq.VQ_EUNSUPPORTED
+
+
 def test_gemv_residual_validation_errors():
     ok_x, ok_y = [FAKE], [FAKE]
     assert _gemv([_m(signs=None)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL

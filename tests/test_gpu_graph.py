@@ -1,6 +1,6 @@
 """Graph replay of the library's calls (the way bench.py times them).
 
-A HIP graph captured from vq_gemv / vq_gemv_residual must give, on every
+A HIP graph captured from vq_gemv / vq_gemv_residual / vq_gemv_swiglu must give, on every
 replay, bitwise the result of the same call made eagerly: the calls record
 only kernels (no memset nodes), the residual call's counters and
 accumulators are left at zero by every call, and the 16-bit call rewrites
@@ -36,6 +36,9 @@ def _case(kind):
         return mis, 1, True
     if kind == "wc12":
         return [synth.small_matrix(1024, 300, 4, 12, seed=36)], 1, False
+    if kind == "swiglu":
+        mis = [synth.small_matrix(2048, 300, 4, 8, seed=39), synth.small_matrix(2048, 300, 4, 8, seed=40)]
+        return mis, 1, False
     if kind == "wc16":
         return [synth.small_matrix(1024, 100, 8, 16, B=4, seed=37),
                 synth.small_matrix(2048, 40, 8, 16, B=4, seed=38)], 4, False
@@ -50,7 +53,7 @@ def _upload(mi, residual):
     return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, device=DEV)
 
 
-@pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "wc12", "wc16"])
+@pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "wc12", "wc16", "swiglu"])
 def test_graph_replays_match_eager(kind):
     print(f"[graph] {kind}", flush=True)
     mis, B, residual = _case(kind)
@@ -59,11 +62,16 @@ def test_graph_replays_match_eager(kind):
     ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
     ws = vq.alloc_workspace(mats, B, residual=residual, device=DEV)
     call = vq.vq_gemv_residual if residual else vq.vq_gemv
+    if kind == "swiglu":
+        def call(ms, xs_, B_, ys_, ws_, n_, stream=None):
+            vq.vq_gemv_swiglu(ms[0::2], ms[1::2], xs_[0::2], B_, ys_[0::2], ws_, n_, stream=stream)
 
     # eager reference
     call(mats, xs, B, ys, ws, ws.numel())
     torch.cuda.synchronize()
     ref = [y.cpu().numpy().copy() for y in ys]
+    if kind == "swiglu":
+        ref = ref[:1]            # one gated output per pair; the up matrix's slot is not written
     assert all(np.isfinite(r).all() for r in ref)
 
     # an unrelated eager call between replays, on its own outputs and workspace

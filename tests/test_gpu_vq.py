@@ -341,6 +341,27 @@ def test_gemv_workload8_four_tokens_sampled():
         _assert_close(y[:, rows], ref, f"workload 8 matrix {m}")
 
 
+@pytest.mark.parametrize("K,N,B,pairs", [(256, 17, 1, 1), (1024, 333, 2, 2), (4096, 700, 1, 3),
+                                         (2048, 768, 2, 4), (8192, 77, 1, 1)])
+def test_gemv_swiglu_pairs(K, N, B, pairs):
+    # silu(gate x) * (up x) for gate/up pairs sharing x, against the oracle's
+    # two GEMVs and its gating
+    _say(f"swiglu K={K} N={N} B={B} pairs={pairs}")
+    gates = [synth.small_matrix(K, N, 4, 8, B=B, seed=500 + 2 * p) for p in range(pairs)]
+    ups = [synth.small_matrix(K, N, 4, 8, B=B, seed=501 + 2 * p) for p in range(pairs)]
+    xs = [torch.from_numpy(g.x).to(DEV) for g in gates]       # each pair uses its gate's x
+    ys = [torch.full((B, N), float("nan"), dtype=torch.float32, device=DEV) for _ in range(pairs)]
+    gm = [_upload(g) for g in gates]
+    um = [_upload(u) for u in ups]
+    ws = vq.alloc_workspace(gm, B, device=DEV)
+    vq.vq_gemv_swiglu(gm, um, xs, B, ys, ws, ws.numel())
+    torch.cuda.synchronize()
+    for p, (g, u, y) in enumerate(zip(gates, ups, ys)):
+        gy = oracle.vq_gemv(g.x, g.wc, oracle.pack_rows(g.idx, 8), N, K, 4, 8)
+        uy = oracle.vq_gemv(g.x, u.wc, oracle.pack_rows(u.idx, 8), N, K, 4, 8)
+        _assert_close(y.cpu().numpy(), oracle.silu_gated(gy, uy), f"swiglu pair {p}")
+
+
 def test_gemv_mixed_group():
     _say("gemv mixed shapes in one launch")
     mis = [synth.small_matrix(1024, 300, 4, 8, seed=1), synth.small_matrix(512, 2000, 4, 8, seed=2),

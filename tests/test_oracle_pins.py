@@ -385,3 +385,19 @@ def test_dequant_form_matches_lookup_form_and_a_loop():
             for t in range(2):
                 ref[0, r] += float(x[0, 2 * j + t]) * float(wc[idx[r, j], t])
     assert np.array_equal(y, ref)
+
+
+def test_silu_gating_closed_forms():
+    # silu(0) = 0; silu(1) = 1 / (1 + 1/e); silu(z) - silu(-z) = z; silu(z)
+    # tends to z for large z and to 0 for very negative z; u scales linearly
+    e = np.e
+    g = np.array([0.0, 1.0, -1.0, 2.5, -2.5, 40.0, -800.0])
+    u = np.array([3.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0])
+    y = o.silu_gated(g, u)
+    assert y[0] == 0.0
+    assert abs(y[1] - 1.0 / (1.0 + 1.0 / e)) < 1e-15
+    assert abs(y[2] - (-1.0 / (1.0 + e))) < 1e-15
+    assert abs((y[3] - y[4]) - 2.5) < 1e-14
+    assert abs(y[5] - 40.0) < 1e-12
+    assert y[6] == 0.0 or abs(y[6]) < 1e-300
+    assert np.allclose(o.silu_gated(g[:6], 2.0 * u[:6]), 2.0 * y[:6], rtol=0, atol=1e-15)

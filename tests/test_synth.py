@@ -65,3 +65,4 @@ def test_weight_bytes_per_layer():
     assert synth.weight_bytes(7) == 8 * (2048 * 192 + 2048)
     assert synth.workload(6).count == 16 and synth.workload(7).count == 8
     assert synth.weight_bytes(8) == synth.weight_bytes(2) and synth.workload(8).B == 4
+    assert synth.weight_bytes(9) == 2 * (11008 * 1024 + 2048) and synth.workload(9).gated_pairs

@@ -75,6 +75,8 @@ _c = {
     "vq_gemv_residual": _sig("vq_gemv_residual", ctypes.c_int,
                              [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                               ctypes.POINTER(_vp), _vp, _sz, _vp]),
+    "vq_gemv_swiglu": _sig("vq_gemv_swiglu", ctypes.c_int,
+                           [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
 }
 
 # every symbol the header declares (checked by the ABI test)
@@ -228,6 +230,16 @@ def vq_gemv_residual(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspa
     _check(_c["vq_gemv_residual"](arr, len(mats), _ptr_array(xs), B, _ptr_array(ys),
                                   _ptr(workspace), ws_bytes, _stream(stream)),
            "vq_gemv_residual")
+
+
+def vq_gemv_swiglu(gates: Sequence, ups: Sequence, xs: Sequence, B: int, ys: Sequence, workspace,
+                   ws_bytes: int, stream=None) -> None:
+    """y[i] = silu(gate[i] x[i]) * (up[i] x[i]), gate/up pairs of one shape."""
+    if len(gates) != len(ups):
+        raise ValueError("one up matrix per gate matrix")
+    _check(_c["vq_gemv_swiglu"](_mat_array(gates), _mat_array(ups), len(gates), _ptr_array(xs), B,
+                                _ptr_array(ys), _ptr(workspace), ws_bytes, _stream(stream)),
+           "vq_gemv_swiglu")
 
 
 # ------------------------------------------------------------------ helpers

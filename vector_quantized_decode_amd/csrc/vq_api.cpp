@@ -495,4 +495,63 @@ int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x
   return gemv_residual(m, count, x, B, y, workspace, ws_bytes, stream);
 }
 
+int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
+                   const uint16_t *const *x, int32_t B, float *const *y, void *workspace,
+                   size_t ws_bytes, void *stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!up) return VQ_EINVAL;
+  int st = check_group(gate, count, x, B, y, false);
+  if (st != VQ_OK) return st;
+  for (int i = 0; i < count; ++i) {
+    st = check_matrix(up[i], B, false);
+    if (st != VQ_OK) return st;
+    if (up[i].K != gate[i].K || up[i].N != gate[i].N || up[i].d != gate[i].d ||
+        up[i].nbits != gate[i].nbits)
+      return VQ_EINVAL;
+  }
+  if (format_of(gate[0]) != FMT_LUT8 || B > 2) return VQ_EUNSUPPORTED;
+  WcPairArgs args;
+  memset(&args, 0, sizeof(args));
+  args.a.count = count;
+  // longest rows first, as in the plain call; the split is the plain one
+  int order[VQ_MAX_GROUP];
+  for (int i = 0; i < count; ++i) order[i] = i;
+  for (int a = 1; a < count; ++a)
+    for (int b = a; b > 0 && gate[order[b]].K > gate[order[b - 1]].K; --b) {
+      const int t = order[b];
+      order[b] = order[b - 1];
+      order[b - 1] = t;
+    }
+  int max_split = 1;
+  for (int s = 0; s < count; ++s) {
+    const int i = order[s];
+    WcMat &d = args.a.mat[s];
+    d.wi = static_cast<const uint8_t *>(gate[i].wi);
+    d.wc = gate[i].wc;
+    d.x = x[i];
+    d.y = y[i];
+    d.J = gate[i].K / gate[i].d;
+    d.N = gate[i].N;
+    d.B = B;
+    d.ldy = gate[i].N;
+    d.jsplit = wc8_jsplit(d.N, d.J);
+    if (!wc8_burst_fits(d.N, d.J, d.jsplit)) return VQ_EUNSUPPORTED;
+    if (d.jsplit > max_split) max_split = d.jsplit;
+    args.wi2[s] = static_cast<const uint8_t *>(up[i].wi);
+    args.wc2[s] = up[i].wc;
+  }
+  // two row-group slots (gate, up) per output row group
+  const int waves = wc8_swiglu_waves(max_split);
+  int64_t max_wg = 0;
+  for (int s = 0; s < count; ++s) {
+    WcMat &d = args.a.mat[s];
+    const int R = waves / d.jsplit / 2 * 16;
+    d.nwg = (d.N + R - 1) / R;
+    if (d.nwg > max_wg) max_wg = d.nwg;
+  }
+  if (max_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
+  return hip_status(launch_wc8_swiglu(args, (int)max_wg, waves, B, stream));
+}
+
 }  // extern "C"

@@ -62,6 +62,14 @@ struct WcArgs {
   int32_t count;
 };
 
+// Gate/up pairs of the fused SiLU-gated call: a.mat[i] is the gate matrix
+// (with x and y), wi2 / wc2 the up matrix of the same shape.
+struct WcPairArgs {
+  WcArgs a;
+  const uint8_t *wi2[VQ_MAX_GROUP];
+  const uint16_t *wc2[VQ_MAX_GROUP];
+};
+
 // The 16-bit kernel's per-matrix scratch (in the caller's workspace): the
 // codebook split by dimension and x's values in the order the kernel reads.
 struct Wc16tArgs {
@@ -78,6 +86,8 @@ int wc8_jsplit(int N, int J);
 bool wc8_burst_fits(int N, int J, int jsplit);
 int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, int B, void *stream);
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
+int wc8_swiglu_waves(int max_split);
+int launch_wc8_swiglu(const WcPairArgs &a, int grid_x, int waves, int B, void *stream);
 int wc16t_jsplit(int J);
 int wc16t_rows_per_wg(int jsplit);
 bool wc16t_fits(int N, int J, int jsplit);

@@ -503,6 +503,122 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
 }
 
 // --------------------------------------------------------------------------
+// d = 4, n = 8: gate and up projections with the SiLU-gated product fused
+// --------------------------------------------------------------------------
+// y[b][r] = silu(gate x_b)[r] * (up x_b)[r], silu(z) = z / (1 + e^-z), for
+// the gate/up pairs of a SiLU-gated MLP that share x.  The burst kernel's
+// walk, with the workgroup's row-group slots taken in pairs: slot 2q looks up
+// gate rows, slot 2q + 1 the same rows of up, so every wave does the work of
+// a plain call.  The up codebook's 16 copies sit in the half of each
+// 256-byte LDS row the gate copies leave free (bytes 128-255, banks 32-63),
+// so an up lookup's address is a gate lookup's with bit 7 set.  Both sums
+// are formed in the one-matrix order; the two meet in LDS and only their
+// gated product is stored.
+template <int W, int NCH, int PF0, int TB>
+__global__ void __launch_bounds__(W * 64) wc8_swiglu_kernel(const WcPairArgs args) {
+  constexpr int NT = W * 64;
+  constexpr int RP = 2048 / NT;               // 16-byte replica stores per thread and codebook
+  __shared__ __align__(16) char wcr[256 * 256];
+  __shared__ float part[TB][W * 64];
+  __shared__ float upv[TB][W / 2][64];        // up row sums of each slot pair
+  const WcMat M = load_wcmat(args.a);
+  if ((int)blockIdx.x >= M.nwg) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lS = 31 - __builtin_clz((unsigned)M.jsplit);
+  const int S = 1 << lS;
+  const int slot = wave >> lS, sg = wave & (S - 1);
+  const int pr = slot >> 1, up = slot & 1;    // output row group of the workgroup, matrix
+  const int JT = M.J >> 6;
+  const int NG = (M.N + 15) >> 4;
+  const int rgw = (int)blockIdx.x * (W >> (lS + 1)) + pr;
+  const int rg = min(rgw, NG - 1);
+  const int seg = (JT + S - 1) >> lS;
+  const int kbeg = min(sg * seg, JT), kend = min(kbeg + seg, JT);
+  const uint32_t kstride = (uint32_t)NG * 1024u;
+  const uint8_t *wsel = up ? args.wi2[blockIdx.y] : M.wi;
+  const __amdgpu_buffer_rsrc_t rwi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(wsel + (size_t)rg * 1024), (short)0, (int)(kstride * (uint32_t)JT),
+      kWcBufferWord3);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(M.x), (short)0, M.B * M.J * 8, kWcBufferWord3);
+  auto wi_off = [&](int k) -> uint32_t {
+    return k < kend ? (uint32_t)k * kstride + (uint32_t)lane * 16u : kWcOutOfRange;
+  };
+  auto x_off = [&](int k, int b) -> uint32_t {
+    return (k < kend && b < M.B) ? (uint32_t)(b * M.J + k * 64 + lane) * 8u : kWcOutOfRange;
+  };
+
+  uint2 eg[RP], eu[RP];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    eg[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
+    eu[u] = reinterpret_cast<const uint2 *>(args.wc2[blockIdx.y])[(threadIdx.x + u * NT) >> 3];
+  }
+  u32x4 buf[NCH];
+  uint2 xbuf[NCH][TB];
+#pragma unroll
+  for (int p = 0; p < NCH; ++p)
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      xbuf[p][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rx, x_off(kbeg + p, b), 0, 0));
+#pragma unroll
+  for (int p = 0; p < PF0; ++p)
+    buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, wi_off(kbeg + p), 0, kWcNontemporal));
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int s = threadIdx.x + u * NT;       // entry s >> 3, copies 2 (s & 7) and + 1
+    char *row = wcr + (s >> 3) * 256 + (s & 7) * 16;
+    *reinterpret_cast<u32x4 *>(row) = u32x4{eg[u].x, eg[u].y, eg[u].x, eg[u].y};
+    *reinterpret_cast<u32x4 *>(row + 128) = u32x4{eu[u].x, eu[u].y, eu[u].x, eu[u].y};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = PF0; p < NCH; ++p)
+    buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, wi_off(kbeg + p), 0, kWcNontemporal));
+  __syncthreads();
+
+  const uint32_t base = ((uint32_t)(lane & 15) << 3) | ((uint32_t)up << 7);
+  float acc[TB][16];
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+#pragma unroll
+  for (int p = 0; p < NCH; ++p)
+    if (kbeg + p < kend) wc8_chunk_tb<TB>(acc, buf[p], xbuf[p], wcr, base);
+
+  float v[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) v[b] = wreduce_rows16(acc[b], lane);
+  if (S > 1) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) part[b][wave * 64 + lane] = v[b];
+    __syncthreads();
+    if (sg == 0) {
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        v[b] = part[b][wave * 64 + lane];
+        for (int t = 1; t < S; ++t) v[b] += part[b][(wave + t) * 64 + lane];
+      }
+    }
+  }
+  // the up sums meet the gate sums of the same rows
+  if (sg == 0 && up) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) upv[b][pr][lane] = v[b];
+  }
+  __syncthreads();
+  if (sg != 0 || up) return;
+  const int row = rgw * 16 + ((lane >> 2) & 15);
+  if ((lane & 3) == 0 && rgw < NG && row < M.N) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      if (b < M.B) M.y[(size_t)b * M.ldy + row] = v[b] / (1.f + expf(-v[b])) * upv[b][pr][lane];
+  }
+}
+
+// --------------------------------------------------------------------------
 // d = 8, n = 16, up to 16 tokens: the codebook split by dimension
 // --------------------------------------------------------------------------
 // y[b][r] = sum_t sum_j x[b][8 j + t] WC[c_rj][t]: for each dimension t the
@@ -739,6 +855,26 @@ int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL((wc12_kernel<WC12_W, WC12_PF>), dim3(grid_x, a.count), dim3(WC12_W * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+// Waves of the fused gate/up kernel: two row-group slots per output row
+// group, so 8 waves for a split of up to 4 and 16 for a split of 8.
+int wc8_swiglu_waves(int max_split) { return max_split <= 4 ? WC8_W : 2 * WC8_W; }
+int launch_wc8_swiglu(const WcPairArgs &a, int grid_x, int waves, int B, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // report only this launch's error
+  const dim3 grid(grid_x, a.a.count);
+  if (waves == WC8_W && B == 1)
+    hipLaunchKernelGGL((wc8_swiglu_kernel<WC8_W, WC8_NCH, 2, 1>), grid, dim3(WC8_W * 64), 0, st, a);
+  else if (waves == WC8_W && B == 2)
+    hipLaunchKernelGGL((wc8_swiglu_kernel<WC8_W, WC8_NCH, 2, 2>), grid, dim3(WC8_W * 64), 0, st, a);
+  else if (waves == 2 * WC8_W && B == 1)
+    hipLaunchKernelGGL((wc8_swiglu_kernel<2 * WC8_W, WC8_NCH, 2, 1>), grid, dim3(2 * WC8_W * 64), 0, st, a);
+  else if (waves == 2 * WC8_W && B == 2)
+    hipLaunchKernelGGL((wc8_swiglu_kernel<2 * WC8_W, WC8_NCH, 2, 2>), grid, dim3(2 * WC8_W * 64), 0, st, a);
+  else
+    return (int)hipErrorInvalidConfiguration;
   return (int)hipGetLastError();
 }
 

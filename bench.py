@@ -48,7 +48,8 @@ CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
 # kernels; 12- and 16-bit indices: virtual-codebook kernels)
 KERNEL_SRC = {1: "vq_kernels_wc.hip", 2: "vq_kernels_wc.hip", 3: "vq_kernels_wc.hip",
               4: "vq_kernels_wc.hip", 5: "vq_kernels.hip", 6: "vq_kernels_wc.hip",
-              7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip", 9: "vq_kernels_wc.hip"}
+              7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip", 9: "vq_kernels_wc.hip",
+              10: "vq_kernels_wc.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
@@ -59,7 +60,8 @@ WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
                  6: "qwen3-30b-a3b-moe-8-experts-gate-up-2bit-b1",
                  7: "qwen3-30b-a3b-moe-8-experts-down-2bit-b1",
                  8: "llama7b-attn-qkvo-4096x4096-2bit-b4",
-                 9: "llama7b-mlp-gate-up-silu-fused-2bit-b1"}
+                 9: "llama7b-mlp-gate-up-silu-fused-2bit-b1",
+                  10: "llama7b-attn-qkvo-4096x4096-2bit-b16"}
 
 
 def parse():
@@ -114,6 +116,8 @@ def main():
     torch.cuda.set_device(dev)
     wl = synth.workload(args.workload)
     residual = wl.residual
+    # more than 4 tokens at d=4, n=8: the matrix-core call, on canonical index rows
+    tokens = (wl.d, wl.nbits) == (4, 8) and wl.B > 4
     layer_bytes = synth.weight_bytes(args.workload)
     copies = args.copies or max(1, -(-(2 << 30) // layer_bytes))
 
@@ -127,7 +131,8 @@ def main():
                                          sign_bits=mi.sign_bits, alpha=mi.alpha, group=mi.group,
                                          rht_sign=mi.rht_sign, had_block=mi.had_block, device=dev))
         else:
-            base.append(vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, device=dev))
+            base.append(vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
+                                         canonical=tokens, device=dev))
     xs = [torch.from_numpy(mi.x).to(dev) for mi in mis]
     # further copies: seeded uniform random bytes in the device layouts (uniform bytes are
     # uniform indices and Bernoulli(0.5) sign bits); alpha is shared
@@ -149,6 +154,9 @@ def main():
     ys = [torch.empty((wl.B, m.N), dtype=torch.float32, device=dev) for m in base]
     ws = vq.alloc_workspace(base, wl.B, residual=residual, device=dev)
     call = vq.vq_gemv_residual if residual else vq.vq_gemv
+    if tokens:
+        def call(lay, xs_, B_, ys_, ws_, n_, stream=None):
+            vq.vq_gemv_tokens(lay, xs_, B_, ys_, stream=stream)
     if wl.gated_pairs:
         # gate/up pairs share the gate's x and write one gated output per pair
         def call(lay, xs_, B_, ys_, ws_, n_, stream=None):

@@ -279,6 +279,26 @@ int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
                    const uint16_t *const *x, int32_t B, float *const *y,
                    void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Several tokens per call at (d, nbits) = (4, 8) on the matrix cores:
+ * y[m][b][r] = sum_j x[m][b][4j..4j+3] . WC[WI[r][j]] for 1 <= B <= 16, the
+ * same product as vq_gemv [EVA 2.A: the output codebook OC = X WC^T and the
+ * sum of OC entries picked by the weight indices, here formed entry by entry
+ * from the codebook in LDS].  Each looked-up entry serves all B tokens, so a
+ * call of B tokens streams the indices once.  Unlike vq_gemv, m[i].wi is the
+ * CANONICAL index matrix (one byte per index, row r's K/4 indices at
+ * wi + r * K/4, as vq_pack_indices writes it with nbits = 8), not the
+ * vq_repack_wi layout: the matrix-core operand wants a lane per row, and a
+ * canonical row gives each lane 16 consecutive indices.  x[m] is fp16
+ * [B][K] (16-byte aligned), y[m] fp32 [B][N] (overwritten).  No workspace.
+ * Requires K % 256 == 0, N * K/4 < 2^31 and B * K * 2 < 2^31
+ * (VQ_EUNSUPPORTED otherwise, also for other formats or B > 16; B < 1 is
+ * VQ_EINVAL).  The sums of a matrix are formed in the same order alone or in
+ * a group, and run to run.
+ */
+int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                   float *const *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

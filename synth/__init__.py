@@ -101,6 +101,8 @@ WORKLOADS = {
     9: Workload(9, "LLaMA-7B MLP gate and up, SiLU gating fused, 2 bits/weight",
                 4, 8, 1, [MatrixSpec("gate", 4096, 11008), MatrixSpec("up", 4096, 11008)],
                 gated_pairs=True),
+    10: Workload(10, "LLaMA-7B attention projections q/k/v/o, 16 tokens, 2 bits/weight",
+                 4, 8, 16, list(_LLAMA7B_ATTN)),
 }
 
 

@@ -126,6 +126,26 @@ def test_gemv_swiglu_validation_errors():
              None) == vq.VQ_EUNSUPPORTED
 
 
+def test_gemv_tokens_validation_errors():
+    c = vq._c["vq_gemv_tokens"]
+    arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)
+    ptrs = lambda n, v=FAKE: (ctypes.c_void_p * n)(*([v] * n))
+    assert c(arr([_m()]), 1, ptrs(1), 0, ptrs(1), None) == vq.VQ_EINVAL            # no token
+    assert c(arr([_m()]), 1, ptrs(1), 17, ptrs(1), None) == vq.VQ_EUNSUPPORTED      # at most 16
+    assert c(None, 1, ptrs(1), 4, ptrs(1), None) == vq.VQ_EINVAL
+    assert c(arr([_m()]), 0, ptrs(1), 4, ptrs(1), None) == vq.VQ_EINVAL
+    assert c(arr([_m()] * 17), 17, ptrs(17), 4, ptrs(17), None) == vq.VQ_EINVAL
+    assert c(arr([_m(d=4, nbits=12)]), 1, ptrs(1), 4, ptrs(1), None) == vq.VQ_EUNSUPPORTED
+    assert c(arr([_m(d=8, nbits=16)]), 1, ptrs(1), 4, ptrs(1), None) == vq.VQ_EUNSUPPORTED
+    assert c(arr([_m(K=1088)]), 1, ptrs(1), 4, ptrs(1), None) == vq.VQ_EUNSUPPORTED   # K % 256
+    # indices of 2 GiB or more: past 32-bit buffer offsets
+    assert c(arr([_m(K=65536, N=131072)]), 1, ptrs(1), 4, ptrs(1), None) == vq.VQ_EUNSUPPORTED
+    assert c(arr([_m(wi=FAKE + 8)]), 1, ptrs(1), 4, ptrs(1), None) == vq.VQ_EALIGN
+    assert c(arr([_m()]), 1, ptrs(1, FAKE + 2), 4, ptrs(1), None) == vq.VQ_EALIGN
+    assert c(arr([_m()]), 1, ptrs(1), 4, ptrs(1, FAKE + 1), None) == vq.VQ_EALIGN
+    assert c(arr([_m(), _m(d=4, nbits=12)]), 2, ptrs(2), 4, ptrs(2), None) == vq.VQ_EUNSUPPORTED
+
+
 def test_gemv_residual_validation_errors():
     ok_x, ok_y = [FAKE], [FAKE]
     assert _gemv([_m(signs=None)], ok_x, 1, ok_y, None, 0, True) == vq.VQ_EINVAL

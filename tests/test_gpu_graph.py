@@ -39,13 +39,18 @@ def _case(kind):
     if kind == "swiglu":
         mis = [synth.small_matrix(2048, 300, 4, 8, seed=39), synth.small_matrix(2048, 300, 4, 8, seed=40)]
         return mis, 1, False
+    if kind == "tokens16":
+        return [synth.small_matrix(4096, 300, 4, 8, B=16, seed=41),
+                synth.small_matrix(1024, 77, 4, 8, B=16, seed=42)], 16, False
     if kind == "wc16":
         return [synth.small_matrix(1024, 100, 8, 16, B=4, seed=37),
                 synth.small_matrix(2048, 40, 8, 16, B=4, seed=38)], 4, False
     raise ValueError(kind)
 
 
-def _upload(mi, residual):
+def _upload(mi, residual, canonical=False):
+    if canonical:
+        return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, canonical=True, device=DEV)
     if residual:
         return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
                                 sign_bits=mi.sign_bits, alpha=mi.alpha, group=mi.group,
@@ -53,15 +58,19 @@ def _upload(mi, residual):
     return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, device=DEV)
 
 
-@pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "wc12", "wc16", "swiglu"])
+@pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "wc12", "wc16", "swiglu",
+                                  "tokens16"])
 def test_graph_replays_match_eager(kind):
     print(f"[graph] {kind}", flush=True)
     mis, B, residual = _case(kind)
-    mats = [_upload(mi, residual) for mi in mis]
+    mats = [_upload(mi, residual, canonical=kind == "tokens16") for mi in mis]
     xs = [torch.from_numpy(mi.x).to(DEV) for mi in mis]
     ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
     ws = vq.alloc_workspace(mats, B, residual=residual, device=DEV)
     call = vq.vq_gemv_residual if residual else vq.vq_gemv
+    if kind == "tokens16":
+        def call(ms, xs_, B_, ys_, ws_, n_, stream=None):
+            vq.vq_gemv_tokens(ms, xs_, B_, ys_, stream=stream)
     if kind == "swiglu":
         def call(ms, xs_, B_, ys_, ws_, n_, stream=None):
             vq.vq_gemv_swiglu(ms[0::2], ms[1::2], xs_[0::2], B_, ys_[0::2], ws_, n_, stream=stream)

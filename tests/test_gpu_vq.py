@@ -341,6 +341,62 @@ def test_gemv_workload8_four_tokens_sampled():
         _assert_close(y[:, rows], ref, f"workload 8 matrix {m}")
 
 
+def _upload_canonical(mi):
+    return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, canonical=True, device=DEV)
+
+
+def _run_tokens(mats, xs, B):
+    ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
+    xt = [torch.from_numpy(x).to(DEV) for x in xs]
+    vq.vq_gemv_tokens(mats, xt, B, ys)
+    torch.cuda.synchronize()
+    return [y.cpu().numpy() for y in ys]
+
+
+@pytest.mark.parametrize("K,N,B", [(256, 1, 16), (256, 17, 5), (512, 4103, 3), (1024, 333, 16),
+                                   (2048, 64, 1), (4096, 700, 8), (4096, 1000, 13),
+                                   (11008, 100, 16), (16384, 48, 16)])
+def test_gemv_tokens_shapes(K, N, B):
+    # 1 to 16 tokens on the matrix cores from canonical index rows: every
+    # token within tolerance; ragged row tails, one to 256 columns of 64
+    # subvectors per row; bitwise equal alone and grouped
+    _say(f"gemv_tokens K={K} N={N} B={B}")
+    mi = synth.small_matrix(K, N, 4, 8, B=B, seed=K + 3 * N + B)
+    other = synth.small_matrix(2048, 1500, 4, 8, B=B, seed=98)
+    mats = [_upload_canonical(mi), _upload_canonical(other)]
+    ys = _run_tokens(mats, [mi.x, other.x], B)
+    _assert_close(ys[0], _oracle_plain(mi), f"tokens K={K} N={N} B={B}")
+    _assert_close(ys[1], _oracle_plain(other), f"tokens grouped companion B={B}")
+    (y1,) = _run_tokens(mats[:1], [mi.x], B)
+    assert np.array_equal(y1.view(np.uint32), ys[0].view(np.uint32))
+
+
+def test_gemv_tokens_agrees_with_plain_call():
+    # the same 4-token product through both 8-bit entry points, each within
+    # tolerance of the oracle and of the other
+    _say("gemv_tokens against vq_gemv, 4 tokens")
+    mi = synth.small_matrix(4096, 2000, 4, 8, B=4, seed=4242)
+    (yt,) = _run_tokens([_upload_canonical(mi)], [mi.x], 4)
+    (yp,), _ = _run_gemv([_upload(mi)], [mi.x], B=4)
+    ref = _oracle_plain(mi)
+    _assert_close(yt, ref, "tokens call")
+    _assert_close(yp, ref, "plain call")
+    _assert_close(yt, yp.astype(np.float64), "tokens against plain")
+
+
+def test_gemv_workload10_sixteen_tokens_sampled():
+    # LLaMA-7B q/k/v/o for 16 tokens in one launch, in the launch bench.py times
+    _say("gemv_tokens workload 10 (4 x 4096x4096, 16 tokens, one launch)")
+    w = synth.workload(10)
+    mis = [synth.matrix_inputs(10, m) for m in range(w.count)]
+    ys = _run_tokens([_upload_canonical(mi) for mi in mis], [mi.x for mi in mis], 16)
+    rng = np.random.default_rng(10)
+    for m, (mi, y) in enumerate(zip(mis, ys)):
+        rows = np.sort(rng.choice(mi.N, size=256, replace=False))
+        ref = oracle.vq_gemv(mi.x, mi.wc, oracle.pack_rows(mi.idx[rows], 8), rows.size, mi.K, 4, 8)
+        _assert_close(y[:, rows], ref, f"workload 10 matrix {m}")
+
+
 @pytest.mark.parametrize("K,N,B,pairs", [(256, 17, 1, 1), (1024, 333, 2, 2), (4096, 700, 1, 3),
                                          (2048, 768, 2, 4), (8192, 77, 1, 1)])
 def test_gemv_swiglu_pairs(K, N, B, pairs):

@@ -66,3 +66,4 @@ def test_weight_bytes_per_layer():
     assert synth.workload(6).count == 16 and synth.workload(7).count == 8
     assert synth.weight_bytes(8) == synth.weight_bytes(2) and synth.workload(8).B == 4
     assert synth.weight_bytes(9) == 2 * (11008 * 1024 + 2048) and synth.workload(9).gated_pairs
+    assert synth.weight_bytes(10) == synth.weight_bytes(2) and synth.workload(10).B == 16

@@ -77,6 +77,9 @@ _c = {
                               ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "vq_gemv_swiglu": _sig("vq_gemv_swiglu", ctypes.c_int,
                            [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "vq_gemv_tokens": _sig("vq_gemv_tokens", ctypes.c_int,
+                           [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
+                            ctypes.POINTER(_vp), _vp]),
 }
 
 # every symbol the header declares (checked by the ABI test)
@@ -242,6 +245,12 @@ def vq_gemv_swiglu(gates: Sequence, ups: Sequence, xs: Sequence, B: int, ys: Seq
            "vq_gemv_swiglu")
 
 
+def vq_gemv_tokens(mats: Sequence, xs: Sequence, B: int, ys: Sequence, stream=None) -> None:
+    """vq_gemv for 1-16 tokens at d=4, n=8; each mats[i].wi holds canonical index rows."""
+    _check(_c["vq_gemv_tokens"](_mat_array(mats), len(mats), _ptr_array(xs), B, _ptr_array(ys),
+                                _stream(stream)), "vq_gemv_tokens")
+
+
 # ------------------------------------------------------------------ helpers
 def alloc_workspace(mats: Sequence, B: int, residual: bool = False, device="cuda"):
     """Allocate (torch) and initialize a workspace for these matrices."""
@@ -255,13 +264,14 @@ def alloc_workspace(mats: Sequence, B: int, residual: bool = False, device="cuda
 
 
 def upload_matrix(idx, wc, K: int, N: int, d: int, nbits: int, *, sign_bits=None, alpha=None,
-                  group: int = 128, rht_sign=None, had_block: int = 0, device="cuda",
-                  stream=None) -> DeviceMatrix:
+                  group: int = 128, rht_sign=None, had_block: int = 0, canonical: bool = False,
+                  device="cuda", stream=None) -> DeviceMatrix:
     """Copy host inputs to the device and build the device layouts with the
     library's pack and repack kernels.
 
     idx: integer array [N][K/d]; wc: fp16 [2^n][d]; sign_bits: {0,1} [N][K];
-    alpha: fp16 [N][K/group]; rht_sign: int8 [K].
+    alpha: fp16 [N][K/group]; rht_sign: int8 [K].  canonical: keep WI in the
+    canonical packed form (what vq_gemv_tokens reads) instead of the device layout.
     """
     import numpy as np
     import torch
@@ -269,8 +279,11 @@ def upload_matrix(idx, wc, K: int, N: int, d: int, nbits: int, *, sign_bits=None
     idx_t = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.uint32).view(np.int32)).to(device)
     canon = torch.empty((N * J * nbits + 7) // 8, dtype=torch.uint8, device=device)
     vq_pack_indices(idx_t, N * J, nbits, canon, stream)
-    wi = torch.empty(vq_wi_device_bytes(N, K, d, nbits), dtype=torch.uint8, device=device)
-    vq_repack_wi(canon, N, K, d, nbits, wi, stream)
+    if canonical:
+        wi = canon
+    else:
+        wi = torch.empty(vq_wi_device_bytes(N, K, d, nbits), dtype=torch.uint8, device=device)
+        vq_repack_wi(canon, N, K, d, nbits, wi, stream)
     wc_t = torch.from_numpy(np.ascontiguousarray(wc, dtype=np.float16)).to(device)
     m = DeviceMatrix(K, N, d, nbits, wi, wc_t)
     if sign_bits is not None:

@@ -554,4 +554,52 @@ int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
   return hip_status(launch_wc8_swiglu(args, (int)max_wg, waves, B, stream));
 }
 
+int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                   float *const *y, void *stream) {
+  if (B < 1) return VQ_EINVAL;
+  int st = check_group(m, count, x, 1, y, false);
+  if (st != VQ_OK) return st;
+  if (format_of(m[0]) != FMT_LUT8 || B > 16) return VQ_EUNSUPPORTED;
+  for (int i = 0; i < count; ++i) {
+    // 32-bit buffer offsets: the index rows and x below 2^31 bytes
+    if ((int64_t)m[i].N * (m[i].K / 4) >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
+    if ((int64_t)B * m[i].K * 2 >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
+  }
+  WcArgs args;
+  memset(&args, 0, sizeof(args));
+  args.count = count;
+  for (int i = 0; i < count; ++i) {
+    WcMat &d = args.mat[i];
+    d.wi = static_cast<const uint8_t *>(m[i].wi);
+    d.wc = m[i].wc;
+    d.x = x[i];
+    d.y = y[i];
+    d.J = m[i].K / 4;
+    d.N = m[i].N;
+    d.B = B;
+    d.ldy = m[i].N;
+    d.jsplit = wc8t_jsplit(d.J);
+  }
+  // row groups per wave: the most (4, 2, 1) that still gives the call 256
+  // workgroups; it changes which wave adds a row, not the order of its sums
+  int rw = 4;
+  for (; rw > 1; rw /= 2) {
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i) {
+      const int R = wc8t_rows_per_wg(args.mat[i].jsplit, rw);
+      wgs += (args.mat[i].N + R - 1) / R;
+    }
+    if (wgs >= kResidentWorkgroups) break;
+  }
+  int64_t max_wg = 0;
+  for (int i = 0; i < count; ++i) {
+    WcMat &d = args.mat[i];
+    const int R = wc8t_rows_per_wg(d.jsplit, rw);
+    d.nwg = (d.N + R - 1) / R;
+    if (d.nwg > max_wg) max_wg = d.nwg;
+  }
+  if (max_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
+  return hip_status(launch_wc8t(args, (int)max_wg, rw, stream));
+}
+
 }  // extern "C"

@@ -164,8 +164,10 @@ __global__ void __launch_bounds__(W * 64) wc8t_kernel(const WcArgs args) {
   f32x4_t acc[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  wc8t_exchange(xa);
   for (int k = kbeg; k < kend; ++k) {
+    // this column's x (requested one column earlier) to the product order,
+    // then the next column's requests, kept ahead of the lookups
+    wc8t_exchange(xa);
     u32x4 ibn[RW], xn[8];
 #pragma unroll
     for (int r = 0; r < RW; ++r)
@@ -173,6 +175,7 @@ __global__ void __launch_bounds__(W * 64) wc8t_kernel(const WcArgs args) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       xn[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off(k + 1, q), 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
 #pragma unroll
@@ -189,7 +192,6 @@ __global__ void __launch_bounds__(W * 64) wc8t_kernel(const WcArgs args) {
     }
 #pragma unroll
     for (int r = 0; r < RW; ++r) ib[r] = ibn[r];
-    wc8t_exchange(xn);
 #pragma unroll
     for (int q = 0; q < 8; ++q) xa[q] = xn[q];
   }

@@ -116,7 +116,7 @@ def main():
     torch.cuda.set_device(dev)
     wl = synth.workload(args.workload)
     residual = wl.residual
-    # more than 4 tokens at d=4, n=8: the matrix-core call, on canonical index rows
+    # more than 4 tokens at d=4, n=8: the matrix-core call, on the row-tile index layout
     tokens = (wl.d, wl.nbits) == (4, 8) and wl.B > 4
     layer_bytes = synth.weight_bytes(args.workload)
     copies = args.copies or max(1, -(-(2 << 30) // layer_bytes))
@@ -132,7 +132,7 @@ def main():
                                          rht_sign=mi.rht_sign, had_block=mi.had_block, device=dev))
         else:
             base.append(vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
-                                         canonical=tokens, device=dev))
+                                         tokens=tokens, device=dev))
     xs = [torch.from_numpy(mi.x).to(dev) for mi in mis]
     # further copies: seeded uniform random bytes in the device layouts (uniform bytes are
     # uniform indices and Bernoulli(0.5) sign bits); alpha is shared

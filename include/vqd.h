@@ -285,19 +285,32 @@ int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
  * same product as vq_gemv [EVA 2.A: the output codebook OC = X WC^T and the
  * sum of OC entries picked by the weight indices, here formed entry by entry
  * from the codebook in LDS].  Each looked-up entry serves all B tokens, so a
- * call of B tokens streams the indices once.  Unlike vq_gemv, m[i].wi is the
- * CANONICAL index matrix (one byte per index, row r's K/4 indices at
- * wi + r * K/4, as vq_pack_indices writes it with nbits = 8), not the
- * vq_repack_wi layout: the matrix-core operand wants a lane per row, and a
- * canonical row gives each lane 16 consecutive indices.  x[m] is fp16
+ * call of B tokens streams the indices once.  Unlike vq_gemv, m[i].wi is in
+ * the ROW-TILE layout written by vq_repack_wi_rows, not the vq_repack_wi
+ * layout: the matrix-core operand wants a lane per row.  x[m] is fp16
  * [B][K] (16-byte aligned), y[m] fp32 [B][N] (overwritten).  No workspace.
- * Requires K % 256 == 0, N * K/4 < 2^31 and B * K * 2 < 2^31
+ * Requires K % 256 == 0, ceil(N/16) * 16 * K/4 < 2^31 and B * K * 2 < 2^31
  * (VQ_EUNSUPPORTED otherwise, also for other formats or B > 16; B < 1 is
  * VQ_EINVAL).  The sums of a matrix are formed in the same order alone or in
  * a group, and run to run.
  */
 int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                    float *const *y, void *stream);
+
+/*
+ * Row-tile layout of 8-bit indices for vq_gemv_tokens [EVA 2.B: indices
+ * stream in tiles], from the canonical form (one byte per index, row r's K/4
+ * indices at canonical + r * K/4, as vq_pack_indices writes it with
+ * nbits = 8).  Chunk (column t of 64 subvectors, row group g of 16 rows) is
+ * 1 KiB at byte (t * ceil(N/16) + g) * 1024; its 16 bytes at 16 l hold the
+ * indices of row 16 g + l % 16 at subvectors 64 t + 16 (l / 16) + i, i < 16;
+ * rows past N are zero.  The layout is vq_wi_device_bytes(N, K, 4, 8) bytes.
+ * Load-time, asynchronous on `stream`.  Requires K % 256 == 0 and
+ * ceil(N/16) * 16 * K/4 < 2^31 (VQ_EUNSUPPORTED); both pointers 16-byte
+ * aligned (VQ_EALIGN).
+ */
+int vq_repack_wi_rows(const uint8_t *canonical, int32_t N, int32_t K, void *device_layout,
+                      void *stream);
 
 #ifdef __cplusplus
 }

@@ -172,6 +172,12 @@ def test_other_entry_points_validate():
     assert c["vq_unpack_indices"](FAKE, 5, 8, FAKE + 2, None) == vq.VQ_EALIGN
     assert c["vq_repack_wi"](FAKE, 64, 1000, 4, 8, FAKE, None) == vq.VQ_EUNSUPPORTED
     assert c["vq_repack_wi"](FAKE, 64, 1024, 4, 8, FAKE + 4, None) == vq.VQ_EALIGN
+    assert c["vq_repack_wi_rows"](None, 64, 1024, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_repack_wi_rows"](FAKE, 0, 1024, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_repack_wi_rows"](FAKE, 64, 1000, FAKE, None) == vq.VQ_EUNSUPPORTED   # K % 256
+    assert c["vq_repack_wi_rows"](FAKE, 131072, 65536, FAKE, None) == vq.VQ_EUNSUPPORTED
+    assert c["vq_repack_wi_rows"](FAKE + 8, 64, 1024, FAKE, None) == vq.VQ_EALIGN
+    assert c["vq_repack_wi_rows"](FAKE, 64, 1024, FAKE + 4, None) == vq.VQ_EALIGN
     assert c["vq_repack_signs"](FAKE, 64, 1000, FAKE, None) == vq.VQ_EUNSUPPORTED
     assert c["vq_repack_alpha"](FAKE, 64, 1024, 100, FAKE, None) == vq.VQ_EINVAL
     assert c["vq_build_oc"](FAKE, 1, 10, 4, 8, FAKE, FAKE, vq.VQ_F32, None) == vq.VQ_EINVAL

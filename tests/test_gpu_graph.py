@@ -48,9 +48,9 @@ def _case(kind):
     raise ValueError(kind)
 
 
-def _upload(mi, residual, canonical=False):
-    if canonical:
-        return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, canonical=True, device=DEV)
+def _upload(mi, residual, tokens=False):
+    if tokens:
+        return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, tokens=True, device=DEV)
     if residual:
         return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
                                 sign_bits=mi.sign_bits, alpha=mi.alpha, group=mi.group,
@@ -63,7 +63,7 @@ def _upload(mi, residual, canonical=False):
 def test_graph_replays_match_eager(kind):
     print(f"[graph] {kind}", flush=True)
     mis, B, residual = _case(kind)
-    mats = [_upload(mi, residual, canonical=kind == "tokens16") for mi in mis]
+    mats = [_upload(mi, residual, tokens=kind == "tokens16") for mi in mis]
     xs = [torch.from_numpy(mi.x).to(DEV) for mi in mis]
     ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
     ws = vq.alloc_workspace(mats, B, residual=residual, device=DEV)

@@ -341,8 +341,27 @@ def test_gemv_workload8_four_tokens_sampled():
         _assert_close(y[:, rows], ref, f"workload 8 matrix {m}")
 
 
-def _upload_canonical(mi):
-    return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, canonical=True, device=DEV)
+def _upload_rows(mi):
+    return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, tokens=True, device=DEV)
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (17, 256), (1000, 1024), (4103, 512), (48, 16384)])
+def test_repack_rows_bitexact(N, K):
+    # row tiles against a host construction from the canonical indices
+    _say(f"repack rows N={N} K={K}")
+    rng = np.random.default_rng(N * 31 + K)
+    J = K // 4
+    idx = rng.integers(0, 256, size=(N, J), dtype=np.uint8)
+    canon = torch.from_numpy(oracle.pack_rows(idx, 8)).to(DEV)
+    dev = torch.full((vq.vq_wi_device_bytes(N, K, 4, 8),), 0xA5, dtype=torch.uint8, device=DEV)
+    vq.vq_repack_wi_rows(canon, N, K, dev)
+    torch.cuda.synchronize()
+    NG = (N + 15) // 16
+    pad = np.zeros((NG * 16, J), dtype=np.uint8)
+    pad[:N] = idx
+    # [column k][row group][lane l = 16 (l // 16) + l % 16 ... ] -> row 16 rg + l % 16, bytes 16 (l // 16)
+    ref = pad.reshape(NG, 16, J // 64, 4, 16).transpose(2, 0, 3, 1, 4).reshape(-1)
+    assert np.array_equal(dev.cpu().numpy(), ref)
 
 
 def _run_tokens(mats, xs, B):
@@ -357,13 +376,13 @@ def _run_tokens(mats, xs, B):
                                    (2048, 64, 1), (4096, 700, 8), (4096, 1000, 13),
                                    (11008, 100, 16), (16384, 48, 16)])
 def test_gemv_tokens_shapes(K, N, B):
-    # 1 to 16 tokens on the matrix cores from canonical index rows: every
+    # 1 to 16 tokens on the matrix cores from row tiles: every
     # token within tolerance; ragged row tails, one to 256 columns of 64
     # subvectors per row; bitwise equal alone and grouped
     _say(f"gemv_tokens K={K} N={N} B={B}")
     mi = synth.small_matrix(K, N, 4, 8, B=B, seed=K + 3 * N + B)
     other = synth.small_matrix(2048, 1500, 4, 8, B=B, seed=98)
-    mats = [_upload_canonical(mi), _upload_canonical(other)]
+    mats = [_upload_rows(mi), _upload_rows(other)]
     ys = _run_tokens(mats, [mi.x, other.x], B)
     _assert_close(ys[0], _oracle_plain(mi), f"tokens K={K} N={N} B={B}")
     _assert_close(ys[1], _oracle_plain(other), f"tokens grouped companion B={B}")
@@ -376,7 +395,7 @@ def test_gemv_tokens_agrees_with_plain_call():
     # tolerance of the oracle and of the other
     _say("gemv_tokens against vq_gemv, 4 tokens")
     mi = synth.small_matrix(4096, 2000, 4, 8, B=4, seed=4242)
-    (yt,) = _run_tokens([_upload_canonical(mi)], [mi.x], 4)
+    (yt,) = _run_tokens([_upload_rows(mi)], [mi.x], 4)
     (yp,), _ = _run_gemv([_upload(mi)], [mi.x], B=4)
     ref = _oracle_plain(mi)
     _assert_close(yt, ref, "tokens call")
@@ -389,7 +408,7 @@ def test_gemv_workload10_sixteen_tokens_sampled():
     _say("gemv_tokens workload 10 (4 x 4096x4096, 16 tokens, one launch)")
     w = synth.workload(10)
     mis = [synth.matrix_inputs(10, m) for m in range(w.count)]
-    ys = _run_tokens([_upload_canonical(mi) for mi in mis], [mi.x for mi in mis], 16)
+    ys = _run_tokens([_upload_rows(mi) for mi in mis], [mi.x for mi in mis], 16)
     rng = np.random.default_rng(10)
     for m, (mi, y) in enumerate(zip(mis, ys)):
         rows = np.sort(rng.choice(mi.N, size=256, replace=False))

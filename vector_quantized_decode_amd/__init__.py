@@ -64,6 +64,7 @@ _c = {
     "vq_pack_indices": _sig("vq_pack_indices", ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
     "vq_unpack_indices": _sig("vq_unpack_indices", ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
     "vq_repack_wi": _sig("vq_repack_wi", ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "vq_repack_wi_rows": _sig("vq_repack_wi_rows", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "vq_repack_signs": _sig("vq_repack_signs", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "vq_repack_alpha": _sig("vq_repack_alpha", ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "vq_build_oc": _sig("vq_build_oc", ctypes.c_int,
@@ -152,6 +153,11 @@ def vq_unpack_indices(packed, count: int, nbits: int, out, stream=None) -> None:
 def vq_repack_wi(canonical, N: int, K: int, d: int, nbits: int, device_layout, stream=None) -> None:
     _check(_c["vq_repack_wi"](_ptr(canonical), N, K, d, nbits, _ptr(device_layout),
                               _stream(stream)), "vq_repack_wi")
+
+
+def vq_repack_wi_rows(canonical, N: int, K: int, device_layout, stream=None) -> None:
+    _check(_c["vq_repack_wi_rows"](_ptr(canonical), N, K, _ptr(device_layout), _stream(stream)),
+           "vq_repack_wi_rows")
 
 
 def vq_repack_signs(canonical, N: int, K: int, device_layout, stream=None) -> None:
@@ -246,7 +252,7 @@ def vq_gemv_swiglu(gates: Sequence, ups: Sequence, xs: Sequence, B: int, ys: Seq
 
 
 def vq_gemv_tokens(mats: Sequence, xs: Sequence, B: int, ys: Sequence, stream=None) -> None:
-    """vq_gemv for 1-16 tokens at d=4, n=8; each mats[i].wi holds canonical index rows."""
+    """vq_gemv for 1-16 tokens at d=4, n=8; each mats[i].wi holds row tiles (vq_repack_wi_rows)."""
     _check(_c["vq_gemv_tokens"](_mat_array(mats), len(mats), _ptr_array(xs), B, _ptr_array(ys),
                                 _stream(stream)), "vq_gemv_tokens")
 
@@ -264,14 +270,14 @@ def alloc_workspace(mats: Sequence, B: int, residual: bool = False, device="cuda
 
 
 def upload_matrix(idx, wc, K: int, N: int, d: int, nbits: int, *, sign_bits=None, alpha=None,
-                  group: int = 128, rht_sign=None, had_block: int = 0, canonical: bool = False,
+                  group: int = 128, rht_sign=None, had_block: int = 0, tokens: bool = False,
                   device="cuda", stream=None) -> DeviceMatrix:
     """Copy host inputs to the device and build the device layouts with the
     library's pack and repack kernels.
 
     idx: integer array [N][K/d]; wc: fp16 [2^n][d]; sign_bits: {0,1} [N][K];
-    alpha: fp16 [N][K/group]; rht_sign: int8 [K].  canonical: keep WI in the
-    canonical packed form (what vq_gemv_tokens reads) instead of the device layout.
+    alpha: fp16 [N][K/group]; rht_sign: int8 [K].  tokens: lay WI out in row
+    tiles (vq_repack_wi_rows, what vq_gemv_tokens reads) instead of vq_repack_wi's layout.
     """
     import numpy as np
     import torch
@@ -279,8 +285,9 @@ def upload_matrix(idx, wc, K: int, N: int, d: int, nbits: int, *, sign_bits=None
     idx_t = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.uint32).view(np.int32)).to(device)
     canon = torch.empty((N * J * nbits + 7) // 8, dtype=torch.uint8, device=device)
     vq_pack_indices(idx_t, N * J, nbits, canon, stream)
-    if canonical:
-        wi = canon
+    if tokens:
+        wi = torch.empty(vq_wi_device_bytes(N, K, d, nbits), dtype=torch.uint8, device=device)
+        vq_repack_wi_rows(canon, N, K, wi, stream)
     else:
         wi = torch.empty(vq_wi_device_bytes(N, K, d, nbits), dtype=torch.uint8, device=device)
         vq_repack_wi(canon, N, K, d, nbits, wi, stream)

@@ -447,6 +447,14 @@ int vq_repack_wi(const uint8_t *canonical, int32_t N, int32_t K, int32_t d, int3
   }
 }
 
+int vq_repack_wi_rows(const uint8_t *canonical, int32_t N, int32_t K, void *device_layout, void *stream) {
+  if (!canonical || !device_layout || N <= 0 || K <= 0) return VQ_EINVAL;
+  if (K % 256) return VQ_EUNSUPPORTED;
+  if ((int64_t)(N + 15) / 16 * 16 * (K / 4) >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
+  if (!aligned(canonical, 16) || !aligned(device_layout, 16)) return VQ_EALIGN;
+  return hip_status(launch_repack_wi8_rows(canonical, N, K / 4, static_cast<uint8_t *>(device_layout), stream));
+}
+
 int vq_repack_signs(const uint8_t *canonical, int32_t N, int32_t K, void *device_layout, void *stream) {
   if (!canonical || !device_layout || N <= 0 || K <= 0 || K % 8) return VQ_EINVAL;
   if (vq_signs_device_bytes(N, K) == 0) return VQ_EUNSUPPORTED;
@@ -561,8 +569,8 @@ int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
   if (st != VQ_OK) return st;
   if (format_of(m[0]) != FMT_LUT8 || B > 16) return VQ_EUNSUPPORTED;
   for (int i = 0; i < count; ++i) {
-    // 32-bit buffer offsets: the index rows and x below 2^31 bytes
-    if ((int64_t)m[i].N * (m[i].K / 4) >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
+    // 32-bit buffer offsets: the row tiles and x below 2^31 bytes
+    if ((int64_t)(m[i].N + 15) / 16 * 16 * (m[i].K / 4) >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
     if ((int64_t)B * m[i].K * 2 >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
   }
   WcArgs args;

@@ -45,7 +45,7 @@ struct Lut8Args {
 
 // Per-matrix descriptor of the virtual-OC kernels (n = 12 and n = 16).
 struct WcMat {
-  const uint8_t *wi;      // WI: device layout tile-16x64(-12) or tile-16x32-16, or canonical rows
+  const uint8_t *wi;      // WI: device layout tile-16x64(-12), tile-16x32-16 or row tiles
   const uint16_t *wc;     // fp16 codebook [2^n][d]
   const uint16_t *x;      // fp16 input [B][K]
   float *y;               // fp32 output [B][N], row stride ldy
@@ -91,6 +91,7 @@ int launch_wc8_swiglu(const WcPairArgs &a, int grid_x, int waves, int B, void *s
 int wc8t_jsplit(int J);
 int wc8t_rows_per_wg(int jsplit, int rw);
 int launch_wc8t(const WcArgs &a, int grid_x, int rw, void *stream);
+int launch_repack_wi8_rows(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
 int wc16t_jsplit(int J);
 int wc16t_rows_per_wg(int jsplit);
 bool wc16t_fits(int N, int J, int jsplit);

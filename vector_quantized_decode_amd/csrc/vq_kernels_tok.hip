@@ -56,9 +56,10 @@ __device__ __forceinline__ WcMat load_mat(const WcArgs &args) {
 // so 16 rows x 16 tokens x 8 subvectors (32 weights) form one
 // v_mfma_f32_16x16x32_f16: x's tokens as A, the rows' looked-up entries as
 // B.  B wants a lane per row -- lane l serves row l % 16 and subvectors
-// 16 (l / 16) + q, q < 16, of a 64-subvector column -- and in the canonical
-// index matrix ([N][K/4] bytes) those are 16 consecutive bytes, so this
-// kernel reads WI in that form.  The codebook sits in LDS in 32 copies
+// 16 (l / 16) + q, q < 16, of a 64-subvector column -- so WI is laid out
+// in row tiles: chunk (column k, row group rg) is 1 KiB, and its 16 bytes at
+// 16 l are those 16 indices of lane l (consecutive bytes of the canonical
+// row), so a wave's chunk is one contiguous 1 KiB read.  The codebook sits in LDS in 32 copies
 // (entry c, copy k at byte 256 c + 8 k) and lane l reads copy l % 32: the 32
 // lanes of one LDS read pass reach 32 different bank pairs whatever the
 // indices are ([EVA] 2.A).  A wave owns RW row groups and one segment of the
@@ -124,15 +125,17 @@ __global__ void __launch_bounds__(W * 64) wc8t_kernel(const WcArgs args) {
   const int seg = (JT + S - 1) >> lS;
   const int kbeg = min(sg * seg, JT), kend = min(kbeg + seg, JT);
   const int m16 = lane & 15, g = lane >> 4;
+  const int NG = (M.N + 15) >> 4;
   const __amdgpu_buffer_rsrc_t rwi = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(M.wi), (short)0, M.N * M.J, kBufferWord3);
+      const_cast<uint8_t *>(M.wi), (short)0, NG * 16 * M.J, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(M.x), (short)0, M.B * M.J * 8, kBufferWord3);
-  // rows past N, columns past the segment and tokens past B read zeros
+  // row groups past the matrix, columns past the segment and tokens past B
+  // read zeros (rows past N within the last group are zero in the layout)
   auto wi_off = [&](int r, int k) -> uint32_t {
-    const int row = (rg0 + r) * 16 + m16;
-    return (k < kend && row < M.N) ? (uint32_t)row * (uint32_t)M.J + (uint32_t)(k * 64 + g * 16)
-                                   : kOutOfRange;
+    const int rg = rg0 + r;
+    return (k < kend && rg < NG) ? ((uint32_t)k * (uint32_t)NG + (uint32_t)rg) * 1024u + (uint32_t)lane * 16u
+                                 : kOutOfRange;
   };
   auto x_off = [&](int k, int i) -> uint32_t {
     return (k < kend && m16 < M.B)
@@ -224,6 +227,25 @@ __global__ void __launch_bounds__(W * 64) wc8t_kernel(const WcArgs args) {
   }
 }
 
+// canonical 8-bit rows ([N][J] bytes) -> row tiles: chunk (column k, row
+// group rg) at (k NG + rg) KiB, its 16 bytes at 16 l = row 16 rg + l % 16,
+// subvectors 64 k + 16 (l / 16) .. + 15 (zeros for rows past N)
+__global__ void repack_wi8_rows_kernel(const uint8_t *canon, int N, int J, uint8_t *dev) {
+  const int NG = (N + 15) >> 4;
+  const int64_t total = (int64_t)(J >> 6) * NG * 64;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(e & 63);
+    const int64_t chunk = e >> 6;
+    const int rg = (int)(chunk % NG);
+    const int k = (int)(chunk / NG);
+    const int row = rg * 16 + (l & 15);
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (row < N) v = *reinterpret_cast<const u32x4 *>(canon + (size_t)row * J + k * 64 + (l >> 4) * 16);
+    *reinterpret_cast<u32x4 *>(dev + e * 16) = v;
+  }
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------
@@ -240,6 +262,17 @@ int wc8t_jsplit(int J) {
   return s;
 }
 int wc8t_rows_per_wg(int jsplit, int rw) { return TK_W / jsplit * rw * 16; }
+int launch_repack_wi8_rows(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream) {
+  const int64_t total = (int64_t)(J >> 6) * ((N + 15) >> 4) * 64;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65536) blocks = 65536;
+  (void)hipGetLastError();  // report only this launch's error
+  hipLaunchKernelGGL(repack_wi8_rows_kernel, dim3((int)blocks), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), canon, N, J, dev);
+  return (int)hipGetLastError();
+}
+
 int launch_wc8t(const WcArgs &a, int grid_x, int rw, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error

@@ -42,6 +42,9 @@ def _case(kind):
     if kind == "tokens16":
         return [synth.small_matrix(4096, 300, 4, 8, B=16, seed=41),
                 synth.small_matrix(1024, 77, 4, 8, B=16, seed=42)], 16, False
+    if kind == "tokens5":
+        return [synth.small_matrix(4096, 300, 4, 8, B=5, seed=43),
+                synth.small_matrix(1024, 77, 4, 8, B=5, seed=44)], 5, False
     if kind == "wc16":
         return [synth.small_matrix(1024, 100, 8, 16, B=4, seed=37),
                 synth.small_matrix(2048, 40, 8, 16, B=4, seed=38)], 4, False
@@ -59,16 +62,16 @@ def _upload(mi, residual, tokens=False):
 
 
 @pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "wc12", "wc16", "swiglu",
-                                  "tokens16"])
+                                  "tokens16", "tokens5"])
 def test_graph_replays_match_eager(kind):
     print(f"[graph] {kind}", flush=True)
     mis, B, residual = _case(kind)
-    mats = [_upload(mi, residual, tokens=kind == "tokens16") for mi in mis]
+    mats = [_upload(mi, residual, tokens=kind.startswith("tokens")) for mi in mis]
     xs = [torch.from_numpy(mi.x).to(DEV) for mi in mis]
     ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
     ws = vq.alloc_workspace(mats, B, residual=residual, device=DEV)
     call = vq.vq_gemv_residual if residual else vq.vq_gemv
-    if kind == "tokens16":
+    if kind.startswith("tokens"):
         def call(ms, xs_, B_, ys_, ws_, n_, stream=None):
             vq.vq_gemv_tokens(ms, xs_, B_, ys_, stream=stream)
     if kind == "swiglu":

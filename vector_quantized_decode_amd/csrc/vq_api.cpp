@@ -586,11 +586,12 @@ int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     d.N = m[i].N;
     d.B = B;
     d.ldy = m[i].N;
-    d.jsplit = wc8t_jsplit(d.J);
+    d.jsplit = wc8t_jsplit(d.J, B);
   }
-  // row groups per wave: the most (4, 2, 1) that still gives the call 256
-  // workgroups; it changes which wave adds a row, not the order of its sums
-  int rw = 4;
+  // row groups per wave: the most (up to wc8t_max_rw(B)) that still gives
+  // the call 256 workgroups; it changes which wave adds a row, not the order
+  // of its sums
+  int rw = wc8t_max_rw(B);
   for (; rw > 1; rw /= 2) {
     int64_t wgs = 0;
     for (int i = 0; i < count; ++i) {

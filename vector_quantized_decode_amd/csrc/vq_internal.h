@@ -88,7 +88,8 @@ int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, int B, void *
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream);
 int wc8_swiglu_waves(int max_split);
 int launch_wc8_swiglu(const WcPairArgs &a, int grid_x, int waves, int B, void *stream);
-int wc8t_jsplit(int J);
+int wc8t_jsplit(int J, int B);
+int wc8t_max_rw(int B);
 int wc8t_rows_per_wg(int jsplit, int rw);
 int launch_wc8t(const WcArgs &a, int grid_x, int rw, void *stream);
 int launch_repack_wi8_rows(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);

@@ -251,14 +251,21 @@ __global__ void repack_wi8_rows_kernel(const uint8_t *canon, int N, int J, uint8
 // --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
+// Columns of 64 subvectors per wave and the most row groups per wave: more
+// tokens mean more x per column, which more row groups per wave share, and
+// shorter segments keep more waves on the rows (measured on 4 x 4096 x 4096:
+// up to 12 tokens four columns and two row groups, above that two columns
+// and four row groups).
+int wc8t_max_cols(int B) { return B > 12 ? 2 : 4; }
+int wc8t_max_rw(int B) { return B > 12 ? 4 : 2; }
 // Waves per row group along J for the token kernel: the smallest power of
-// two (at most 8) that leaves each wave at most two 64-subvector columns.  It
-// depends on the row length alone, so a matrix sums in the same order alone
-// or in a group.
-int wc8t_jsplit(int J) {
-  const int jt = J / 64;
+// two (at most 8) that leaves each wave at most wc8t_max_cols(B) columns.  It
+// depends on the row length and the token count alone, so a matrix sums in
+// the same order alone or in a group.
+int wc8t_jsplit(int J, int B) {
+  const int jt = J / 64, cols = wc8t_max_cols(B);
   int s = 1;
-  while (s < TK_W && (jt + s - 1) / s > 2) s *= 2;
+  while (s < TK_W && (jt + s - 1) / s > cols) s *= 2;
   return s;
 }
 int wc8t_rows_per_wg(int jsplit, int rw) { return TK_W / jsplit * rw * 16; }

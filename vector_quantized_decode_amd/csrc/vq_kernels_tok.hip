@@ -59,14 +59,14 @@ __device__ __forceinline__ WcMat load_mat(const WcArgs &args) {
 // 16 (l / 16) + q, q < 16, of a 64-subvector column -- so WI is laid out
 // in row tiles: chunk (column k, row group rg) is 1 KiB, and its 16 bytes at
 // 16 l are those 16 indices of lane l (consecutive bytes of the canonical
-// row), so a wave's chunk is one contiguous 1 KiB read.  The codebook sits in LDS in 32 copies
-// (entry c, copy k at byte 256 c + 8 k) and lane l reads copy l % 32: the 32
-// lanes of one LDS read pass reach 32 different bank pairs whatever the
-// indices are ([EVA] 2.A).  A wave owns RW row groups and one segment of the
-// columns (S waves per row group, added in order through LDS); a column's x
-// operands (8 KiB for the wave) are loaded once for its RW row groups, and
-// the next column's indices and x are requested before the current column's
-// lookups.
+// row), so a wave's chunk is one contiguous 1 KiB read.  The codebook sits
+// in LDS in 32 copies (entry c, copy k at byte 256 c + 8 k) and lane l reads
+// copy l % 32: the 32 lanes of one LDS read pass reach 32 different bank
+// pairs whatever the indices are ([EVA] 2.A).  A wave owns RW row groups and
+// one segment of the columns (S waves per row group, added in order through
+// LDS); a column's x operands (8 KiB for the wave at 16 tokens) are loaded
+// once for its RW row groups, and the next column's indices and x are
+// requested before the current column's lookups.
 //
 // x's operands.  Lane (m, g) (token m = l % 16, k-group g = l / 16) needs
 // block g of token m's column slice -- 128 bytes, eight 16-byte pieces, piece
@@ -256,7 +256,7 @@ __global__ void repack_wi8_rows_kernel(const uint8_t *canon, int N, int J, uint8
 // shorter segments keep more waves on the rows (measured on 4 x 4096 x 4096:
 // up to 12 tokens four columns and two row groups, above that two columns
 // and four row groups).
-int wc8t_max_cols(int B) { return B > 12 ? 2 : 4; }
+static int wc8t_max_cols(int B) { return B > 12 ? 2 : 4; }
 int wc8t_max_rw(int B) { return B > 12 ? 4 : 2; }
 // Waves per row group along J for the token kernel: the smallest power of
 // two (at most 8) that leaves each wave at most wc8t_max_cols(B) columns.  It

@@ -390,6 +390,16 @@ def test_gemv_tokens_shapes(K, N, B):
     assert np.array_equal(y1.view(np.uint32), ys[0].view(np.uint32))
 
 
+def test_gemv_tokens_moe_expert_group():
+    # 8 routed experts' gate and up matrices (16 x 2048 -> 768, MoE-shaped),
+    # each with its own codebook and its own 8 tokens, in one launch
+    _say("gemv_tokens MoE group: 16 x 2048x768, 8 tokens")
+    mis = [synth.small_matrix(2048, 768, 4, 8, B=8, seed=700 + e) for e in range(16)]
+    ys = _run_tokens([_upload_rows(mi) for mi in mis], [mi.x for mi in mis], 8)
+    for e, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _oracle_plain(mi), f"expert matrix {e}")
+
+
 def test_gemv_tokens_agrees_with_plain_call():
     # the same 4-token product through both 8-bit entry points, each within
     # tolerance of the oracle and of the other

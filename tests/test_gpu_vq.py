@@ -374,11 +374,13 @@ def _run_tokens(mats, xs, B):
 
 @pytest.mark.parametrize("K,N,B", [(256, 1, 16), (256, 17, 5), (512, 4103, 3), (1024, 333, 16),
                                    (2048, 64, 1), (4096, 700, 8), (4096, 1000, 13),
-                                   (11008, 100, 16), (16384, 48, 16)])
+                                   (11008, 100, 16), (16384, 48, 16), (65536, 40, 16),
+                                   (65536, 33, 3)])
 def test_gemv_tokens_shapes(K, N, B):
     # 1 to 16 tokens on the matrix cores from row tiles: every
     # token within tolerance; ragged row tails, one to 256 columns of 64
-    # subvectors per row; bitwise equal alone and grouped
+    # subvectors per row (K = 65536: 32 columns per wave); bitwise equal
+    # alone and grouped
     _say(f"gemv_tokens K={K} N={N} B={B}")
     mi = synth.small_matrix(K, N, 4, 8, B=B, seed=K + 3 * N + B)
     other = synth.small_matrix(2048, 1500, 4, 8, B=B, seed=98)

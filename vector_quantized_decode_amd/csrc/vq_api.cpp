@@ -28,7 +28,8 @@ static bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- shapes
-// Workgroups of the residual kernel resident at once: one per CU.
+// One workgroup per CU (256 CUs): the residual kernel's resident round, and
+// the workgroup count the token call's row-groups-per-wave rule aims for.
 static constexpr int64_t kResidentWorkgroups = 256;
 
 // Row pairs per workgroup of a matrix with np pairs for a target run of T:

@@ -248,6 +248,20 @@ int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x,
             void *stream);
 
 /*
+ * vq_gemv with an fp16 epilogue: the same sums, stored as fp16 for a
+ * consumer that reads fp16 (the next layer's input), so no separate
+ * conversion launch follows [EVA 2.B: the epilogue unit finishes the
+ * reduced outputs on chip].  y[m][b][r] is the fp32 sum vq_gemv would store,
+ * rounded to the nearest fp16 value, ties to even (values beyond the fp16
+ * range become infinities).  y: host array of `count` device pointers, fp16
+ * [B][N_m] each (2-byte aligned), overwritten.  Formats, limits, workspace,
+ * errors and ordering as vq_gemv.
+ */
+int vq_gemv_f16(const vq_matrix *m, int32_t count, const uint16_t *const *x,
+                int32_t B, uint16_t *const *y, void *workspace, size_t ws_bytes,
+                void *stream);
+
+/*
  * Rotated VQ GEMV plus 1-bit residual [EDGE section details]: with
  * x_rot = rotation of x[m] (or x[m] itself when rht_sign is NULL),
  * y[m][b][r] = sum_j OC(x_rot)[b*K/d + j][WI[r][j]]

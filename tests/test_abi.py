@@ -126,6 +126,19 @@ def test_gemv_swiglu_validation_errors():
              None) == vq.VQ_EUNSUPPORTED
 
 
+def test_gemv_f16_validation_errors():
+    c = vq._c["vq_gemv_f16"]
+    arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)
+    ptrs = lambda n, v=FAKE: (ctypes.c_void_p * n)(*([v] * n))
+    assert c(arr([_m()]), 1, ptrs(1), 0, ptrs(1), None, 0, None) == vq.VQ_EINVAL
+    assert c(arr([_m()]), 1, ptrs(1), 5, ptrs(1), None, 0, None) == vq.VQ_EUNSUPPORTED   # B <= 4
+    assert c(arr([_m()]), 1, ptrs(1), 1, ptrs(1, FAKE + 1), None, 0, None) == vq.VQ_EALIGN
+    assert c(arr([_m()]), 1, ptrs(1, FAKE + 2), 1, ptrs(1), None, 0, None) == vq.VQ_EALIGN
+    assert c(arr([_m(d=8, nbits=16)]), 1, ptrs(1), 1, ptrs(1, FAKE + 2), None, 0,
+             None) == vq.VQ_EWORKSPACE                                      # 2-byte y passes
+    assert c(arr([_m(d=3)]), 1, ptrs(1), 1, ptrs(1), None, 0, None) == vq.VQ_EINVAL
+
+
 def test_gemv_tokens_validation_errors():
     c = vq._c["vq_gemv_tokens"]
     arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)

@@ -392,6 +392,25 @@ def test_gemv_tokens_shapes(K, N, B):
     assert np.array_equal(y1.view(np.uint32), ys[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("K,N,d,nbits,B", [(4096, 700, 4, 8, 1), (512, 17, 4, 8, 2),
+                                           (12288, 100, 4, 8, 3), (1024, 300, 4, 12, 1),
+                                           (1024, 100, 8, 16, 4)])
+def test_gemv_f16_epilogue(K, N, d, nbits, B):
+    # fp16 outputs: bitwise the fp32 call's sums rounded to nearest even (the
+    # same kernels, burst and streaming 8-bit, 12- and 16-bit), and within
+    # tolerance of the oracle
+    _say(f"gemv_f16 K={K} N={N} d={d} n={nbits} B={B}")
+    mi = synth.small_matrix(K, N, d, nbits, B=B, seed=K + N + 5 * B)
+    m = _upload(mi)
+    (y32,), (mats, xt, _, ws) = _run_gemv([m], [mi.x], B=B)
+    y16 = torch.full((B, N), float("nan"), dtype=torch.float16, device=DEV)
+    vq.vq_gemv_f16(mats, xt, B, [y16], ws, ws.numel())
+    torch.cuda.synchronize()
+    want = torch.from_numpy(y32).to(DEV).half()
+    assert torch.equal(y16.view(torch.int16), want.view(torch.int16))
+    _assert_close(y16.float().cpu().numpy(), _oracle_plain(mi), f"f16 K={K} N={N}")
+
+
 def test_gemv_tokens_moe_expert_group():
     # 8 routed experts' gate and up matrices (16 x 2048 -> 768, MoE-shaped),
     # each with its own codebook and its own 8 tokens, in one launch

@@ -73,6 +73,9 @@ _c = {
     "vq_gemv": _sig("vq_gemv", ctypes.c_int,
                     [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                      ctypes.POINTER(_vp), _vp, _sz, _vp]),
+    "vq_gemv_f16": _sig("vq_gemv_f16", ctypes.c_int,
+                        [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
+                         ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "vq_gemv_residual": _sig("vq_gemv_residual", ctypes.c_int,
                              [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                               ctypes.POINTER(_vp), _vp, _sz, _vp]),
@@ -231,6 +234,13 @@ def vq_gemv(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace, ws_by
     arr = _mat_array(mats)
     _check(_c["vq_gemv"](arr, len(mats), _ptr_array(xs), B, _ptr_array(ys), _ptr(workspace),
                          ws_bytes, _stream(stream)), "vq_gemv")
+
+
+def vq_gemv_f16(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace, ws_bytes: int,
+                stream=None) -> None:
+    """vq_gemv storing fp16 y (the fp32 sums rounded to nearest even)."""
+    _check(_c["vq_gemv_f16"](_mat_array(mats), len(mats), _ptr_array(xs), B, _ptr_array(ys),
+                             _ptr(workspace), ws_bytes, _stream(stream)), "vq_gemv_f16")
 
 
 def vq_gemv_residual(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace,

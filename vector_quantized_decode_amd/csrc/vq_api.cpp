@@ -180,7 +180,7 @@ static int check_matrix(const vq_matrix &a, int32_t B, bool residual) {
 }
 
 static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                       float *const *y, bool residual) {
+                       float *const *y, bool residual, uintptr_t y_align = 4) {
   if (!m || !x || !y) return VQ_EINVAL;
   if (count < 1 || count > VQ_MAX_GROUP) return VQ_EINVAL;
   if (B < 1) return VQ_EINVAL;
@@ -190,7 +190,7 @@ static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const 
     if (format_of(m[i]) != format_of(m[0])) return VQ_EUNSUPPORTED;   // one kernel per call
     if (!x[i] || !y[i]) return VQ_EINVAL;
     if (!aligned(x[i], 16)) return VQ_EALIGN;
-    if (!aligned(y[i], 4)) return VQ_EALIGN;
+    if (!aligned(y[i], y_align)) return VQ_EALIGN;
   }
   return VQ_OK;
 }
@@ -205,7 +205,7 @@ static size_t wc16_ws_bytes(const vq_matrix &a, int32_t B) {
 // Virtual-OC kernels: whole rows per workgroup; only the 16-bit kernel takes
 // a workspace.
 static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                   float *const *y, void *workspace, size_t ws_bytes, void *stream) {
+                   void *const *y, bool yf16, void *workspace, size_t ws_bytes, void *stream) {
   const Format f = format_of(m[0]);
   WcArgs args;
   memset(&args, 0, sizeof(args));
@@ -232,7 +232,8 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     d.wi = static_cast<const uint8_t *>(m[i].wi);
     d.wc = m[i].wc;
     d.x = x[i];
-    d.y = y[i];
+    d.y = static_cast<float *>(y[i]);
+    d.yf16 = yf16 ? 1 : 0;
     d.J = m[i].K / m[i].d;
     d.N = m[i].N;
     d.B = B;
@@ -286,7 +287,7 @@ static int gemv_plain(const vq_matrix *m, int32_t count, const uint16_t *const *
                       float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   const int st = check_group(m, count, x, B, y, false);
   if (st != VQ_OK) return st;
-  return gemv_wc(m, count, x, B, y, workspace, ws_bytes, stream);
+  return gemv_wc(m, count, x, B, reinterpret_cast<void *const *>(y), false, workspace, ws_bytes, stream);
 }
 
 static int gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
@@ -502,6 +503,13 @@ int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t
 int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                      float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   return gemv_residual(m, count, x, B, y, workspace, ws_bytes, stream);
+}
+
+int vq_gemv_f16(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                uint16_t *const *y, void *workspace, size_t ws_bytes, void *stream) {
+  const int st = check_group(m, count, x, B, reinterpret_cast<float *const *>(y), false, 2);
+  if (st != VQ_OK) return st;
+  return gemv_wc(m, count, x, B, reinterpret_cast<void *const *>(y), true, workspace, ws_bytes, stream);
 }
 
 int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,

@@ -48,13 +48,14 @@ struct WcMat {
   const uint8_t *wi;      // WI: device layout tile-16x64(-12), tile-16x32-16 or row tiles
   const uint16_t *wc;     // fp16 codebook [2^n][d]
   const uint16_t *x;      // fp16 input [B][K]
-  float *y;               // fp32 output [B][N], row stride ldy
+  float *y;               // output [B][N], row stride ldy: fp32, or fp16 when yf16
   int32_t J;              // subvectors per row, K/d
   int32_t N;              // output rows
   int32_t B;              // tokens
   int32_t ldy;            // y row stride (N)
   int32_t nwg;            // workgroups of this matrix
   int32_t jsplit;         // waves sharing a row group along J (1, 2, 4)
+  int32_t yf16;           // 1: y holds fp16 (the fp32 sum rounded to nearest even)
 };
 
 struct WcArgs {

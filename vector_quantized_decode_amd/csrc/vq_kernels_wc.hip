@@ -103,9 +103,19 @@ __device__ __forceinline__ WcMat load_wcmat(const WcArgs &args) {
   M.ldy = R.ldy;
   M.nwg = R.nwg;
   M.jsplit = R.jsplit;
+  M.yf16 = R.yf16;
   __asm__ volatile("" ::"s"(M.wi), "s"(M.wc), "s"(M.x), "s"(M.y), "s"(M.J), "s"(M.N), "s"(M.B),
-                   "s"(M.ldy), "s"(M.nwg), "s"(M.jsplit));
+                   "s"(M.ldy), "s"(M.nwg), "s"(M.jsplit), "s"(M.yf16));
   return M;
+}
+
+// Output element i of y: the fp32 sum, or (fp16 epilogue) that sum rounded
+// to the nearest fp16, ties to even, for a consumer that reads fp16.
+__device__ __forceinline__ void store_y(const WcMat &M, size_t i, float v) {
+  if (M.yf16)
+    reinterpret_cast<_Float16 *>(M.y)[i] = (_Float16)v;
+  else
+    M.y[i] = v;
 }
 
 // --------------------------------------------------------------------------
@@ -238,7 +248,7 @@ __global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
     for (int t = 1; t < S; ++t) v += part[(wave + t) * 64 + lane];
   }
   const int row = rgw * 16 + ((lane >> 2) & 15);
-  if ((lane & 3) == 0 && rgw < NG && row < M.N) M.y[row] = v;
+  if ((lane & 3) == 0 && rgw < NG && row < M.N) store_y(M, row, v);
 }
 
 // --------------------------------------------------------------------------
@@ -386,7 +396,7 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   if ((lane & 3) == 0 && rgw < NG && row < M.N) {
 #pragma unroll
     for (int b = 0; b < TB; ++b)
-      if (b < M.B) M.y[(size_t)b * M.ldy + row] = v[b];
+      if (b < M.B) store_y(M, (size_t)b * M.ldy + row, v[b]);
   }
 }
 
@@ -498,7 +508,7 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
   if ((lane & 3) == 0 && rgw < NG && row < M.N) {
 #pragma unroll
     for (int b = 0; b < TB; ++b)
-      if (b < M.B) M.y[(size_t)b * M.ldy + row] = v[b];
+      if (b < M.B) store_y(M, (size_t)b * M.ldy + row, v[b]);
   }
 }
 
@@ -614,7 +624,7 @@ __global__ void __launch_bounds__(W * 64) wc8_swiglu_kernel(const WcPairArgs arg
   if ((lane & 3) == 0 && rgw < NG && row < M.N) {
 #pragma unroll
     for (int b = 0; b < TB; ++b)
-      if (b < M.B) M.y[(size_t)b * M.ldy + row] = v[b] / (1.f + expf(-v[b])) * upv[b][pr][lane];
+      if (b < M.B) store_y(M, (size_t)b * M.ldy + row, v[b] / (1.f + expf(-v[b])) * upv[b][pr][lane]);
   }
 }
 
@@ -731,7 +741,7 @@ __global__ void __launch_bounds__(W * 64) wc16t_kernel(const Wc16tArgs args) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = sub * 4 + i;
-      if (tt < M.B && row < M.N) M.y[(size_t)tt * M.ldy + row] = acc[i];
+      if (tt < M.B && row < M.N) store_y(M, (size_t)tt * M.ldy + row, acc[i]);
     }
   }
 }

@@ -76,6 +76,8 @@ def parse():
     p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle baseline")
+    p.add_argument("--f16-out", action="store_true",
+                   help="plain workloads: fp16 outputs through vq_gemv_f16 (the fp16 epilogue)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -151,9 +153,14 @@ def main():
                 cp.alpha, cp.group, cp.rht_sign, cp.had_block = m.alpha, m.group, m.rht_sign, m.had_block
             lay.append(cp)
         layers.append(lay)
-    ys = [torch.empty((wl.B, m.N), dtype=torch.float32, device=dev) for m in base]
+    f16_out = bool(args.f16_out)
+    if f16_out and (residual or wl.gated_pairs or wl.B > 4):
+        print("--f16-out applies to the plain vq_gemv workloads", file=sys.stderr)
+        sys.exit(2)
+    ydt = torch.float16 if f16_out else torch.float32
+    ys = [torch.empty((wl.B, m.N), dtype=ydt, device=dev) for m in base]
     ws = vq.alloc_workspace(base, wl.B, residual=residual, device=dev)
-    call = vq.vq_gemv_residual if residual else vq.vq_gemv
+    call = vq.vq_gemv_residual if residual else (vq.vq_gemv_f16 if f16_out else vq.vq_gemv)
     if tokens:
         def call(lay, xs_, B_, ys_, ws_, n_, stream=None):
             vq.vq_gemv_tokens(lay, xs_, B_, ys_, stream=stream)
@@ -193,7 +200,7 @@ def main():
             else:
                 ref = oracle.vq_gemv(mi.x, mi.wc, oracle.pack_rows(mi.idx[rows], mi.nbits),
                                      rows.size, mi.K, mi.d, mi.nbits)
-            got = y.cpu().numpy()[:, rows]
+            got = y.float().cpu().numpy()[:, rows]
             rel, mx, rms = oracle.compare(got, ref)
             worst = max(worst, rel)
             ok = ok and oracle.within_tolerance(got, ref)
@@ -312,6 +319,8 @@ def main():
               flush=True)
 
     traffic, traffic_src = committed_traffic(args.workload)
+    if f16_out:
+        traffic, traffic_src = None, None   # the counters were taken with fp32 outputs
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -330,7 +339,8 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.workload], "matrices": wl.count,
                    "K_N": [[s.K, s.N] for s in wl.matrices], "d": wl.d, "nbits": wl.nbits,
                    "B": wl.B, "weight_bytes_per_layer": layer_bytes, "layer_copies": copies,
-                   "launch": "hip graph" if graph is not None else "stream"},
+                   "launch": "hip graph" if graph is not None else "stream",
+                   "y": "f16" if f16_out else "f32"},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(launch_us, 4),

@@ -104,8 +104,9 @@ def committed_traffic(workload: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(how the path would shard is described in DESIGN.md)",
+        print(json.dumps({"error": "the benchmark measures one GPU; --gpus must be 1 (across "
+                                   "GPUs a layer's matrices split by output rows, or by K with "
+                                   "one all-reduce, each GPU running this path on its shard)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 

@@ -39,6 +39,9 @@ def _case(kind):
     if kind == "swiglu":
         mis = [synth.small_matrix(2048, 300, 4, 8, seed=39), synth.small_matrix(2048, 300, 4, 8, seed=40)]
         return mis, 1, False
+    if kind == "f16":
+        mis = [synth.small_matrix(4096, 700, 4, 8, seed=45), synth.small_matrix(2048, 300, 4, 8, seed=46)]
+        return mis, 1, False
     if kind == "tokens16":
         return [synth.small_matrix(4096, 300, 4, 8, B=16, seed=41),
                 synth.small_matrix(1024, 77, 4, 8, B=16, seed=42)], 16, False
@@ -62,15 +65,16 @@ def _upload(mi, residual, tokens=False):
 
 
 @pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "wc12", "wc16", "swiglu",
-                                  "tokens16", "tokens5"])
+                                  "tokens16", "tokens5", "f16"])
 def test_graph_replays_match_eager(kind):
     print(f"[graph] {kind}", flush=True)
     mis, B, residual = _case(kind)
     mats = [_upload(mi, residual, tokens=kind.startswith("tokens")) for mi in mis]
     xs = [torch.from_numpy(mi.x).to(DEV) for mi in mis]
-    ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
+    ydt = torch.float16 if kind == "f16" else torch.float32
+    ys = [torch.full((B, m.N), float("nan"), dtype=ydt, device=DEV) for m in mats]
     ws = vq.alloc_workspace(mats, B, residual=residual, device=DEV)
-    call = vq.vq_gemv_residual if residual else vq.vq_gemv
+    call = vq.vq_gemv_residual if residual else (vq.vq_gemv_f16 if kind == "f16" else vq.vq_gemv)
     if kind.startswith("tokens"):
         def call(ms, xs_, B_, ys_, ws_, n_, stream=None):
             vq.vq_gemv_tokens(ms, xs_, B_, ys_, stream=stream)
@@ -108,4 +112,4 @@ def test_graph_replays_match_eager(kind):
         torch.cuda.synchronize()
         for m, (y, r) in enumerate(zip(ys, ref)):
             got = y.cpu().numpy()
-            assert np.array_equal(got.view(np.uint32), r.view(np.uint32)), f"{kind} replay {rep} matrix {m}"
+            assert np.array_equal(got.view(np.uint8), r.view(np.uint8)), f"{kind} replay {rep} matrix {m}"

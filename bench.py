@@ -77,7 +77,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle baseline")
     p.add_argument("--f16-out", action="store_true",
-                   help="plain workloads: fp16 outputs through vq_gemv_f16 (the fp16 epilogue)")
+                   help="fp16 outputs (the fp16 epilogue: vq_gemv_f16, vq_gemv_swiglu_f16)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -155,8 +155,8 @@ def main():
             lay.append(cp)
         layers.append(lay)
     f16_out = bool(args.f16_out)
-    if f16_out and (residual or wl.gated_pairs or wl.B > 4):
-        print("--f16-out applies to the plain vq_gemv workloads", file=sys.stderr)
+    if f16_out and (residual or wl.B > 4):
+        print("--f16-out applies to the plain and fused gate/up workloads", file=sys.stderr)
         sys.exit(2)
     ydt = torch.float16 if f16_out else torch.float32
     ys = [torch.empty((wl.B, m.N), dtype=ydt, device=dev) for m in base]
@@ -168,7 +168,8 @@ def main():
     if wl.gated_pairs:
         # gate/up pairs share the gate's x and write one gated output per pair
         def call(lay, xs_, B_, ys_, ws_, n_, stream=None):
-            vq.vq_gemv_swiglu(lay[0::2], lay[1::2], xs_[0::2], B_, ys_[0::2], ws_, n_, stream=stream)
+            fn = vq.vq_gemv_swiglu_f16 if f16_out else vq.vq_gemv_swiglu
+            fn(lay[0::2], lay[1::2], xs_[0::2], B_, ys_[0::2], ws_, n_, stream=stream)
     torch.cuda.synchronize()
     print(f"# setup: {copies} copies x {layer_bytes} B in {time.time() - t0:.1f} s",
           file=sys.stderr, flush=True)

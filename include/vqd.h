@@ -294,6 +294,18 @@ int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
                    void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * vq_gemv_swiglu with an fp16 epilogue: y[i][b][r] is the fp32 gated
+ * product vq_gemv_swiglu would store, rounded to the nearest fp16 value
+ * (ties to even), the form the down projection's fp16 input takes, so no
+ * conversion launch follows [EVA 2.B: the epilogue unit].  y: host array of
+ * `count` device pointers, fp16 [B][N] each (2-byte aligned), overwritten.
+ * Everything else as vq_gemv_swiglu.
+ */
+int vq_gemv_swiglu_f16(const vq_matrix *gate, const vq_matrix *up, int32_t count,
+                       const uint16_t *const *x, int32_t B, uint16_t *const *y,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Several tokens per call at (d, nbits) = (4, 8) on the matrix cores:
  * y[m][b][r] = sum_j x[m][b][4j..4j+3] . WC[WI[r][j]] for 1 <= B <= 16, the
  * same product as vq_gemv [EVA 2.A: the output codebook OC = X WC^T and the

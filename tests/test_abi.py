@@ -126,6 +126,16 @@ def test_gemv_swiglu_validation_errors():
              None) == vq.VQ_EUNSUPPORTED
 
 
+def test_gemv_swiglu_f16_validation_errors():
+    c = vq._c["vq_gemv_swiglu_f16"]
+    arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)
+    ptrs = lambda n, v=FAKE: (ctypes.c_void_p * n)(*([v] * n))
+    assert c(arr([_m()]), None, 1, ptrs(1), 1, ptrs(1), None, 0, None) == vq.VQ_EINVAL       # no up
+    assert c(arr([_m()]), arr([_m()]), 1, ptrs(1), 3, ptrs(1), None, 0, None) == vq.VQ_EUNSUPPORTED
+    assert c(arr([_m()]), arr([_m()]), 1, ptrs(1), 1, ptrs(1, FAKE + 1), None, 0,
+             None) == vq.VQ_EALIGN
+
+
 def test_gemv_f16_validation_errors():
     c = vq._c["vq_gemv_f16"]
     arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)

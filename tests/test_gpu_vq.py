@@ -468,6 +468,24 @@ def test_gemv_swiglu_pairs(K, N, B, pairs):
         _assert_close(y.cpu().numpy(), oracle.silu_gated(gy, uy), f"swiglu pair {p}")
 
 
+def test_gemv_swiglu_f16_epilogue():
+    # fp16 gated products: bitwise the fp32 call's output rounded to nearest even
+    _say("swiglu f16 K=4096 N=700 B=2 pairs=2")
+    gates = [synth.small_matrix(4096, 700, 4, 8, B=2, seed=520 + 2 * p) for p in range(2)]
+    ups = [synth.small_matrix(4096, 700, 4, 8, B=2, seed=521 + 2 * p) for p in range(2)]
+    xs = [torch.from_numpy(g.x).to(DEV) for g in gates]
+    gm = [_upload(g) for g in gates]
+    um = [_upload(u) for u in ups]
+    y32 = [torch.full((2, 700), float("nan"), dtype=torch.float32, device=DEV) for _ in range(2)]
+    y16 = [torch.full((2, 700), float("nan"), dtype=torch.float16, device=DEV) for _ in range(2)]
+    ws = vq.alloc_workspace(gm, 2, device=DEV)
+    vq.vq_gemv_swiglu(gm, um, xs, 2, y32, ws, ws.numel())
+    vq.vq_gemv_swiglu_f16(gm, um, xs, 2, y16, ws, ws.numel())
+    torch.cuda.synchronize()
+    for p in range(2):
+        assert torch.equal(y16[p].view(torch.int16), y32[p].half().view(torch.int16)), f"pair {p}"
+
+
 def test_gemv_mixed_group():
     _say("gemv mixed shapes in one launch")
     mis = [synth.small_matrix(1024, 300, 4, 8, seed=1), synth.small_matrix(512, 2000, 4, 8, seed=2),

@@ -81,6 +81,8 @@ _c = {
                               ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "vq_gemv_swiglu": _sig("vq_gemv_swiglu", ctypes.c_int,
                            [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "vq_gemv_swiglu_f16": _sig("vq_gemv_swiglu_f16", ctypes.c_int,
+                               [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
     "vq_gemv_tokens": _sig("vq_gemv_tokens", ctypes.c_int,
                            [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                             ctypes.POINTER(_vp), _vp]),
@@ -259,6 +261,16 @@ def vq_gemv_swiglu(gates: Sequence, ups: Sequence, xs: Sequence, B: int, ys: Seq
     _check(_c["vq_gemv_swiglu"](_mat_array(gates), _mat_array(ups), len(gates), _ptr_array(xs), B,
                                 _ptr_array(ys), _ptr(workspace), ws_bytes, _stream(stream)),
            "vq_gemv_swiglu")
+
+
+def vq_gemv_swiglu_f16(gates: Sequence, ups: Sequence, xs: Sequence, B: int, ys: Sequence,
+                       workspace, ws_bytes: int, stream=None) -> None:
+    """vq_gemv_swiglu storing fp16 y (the fp32 gated products rounded to nearest even)."""
+    if len(gates) != len(ups):
+        raise ValueError("one up matrix per gate matrix")
+    _check(_c["vq_gemv_swiglu_f16"](_mat_array(gates), _mat_array(ups), len(gates), _ptr_array(xs),
+                                    B, _ptr_array(ys), _ptr(workspace), ws_bytes, _stream(stream)),
+           "vq_gemv_swiglu_f16")
 
 
 def vq_gemv_tokens(mats: Sequence, xs: Sequence, B: int, ys: Sequence, stream=None) -> None:

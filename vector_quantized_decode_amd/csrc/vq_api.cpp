@@ -512,13 +512,11 @@ int vq_gemv_f16(const vq_matrix *m, int32_t count, const uint16_t *const *x, int
   return gemv_wc(m, count, x, B, reinterpret_cast<void *const *>(y), true, workspace, ws_bytes, stream);
 }
 
-int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
-                   const uint16_t *const *x, int32_t B, float *const *y, void *workspace,
-                   size_t ws_bytes, void *stream) {
-  (void)workspace;
-  (void)ws_bytes;
+static int gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
+                       const uint16_t *const *x, int32_t B, void *const *y, bool yf16,
+                       void *stream) {
   if (!up) return VQ_EINVAL;
-  int st = check_group(gate, count, x, B, y, false);
+  int st = check_group(gate, count, x, B, reinterpret_cast<float *const *>(y), false, yf16 ? 2 : 4);
   if (st != VQ_OK) return st;
   for (int i = 0; i < count; ++i) {
     st = check_matrix(up[i], B, false);
@@ -547,7 +545,8 @@ int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
     d.wi = static_cast<const uint8_t *>(gate[i].wi);
     d.wc = gate[i].wc;
     d.x = x[i];
-    d.y = y[i];
+    d.y = static_cast<float *>(y[i]);
+    d.yf16 = yf16 ? 1 : 0;
     d.J = gate[i].K / gate[i].d;
     d.N = gate[i].N;
     d.B = B;
@@ -569,6 +568,22 @@ int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
   }
   if (max_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
   return hip_status(launch_wc8_swiglu(args, (int)max_wg, waves, B, stream));
+}
+
+int vq_gemv_swiglu(const vq_matrix *gate, const vq_matrix *up, int32_t count,
+                   const uint16_t *const *x, int32_t B, float *const *y, void *workspace,
+                   size_t ws_bytes, void *stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  return gemv_swiglu(gate, up, count, x, B, reinterpret_cast<void *const *>(y), false, stream);
+}
+
+int vq_gemv_swiglu_f16(const vq_matrix *gate, const vq_matrix *up, int32_t count,
+                       const uint16_t *const *x, int32_t B, uint16_t *const *y, void *workspace,
+                       size_t ws_bytes, void *stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  return gemv_swiglu(gate, up, count, x, B, reinterpret_cast<void *const *>(y), true, stream);
 }
 
 int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,

@@ -1,28 +1,40 @@
 #!/usr/bin/env python3
 """Throughput of the VQ decode GEMV on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--copies C]
+    python bench.py [--steps K] [--warmup W] [--repeats R] [--workload 2]
 
-A step is one decode call of one layer: the grouped vq_gemv over the four
-4096x4096 2-bit q/k/v/o matrices of a LLaMA-7B layer, batch 1 (workload 2;
---workload selects another, see synth).  Inputs are resident in HBM before
-the timed region.  The timed steps rotate through C distinct copies of the
-layer's packed indices (>= 2 GiB in total, larger than the 256 MB
-Infinity Cache and the L2s) so every step streams its indices from HBM.  The
-C calls are captured once in a HIP graph and the graph is replayed; HIP
-events on the launch stream bracket the timed replays.
+A step is one decode call of one layer: by default the grouped vq_gemv over
+the four 4096x4096 2-bit q/k/v/o matrices of a LLaMA-7B layer, batch 1
+(workload 2; --workload selects another, see synth).  Inputs are resident in
+HBM before any timed region.
+
+Protocol.  C distinct copies of the layer (indices, codebooks, and for the
+residual workload signs, scales and rotation signs; >= 2 GiB in total, far
+above the 256 MB Infinity Cache and the L2s) are laid out once.  The K timed
+steps of a repeat are K back-to-back calls on K consecutive copies, captured
+in HIP graphs and replayed on one stream; HIP events on that stream bracket
+each repeat.  Exactly K steps are timed per repeat, over R repeats that start
+at successive copies; the reported period is the median repeat's.
 
 Prints one JSON line:
-  value            effective weight-byte throughput (GB/s) of back-to-back
-                   layer calls, launch gaps included; us_per_layer beside it
+  value            weight bytes per layer / median call period (GB/s); us_per_layer
+  timing           median, min and max repeat times; the same K calls issued
+                   one by one from Python (plain stream launches) instead of
+                   from a graph; a warm figure (one copy repeated, cache-resident)
   roofline         the lookup kernel (one launch per call; 16-bit indices add a
-                   pre-pass launch, counted in): algorithmic bytes per call
-                   over the average call period in the timed
-                   region; traffic = HBM bytes per launch from the committed
-                   rocprofv3 counter summary, when it was taken on the
-                   current kernel source (else null)
-  cpu_baseline     the float64 CPU oracle on the same layer, timed on the
-                   host (one thread), repeated until >= --cpu-seconds
+                   pre-pass launch, counted in): algorithmic bytes per call over
+                   the median call period.  stream_read_gbs: a plain streaming
+                   read (vq_stream_read) of the same copies' device index
+                   layouts (plus signs and scales), same K, same graphs, same
+                   repeats; frac_of_stream_read = achieved / stream_read_gbs.
+                   traffic = HBM bytes per launch from the committed rocprofv3
+                   counter summary, when it was taken on the current kernel
+                   source (else null)
+  context          a dense fp16 GEMV at the same shapes (torch.mm on fp16
+                   weights, C' distinct copies >= 2 GiB, same protocol):
+                   context, not a target
+  cpu_baseline     the float64 CPU oracle on the same layer, timed on the host
+                   (one thread), repeated until >= --cpu-seconds
 """
 from __future__ import annotations
 
@@ -44,40 +56,45 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, decimal GB/s
 METRIC = "µs/layer and effective HBM GB/s (% of peak) for VQ-GEMV at LLaMA-7B, B=1"
 CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
-# source of each workload's lookup kernel (8-bit indices: output-codebook tile
-# kernels; 12- and 16-bit indices: virtual-codebook kernels)
+# source of each workload's lookup kernel
 KERNEL_SRC = {1: "vq_kernels_wc.hip", 2: "vq_kernels_wc.hip", 3: "vq_kernels_wc.hip",
               4: "vq_kernels_wc.hip", 5: "vq_kernels.hip", 6: "vq_kernels_wc.hip",
               7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip", 9: "vq_kernels_wc.hip",
               10: "vq_kernels_tok.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 2 << 30       # distinct layer copies: at least this many weight bytes
+MAX_COPIES = 2048          # tiny layers: capped (then the copies are cache-resident)
 
 WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
                   2: "llama7b-attn-qkvo-4096x4096-2bit-b1",
                   3: "llama7b-decoder-7-linears-3bit-b1",
                   4: "llama13b-shaped-batched-decode-2bit-d8-b16",
                   5: "gemma2-9b-mlp-rotated-vq-residual-3.125bit-b1",
-                 6: "qwen3-30b-a3b-moe-8-experts-gate-up-2bit-b1",
-                 7: "qwen3-30b-a3b-moe-8-experts-down-2bit-b1",
-                 8: "llama7b-attn-qkvo-4096x4096-2bit-b4",
-                 9: "llama7b-mlp-gate-up-silu-fused-2bit-b1",
+                  6: "qwen3-30b-a3b-moe-8-experts-gate-up-2bit-b1",
+                  7: "qwen3-30b-a3b-moe-8-experts-down-2bit-b1",
+                  8: "llama7b-attn-qkvo-4096x4096-2bit-b4",
+                  9: "llama7b-mlp-gate-up-silu-fused-2bit-b1",
                   10: "llama7b-attn-qkvo-4096x4096-2bit-b16"}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=25600)
-    p.add_argument("--warmup", type=int, default=1024)
+    p.add_argument("--steps", type=int, default=128, help="calls timed per repeat (exact)")
+    p.add_argument("--warmup", type=int, default=128, help="untimed calls before timing (at least)")
+    p.add_argument("--repeats", type=int, default=20, help="timed repeats (median reported)")
     p.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--copies", type=int, default=0, help="layer copies (0: enough for 2 GiB)")
-    p.add_argument("--no-graph", action="store_true", help="launch from Python instead of a graph")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the stream-read floor, plain-stream, warm and dense fp16 runs")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle baseline")
     p.add_argument("--f16-out", action="store_true",
                    help="fp16 outputs (the fp16 epilogue: vq_gemv_f16, vq_gemv_swiglu_f16)")
+    p.add_argument("--dense-only", action="store_true",
+                   help="only the dense fp16 GEMV context run (prints its JSON)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -101,6 +118,162 @@ def committed_traffic(workload: int):
     return None, None
 
 
+def say(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Exactly K calls per repeat, from graphs captured over consecutive
+    layer copies.  call_for(c) gives a callable(stream) that launches the
+    call on copy c.  With K <= C the copies are cut into C / K windows of K
+    (C is rounded up to a multiple of K), one graph each, and repeat r
+    replays window r mod (C / K); with K > C a repeat replays a graph of all
+    C copies K // C times and a graph of the first K mod C copies once."""
+
+    def __init__(self, torch, call_for, copies: int, K: int, stream, same_copy: bool = False):
+        self.torch, self.stream, self.K = torch, stream, K
+        if same_copy:
+            self.reps = [[self._capture([call_for(0)] * K)]]
+        elif K <= copies:
+            self.reps = [[self._capture([call_for(w * K + i) for i in range(K)])]
+                         for w in range(copies // K)]
+        else:
+            full = self._capture([call_for(c) for c in range(copies)])
+            seq = [full] * (K // copies)
+            if K % copies:
+                seq.append(self._capture([call_for(c) for c in range(K % copies)]))
+            self.reps = [seq]
+
+    def _capture(self, fns):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            s = torch.cuda.current_stream()
+            for f in fns:
+                f(s)
+        torch.cuda.synchronize()
+        return g
+
+    def warm(self, steps: int) -> int:
+        n = max(len(self.reps), -(-steps // self.K))
+        with self.torch.cuda.stream(self.stream):
+            for r in range(n):
+                for g in self.reps[r % len(self.reps)]:
+                    g.replay()
+        self.torch.cuda.synchronize()
+        return n * self.K
+
+    def time(self, repeats: int):
+        torch = self.torch
+        out = []
+        for r in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(self.stream):
+                e0.record(self.stream)
+                for g in self.reps[r % len(self.reps)]:
+                    g.replay()
+                e1.record(self.stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return out
+
+
+def time_stream_launches(torch, call_for, copies: int, K: int, repeats: int, stream):
+    """The same K calls issued one by one from Python (prepared ctypes
+    arguments), no graph."""
+    out = []
+    for r in range(repeats):
+        calls = [call_for((r * K + i) % copies) for i in range(K)]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for f in calls:
+            f(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def summary(ms_list, K):
+    med = statistics.median(ms_list)
+    return {"median_ms": round(med, 5), "min_ms": round(min(ms_list), 5),
+            "max_ms": round(max(ms_list), 5), "us_per_call": round(med * 1e3 / K, 4)}
+
+
+def dense_gemv_run(args) -> dict:
+    """Dense fp16 GEMV at the workload's shapes (torch.mm on fp16 [N][K]
+    weights with x^T), C' distinct weight copies >= 2 GiB, the same exact-K,
+    repeated, graph-replay protocol: context for the quantized call, not a
+    target."""
+    import torch
+
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    try:
+        torch.backends.cuda.preferred_blas_library("cublas")   # rocBLAS on ROCm
+    except Exception:                                           # older torch: its default
+        pass
+    wl = synth.workload(args.workload)
+    K = args.steps
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * args.workload + 98)
+    shapes = [(m.N, m.K) for m in wl.matrices]
+    dense_bytes = sum(n * k * 2 for n, k in shapes)
+    dcopies = max(1, -(-COPY_BYTES // dense_bytes))
+    dws = [[torch.randn(sh, generator=gen, device=dev, dtype=torch.float32).half() for sh in shapes]
+           for _ in range(dcopies)]
+    xT = [torch.randn((k, wl.B), generator=gen, device=dev, dtype=torch.float32).half()
+          for _, k in shapes]
+    yd = [torch.empty((n, wl.B), dtype=torch.float16, device=dev) for n, _ in shapes]
+
+    def dense_for(c):
+        def f(s, c=c):
+            for W, xt, yy in zip(dws[c % dcopies], xT, yd):
+                torch.mm(W, xt, out=yy)
+        return f
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):                   # the BLAS library sets up eagerly
+        for c in range(dcopies):
+            dense_for(c)(stream)
+    torch.cuda.synchronize()
+    dcop = dcopies if K > dcopies else -(-dcopies // K) * K
+    dt = Timer(torch, dense_for, dcop, K, stream)
+    dt.warm(args.warmup)
+    ds = summary(dt.time(args.repeats), K)
+    return dict(ds, weight_bytes_per_layer=dense_bytes,
+                gbs=round(dense_bytes / (ds["us_per_call"] * 1e-6) / 1e9, 1),
+                copies=dcopies, launch="hip graph", blas="rocBLAS (torch preferred_blas_library)",
+                what="torch.mm of fp16 [N][K] weights with x^T, the workload's shapes and "
+                     "tokens; context, not target")
+
+
+def dense_context_subprocess(args) -> dict:
+    """dense_gemv_run in a child process, so that a BLAS library that fails
+    under graph capture cannot end this run."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--dense-only", "--workload",
+           str(args.workload), "--steps", str(args.steps), "--warmup", str(args.warmup),
+           "--repeats", str(args.repeats)]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=240)
+    except subprocess.TimeoutExpired:
+        return {"error": "dense fp16 GEMV run timed out"}
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    if r.returncode != 0 or not lines:
+        tail = (r.stderr.strip().splitlines() or ["no output"])[-1][:300]
+        say(f"# dense fp16 GEMV failed (rc {r.returncode}): {tail}")
+        return {"error": f"rc {r.returncode}: {tail}"}
+    d = json.loads(lines[-1])
+    say(f"# dense fp16 GEMV: {d['us_per_call']:.3f} us/layer, {d['gbs']} GB/s")
+    return d
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -109,6 +282,12 @@ def main():
                                    "one all-reduce, each GPU running this path on its shard)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.steps < 1 or args.repeats < 1:
+        print(json.dumps({"error": "--steps and --repeats must be at least 1"}), flush=True)
+        sys.exit(2)
+    if args.dense_only:
+        print(json.dumps(dense_gemv_run(args)), flush=True)
+        return
 
     import torch
 
@@ -121,8 +300,14 @@ def main():
     residual = wl.residual
     # more than 4 tokens at d=4, n=8: the matrix-core call, on the row-tile index layout
     tokens = (wl.d, wl.nbits) == (4, 8) and wl.B > 4
+    f16_out = bool(args.f16_out)
+    if f16_out and (residual or tokens):
+        say("--f16-out applies to the plain and fused gate/up workloads")
+        sys.exit(2)
     layer_bytes = synth.weight_bytes(args.workload)
-    copies = args.copies or max(1, -(-(2 << 30) // layer_bytes))
+    K = args.steps
+    c0 = args.copies or min(MAX_COPIES, max(1, -(-COPY_BYTES // layer_bytes)))
+    copies = c0 if K > c0 else -(-c0 // K) * K
 
     # ---- inputs: copy 0 from the seeded generator, packed + laid out by the library
     t0 = time.time()
@@ -137,48 +322,64 @@ def main():
             base.append(vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
                                          tokens=tokens, device=dev))
     xs = [torch.from_numpy(mi.x).to(dev) for mi in mis]
-    # further copies: seeded uniform random bytes in the device layouts (uniform bytes are
-    # uniform indices and Bernoulli(0.5) sign bits); alpha is shared
+    # Further copies, each with its own weights: seeded uniform random bytes in
+    # the device layouts (uniform bytes are uniform indices and Bernoulli(0.5)
+    # sign bits), a codebook drawn N(0, 0.02), scales U(0.001, 0.01) laid out by
+    # vq_repack_alpha, rotation signs uniform over +-1.
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 * args.workload + 99)
     layers = [base]
     for c in range(1, copies):
         lay = []
         for m in base:
+            wc = (torch.randn(m.wc.shape, generator=gen, device=dev, dtype=torch.float32)
+                  * 0.02).half()
             cp = vq.DeviceMatrix(m.K, m.N, m.d, m.nbits,
                                  torch.randint(0, 256, m.wi.shape, dtype=torch.uint8, device=dev,
-                                               generator=gen), m.wc)
+                                               generator=gen), wc)
             if residual:
                 cp.signs = torch.randint(0, 256, m.signs.shape, dtype=torch.uint8, device=dev,
                                          generator=gen)
-                cp.alpha, cp.group, cp.rht_sign, cp.had_block = m.alpha, m.group, m.rht_sign, m.had_block
+                G = m.K // m.group
+                al = (torch.rand((m.N, G), generator=gen, device=dev, dtype=torch.float32)
+                      * 0.009 + 0.001).half()
+                cp.alpha = torch.empty_like(m.alpha)
+                vq.vq_repack_alpha(al, m.N, m.K, m.group, cp.alpha)
+                cp.group, cp.had_block = m.group, m.had_block
+                cp.rht_sign = (torch.randint(0, 2, (m.K,), generator=gen, device=dev,
+                                             dtype=torch.int8) * 2 - 1)
             lay.append(cp)
         layers.append(lay)
-    f16_out = bool(args.f16_out)
-    if f16_out and (residual or wl.B > 4):
-        print("--f16-out applies to the plain and fused gate/up workloads", file=sys.stderr)
-        sys.exit(2)
     ydt = torch.float16 if f16_out else torch.float32
     ys = [torch.empty((wl.B, m.N), dtype=ydt, device=dev) for m in base]
     ws = vq.alloc_workspace(base, wl.B, residual=residual, device=dev)
-    call = vq.vq_gemv_residual if residual else (vq.vq_gemv_f16 if f16_out else vq.vq_gemv)
-    if tokens:
-        def call(lay, xs_, B_, ys_, ws_, n_, stream=None):
-            vq.vq_gemv_tokens(lay, xs_, B_, ys_, stream=stream)
-    if wl.gated_pairs:
-        # gate/up pairs share the gate's x and write one gated output per pair
-        def call(lay, xs_, B_, ys_, ws_, n_, stream=None):
-            fn = vq.vq_gemv_swiglu_f16 if f16_out else vq.vq_gemv_swiglu
-            fn(lay[0::2], lay[1::2], xs_[0::2], B_, ys_[0::2], ws_, n_, stream=stream)
+
+    prepared = {}
+
+    def call_for(c):
+        """A prepared call of the timed kind on layer copy c."""
+        if c in prepared:
+            return prepared[c]
+        lay = layers[c]
+        if tokens:
+            pc = vq.prepare_gemv_tokens(lay, xs, wl.B, ys)
+        elif wl.gated_pairs:
+            # gate/up pairs share the gate's x and write one gated output per pair
+            pc = vq.prepare_gemv_swiglu(lay[0::2], lay[1::2], xs[0::2], wl.B, ys[0::2], f16=f16_out)
+        else:
+            name = "vq_gemv_residual" if residual else ("vq_gemv_f16" if f16_out else "vq_gemv")
+            pc = vq.prepare_gemv(name, lay, xs, wl.B, ys, ws, ws.numel())
+        prepared[c] = pc
+        return pc
+
     torch.cuda.synchronize()
-    print(f"# setup: {copies} copies x {layer_bytes} B in {time.time() - t0:.1f} s",
-          file=sys.stderr, flush=True)
+    say(f"# setup: {copies} copies x {layer_bytes} B in {time.time() - t0:.1f} s")
 
     # ---- sampled parity check of copy 0 in the timed launch configuration
     parity = None
     if not args.no_check:
         import oracle
-        call(layers[0], xs, wl.B, ys, ws, ws.numel())
+        call_for(0)(torch.cuda.current_stream())
         torch.cuda.synchronize()
         rng = np.random.default_rng(7)
         worst = 0.0
@@ -207,60 +408,76 @@ def main():
             worst = max(worst, rel)
             ok = ok and oracle.within_tolerance(got, ref)
         parity = {"sampled_rows_per_matrix": 256, "max_rel_l2": worst, "pass": bool(ok)}
-        print(f"# parity (sampled rows): max rel_l2 {worst:.3e} pass={ok}", file=sys.stderr,
-              flush=True)
+        say(f"# parity (sampled rows): max rel_l2 {worst:.3e} pass={ok}")
 
-    # ---- graph of one pass over all copies
     stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    per_graph = copies
-    graph = None
-    if not args.no_graph:
-        with torch.cuda.stream(stream):
-            for lay in layers[:2]:            # warm the launch path before capture
-                call(lay, xs, wl.B, ys, ws, ws.numel(), stream=stream)
-        stream.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for lay in layers:
-                call(lay, xs, wl.B, ys, ws, ws.numel(), stream=torch.cuda.current_stream())
-        torch.cuda.synchronize()
-
-    def run_steps(nsteps):
-        if graph is not None:
-            for _ in range(max(1, nsteps // per_graph)):
-                graph.replay()
-            return max(1, nsteps // per_graph) * per_graph
-        with torch.cuda.stream(stream):
-            for i in range(nsteps):
-                call(layers[i % copies], xs, wl.B, ys, ws, ws.numel(), stream=stream)
-        return nsteps
-
     with torch.cuda.stream(stream):
-        run_steps(max(args.warmup, per_graph))
+        for c in range(min(2, copies)):                   # the launch path before capture
+            call_for(c)(stream)
     torch.cuda.synchronize()
 
-    # ---- timed region: back-to-back layer calls
-    with torch.cuda.stream(stream):
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ev0.record()
-        done = run_steps(args.steps)
-        ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
-    us_per_layer = ms * 1e3 / done
+    # ---- timed region: exactly K back-to-back calls per repeat
+    main_t = Timer(torch, call_for, copies, K, stream)
+    warm_done = main_t.warm(args.warmup)
+    ms = main_t.time(args.repeats)
+    st = summary(ms, K)
+    us_per_layer = st["us_per_call"]
     gbs = layer_bytes / (us_per_layer * 1e-6) / 1e9
-    print(f"# timed {done} steps in {ms:.2f} ms: {us_per_layer:.3f} us/layer, {gbs:.1f} GB/s",
-          file=sys.stderr, flush=True)
+    say(f"# timed {args.repeats} x {K} steps (median {st['median_ms']:.4f} ms, "
+        f"min {st['min_ms']:.4f}, max {st['max_ms']:.4f}): {us_per_layer:.3f} us/layer, "
+        f"{gbs:.1f} GB/s")
+    timing = {"repeats": args.repeats, "steps_per_repeat": K, "warmup_steps_run": warm_done,
+              "graph": st}
 
-    # One call is one launch of the lookup kernel (the 16-bit format adds a
-    # pre-pass launch), so the timed region's average call period is that
-    # kernel's average duration back to back, plus the pre-pass where there
-    # is one (rocprofv3's kernel trace of the same command reports both).
-    launch_us = us_per_layer
-    kernel_gbs = gbs
+    # ---- context: the read floor, plain stream launches, a warm figure, dense fp16
+    read_gbs = None
+    context = None
+    if not args.no_context:
+        def bufs_of(lay):
+            b, n = [], []
+            for m in lay:
+                b.append(m.wi)
+                n.append(m.wi.numel())
+                if residual:
+                    b += [m.signs, m.alpha]
+                    n += [m.signs.numel(), m.alpha.numel() * 2]
+            return b, n
+
+        nb0 = bufs_of(layers[0])[1]
+        sink_words = vq.vq_stream_read_sink_words(nb0)
+        sink = torch.empty(sink_words, dtype=torch.int32, device=dev)
+        read_prepared = {}
+
+        def read_for(c):
+            if c not in read_prepared:
+                b, n = bufs_of(layers[c])
+                read_prepared[c] = vq.prepare_stream_read(b, n, sink, sink_words)
+            return read_prepared[c]
+
+        read_bytes = sum(nb0)
+        rt = Timer(torch, read_for, copies, K, stream)
+        rt.warm(args.warmup)
+        rs = summary(rt.time(args.repeats), K)
+        read_gbs = read_bytes / (rs["us_per_call"] * 1e-6) / 1e9
+        say(f"# stream read of {read_bytes} B per call: {rs['us_per_call']:.3f} us, "
+            f"{read_gbs:.1f} GB/s")
+        del rt
+
+        sl = summary(time_stream_launches(torch, call_for, copies, K, args.repeats, stream), K)
+        say(f"# plain stream launches: {sl['us_per_call']:.3f} us/layer")
+        wt = Timer(torch, call_for, copies, K, stream, same_copy=True)
+        wt.warm(args.warmup)
+        ws_ = summary(wt.time(args.repeats), K)
+        say(f"# warm (copy 0 repeated): {ws_['us_per_call']:.3f} us/layer")
+        del wt
+        timing["stream_launch"] = sl
+        timing["warm_same_copy"] = ws_
+        timing["stream_read"] = dict(rs, bytes_per_call=read_bytes,
+                                     what="vq_stream_read over each copy's device index layouts"
+                                          + (", signs and scales" if residual else ""))
+
+        if not residual:
+            context = {"dense_fp16_gemv": dense_context_subprocess(args)}
 
     # ---- plain copy of known size: the reference reading of the HBM byte counters
     if args.copy_probe:
@@ -271,7 +488,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        print("# copy probe: 5 x 256 MiB device copies", file=sys.stderr, flush=True)
+        say("# copy probe: 5 x 256 MiB device copies")
 
     # ---- CPU oracle baseline: the whole layer, one thread, >= cpu-seconds
     cpu = None
@@ -317,18 +534,27 @@ def main():
                          f"limited to 1), {len(reps)} timed run(s) after 1 warm run, median; "
                          f"host has {cores} cores",
                "us_per_layer": round(med * 1e6, 1)}
-        print(f"# cpu oracle: {med * 1e3:.1f} ms/layer over {len(reps)} runs", file=sys.stderr,
-              flush=True)
+        say(f"# cpu oracle: {med * 1e3:.1f} ms/layer over {len(reps)} runs")
 
     traffic, traffic_src = committed_traffic(args.workload)
     if f16_out:
         traffic, traffic_src = None, None   # the counters were taken with fp32 outputs
+    roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "kernel_us": round(us_per_layer, 4),
+            "launches_per_call": 2 if wl.nbits == 16 else 1,
+            "algorithmic_bytes_per_launch": layer_bytes,
+            "traffic_source": traffic_src,
+            "kernel_source_sha": kernel_source_sha(args.workload)}
+    if read_gbs is not None:
+        roof["stream_read_gbs"] = round(read_gbs, 2)
+        roof["frac_of_stream_read"] = round(gbs / read_gbs, 4)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": done,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": us_per_layer / 1e3,
         "us_per_layer": round(us_per_layer, 4),
@@ -336,19 +562,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16" if f16_out else "f32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "matrices": wl.count,
                    "K_N": [[s.K, s.N] for s in wl.matrices], "d": wl.d, "nbits": wl.nbits,
                    "B": wl.B, "weight_bytes_per_layer": layer_bytes, "layer_copies": copies,
-                   "launch": "hip graph" if graph is not None else "stream",
-                   "y": "f16" if f16_out else "f32"},
-        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel_us": round(launch_us, 4),
-                     "launches_per_call": 2 if wl.nbits == 16 else 1,
-                     "algorithmic_bytes_per_launch": layer_bytes,
-                     "traffic_source": traffic_src, "kernel_source_sha": kernel_source_sha(args.workload)},
+                   "distinct_codebooks_per_copy": True, "launch": "hip graph",
+                   "operands": "f16", "accumulate": "f32", "y": "f16" if f16_out else "f32"},
+        "timing": timing,
+        "roofline": roof,
+        "context": context,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -155,16 +155,25 @@ size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group);
  * except for (d, nbits) = (8, 16): 1 MiB + B*K*2 bytes (each rounded up to
  * 256) per matrix; the residual call needs its split-K accumulators, completion
  * counters, float partials for non-finite inputs and the rotated inputs of
- * Hadamard blocks above 2048.  Returns 0 on invalid arguments too.  The
- * workspace must be set up once with vq_workspace_init before its first
- * use; every call that completes leaves it ready for the next one.  Calls
- * sharing one workspace must be ordered (same stream or explicit
- * dependencies).
+ * Hadamard blocks above 2048.  Returns 0 on invalid arguments too.
+ *
+ * A workspace serves one call kind on one group of matrices: the (m, count,
+ * B, residual) it was sized for.  Set it up with vq_workspace_init before
+ * the first call of that kind and group; every vq_gemv_residual call on that
+ * group that completes leaves its completion counters and accumulators at
+ * zero again, so further calls on the same group need no set-up.  Before
+ * the same buffer serves another group or another call kind, call
+ * vq_workspace_init again: the residual call places its counters at offsets
+ * that depend on the group, and the (8, 16) vq_gemv call rewrites its
+ * buffer from offset 0, so either can leave non-zero bytes where the next
+ * group's counters sit, and a residual call started on such bytes returns
+ * wrong rows without an error.  Calls sharing one workspace must be ordered
+ * (same stream or explicit dependencies).
  */
 size_t vq_workspace_bytes(const vq_matrix *m, int32_t count, int32_t B,
                           int32_t residual);
 
-/* Zero the completion counters of a workspace (a fill kernel, no memset). */
+/* Zero all ws_bytes of a workspace (a fill kernel, no memset). */
 int vq_workspace_init(void *workspace, size_t ws_bytes, void *stream);
 
 /*
@@ -337,6 +346,24 @@ int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
  */
 int vq_repack_wi_rows(const uint8_t *canonical, int32_t N, int32_t K, void *device_layout,
                       void *stream);
+
+/*
+ * Measurement helper, not part of the method: a plain streaming read of
+ * `count` device buffers (1 <= count <= 64, each 16-byte aligned, 1 <= size
+ * < 2^31 bytes) in one kernel launch.  Each workgroup of 8 wavefronts reads
+ * 32 KiB; each wavefront requests four 1 KiB chunks with 16-byte
+ * non-temporal loads (the index loads of the 8-bit lookup kernels) before
+ * it uses the first.  Each wavefront stores the XOR of the words it read to
+ * sink (uint32, sink_words >= vq_stream_read_sink_words(bytes, count),
+ * 4-byte aligned; VQ_EWORKSPACE if smaller), so none of the reads can be
+ * dropped.  Timed over a layer's device index layouts, its launch period
+ * is the read floor of a lookup call of the same bytes.
+ *   buffers  host array of `count` device pointers.
+ *   bytes    host array of `count` byte counts.
+ */
+size_t vq_stream_read_sink_words(const size_t *bytes, int32_t count);
+int vq_stream_read(const void *const *buffers, const size_t *bytes, int32_t count, uint32_t *sink,
+                   size_t sink_words, void *stream);
 
 #ifdef __cplusplus
 }

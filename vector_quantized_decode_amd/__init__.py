@@ -86,6 +86,10 @@ _c = {
     "vq_gemv_tokens": _sig("vq_gemv_tokens", ctypes.c_int,
                            [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                             ctypes.POINTER(_vp), _vp]),
+    "vq_stream_read_sink_words": _sig("vq_stream_read_sink_words", _sz,
+                                      [ctypes.POINTER(_sz), _i32]),
+    "vq_stream_read": _sig("vq_stream_read", ctypes.c_int,
+                           [ctypes.POINTER(_vp), ctypes.POINTER(_sz), _i32, _vp, _sz, _vp]),
 }
 
 # every symbol the header declares (checked by the ABI test)
@@ -277,6 +281,77 @@ def vq_gemv_tokens(mats: Sequence, xs: Sequence, B: int, ys: Sequence, stream=No
     """vq_gemv for 1-16 tokens at d=4, n=8; each mats[i].wi holds row tiles (vq_repack_wi_rows)."""
     _check(_c["vq_gemv_tokens"](_mat_array(mats), len(mats), _ptr_array(xs), B, _ptr_array(ys),
                                 _stream(stream)), "vq_gemv_tokens")
+
+
+def _size_array(ns: Sequence[int]) -> ctypes.Array:
+    arr = (_sz * len(ns))()
+    for i, n in enumerate(ns):
+        arr[i] = int(n)
+    return arr
+
+
+def vq_stream_read_sink_words(nbytes: Sequence[int]) -> int:
+    return _c["vq_stream_read_sink_words"](_size_array(nbytes), len(nbytes))
+
+
+def vq_stream_read(buffers: Sequence, nbytes: Sequence[int], sink, sink_words: int,
+                   stream=None) -> None:
+    """Measurement helper: one plain streaming read of the buffers (no method
+    arithmetic); sink receives one XOR word per wavefront."""
+    _check(_c["vq_stream_read"](_ptr_array(buffers), _size_array(nbytes), len(buffers), _ptr(sink),
+                                sink_words, _stream(stream)), "vq_stream_read")
+
+
+# ------------------------------------------------------------------ prepared calls
+class PreparedCall:
+    """One library call with its ctypes arguments built once, for callers
+    that issue the same call many times from Python (a launch loop): calling
+    it passes only the stream.  It keeps the tensors and arrays it points at
+    referenced."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self._f = _c[name]
+        self._name = name
+        self._args = args
+        self._keep = keep
+
+    def __call__(self, stream) -> None:
+        st = self._f(*self._args, _stream(stream))
+        if st != VQ_OK:
+            raise VQError(st, self._name)
+
+
+def prepare_gemv(name: str, mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace=None,
+                 ws_bytes: int = 0) -> PreparedCall:
+    """A PreparedCall of vq_gemv, vq_gemv_f16 or vq_gemv_residual."""
+    if name not in ("vq_gemv", "vq_gemv_f16", "vq_gemv_residual"):
+        raise ValueError(name)
+    arr, xa, ya = _mat_array(mats), _ptr_array(xs), _ptr_array(ys)
+    return PreparedCall(name, (arr, len(mats), xa, B, ya, _ptr(workspace), ws_bytes),
+                        (arr, xa, ya, tuple(mats), tuple(xs), tuple(ys), workspace))
+
+
+def prepare_gemv_tokens(mats: Sequence, xs: Sequence, B: int, ys: Sequence) -> PreparedCall:
+    arr, xa, ya = _mat_array(mats), _ptr_array(xs), _ptr_array(ys)
+    return PreparedCall("vq_gemv_tokens", (arr, len(mats), xa, B, ya),
+                        (arr, xa, ya, tuple(mats), tuple(xs), tuple(ys)))
+
+
+def prepare_gemv_swiglu(gates: Sequence, ups: Sequence, xs: Sequence, B: int, ys: Sequence,
+                        f16: bool = False) -> PreparedCall:
+    if len(gates) != len(ups):
+        raise ValueError("one up matrix per gate matrix")
+    ga, ua, xa, ya = _mat_array(gates), _mat_array(ups), _ptr_array(xs), _ptr_array(ys)
+    name = "vq_gemv_swiglu_f16" if f16 else "vq_gemv_swiglu"
+    return PreparedCall(name, (ga, ua, len(gates), xa, B, ya, None, 0),
+                        (ga, ua, xa, ya, tuple(gates), tuple(ups), tuple(xs), tuple(ys)))
+
+
+def prepare_stream_read(buffers: Sequence, nbytes: Sequence[int], sink,
+                        sink_words: int) -> PreparedCall:
+    ba, na = _ptr_array(buffers), _size_array(nbytes)
+    return PreparedCall("vq_stream_read", (ba, na, len(buffers), _ptr(sink), sink_words),
+                        (ba, na, tuple(buffers), sink))
 
 
 # ------------------------------------------------------------------ helpers

@@ -635,4 +635,38 @@ int vq_gemv_tokens(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
   return hip_status(launch_wc8t(args, (int)max_wg, rw, stream));
 }
 
+size_t vq_stream_read_sink_words(const size_t *bytes, int32_t count) {
+  if (!bytes || count < 1 || count > VQ_MAX_READ) return 0;
+  size_t mx = 0;
+  for (int i = 0; i < count; ++i) {
+    if (bytes[i] == 0 || bytes[i] >= ((size_t)1 << 31)) return 0;
+    mx = std::max(mx, bytes[i]);
+  }
+  return (size_t)count * (size_t)stream_read_workgroups((uint32_t)mx) *
+         (size_t)stream_read_sink_words_per_wg();
+}
+
+int vq_stream_read(const void *const *buffers, const size_t *bytes, int32_t count, uint32_t *sink,
+                   size_t sink_words, void *stream) {
+  if (!buffers || !bytes || !sink || count < 1) return VQ_EINVAL;
+  if (count > VQ_MAX_READ) return VQ_EUNSUPPORTED;
+  const size_t need = vq_stream_read_sink_words(bytes, count);
+  if (need == 0) return VQ_EINVAL;
+  if (sink_words < need) return VQ_EWORKSPACE;
+  if (!aligned(sink, 4)) return VQ_EALIGN;
+  ReadArgs a;
+  memset(&a, 0, sizeof(a));
+  a.count = count;
+  a.sink = sink;
+  size_t mx = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!buffers[i]) return VQ_EINVAL;
+    if (!aligned(buffers[i], 16)) return VQ_EALIGN;
+    a.buf[i] = static_cast<const uint8_t *>(buffers[i]);
+    a.bytes[i] = (uint32_t)bytes[i];
+    mx = std::max(mx, bytes[i]);
+  }
+  return hip_status(launch_stream_read(a, (int)stream_read_workgroups((uint32_t)mx), stream));
+}
+
 }  // extern "C"

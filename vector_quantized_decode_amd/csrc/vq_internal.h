@@ -128,4 +128,18 @@ int launch_rht(const uint16_t *x, const int8_t *sign, int B, int K, int h, float
                float *x_rot, void *stream);
 int launch_fill_u32(uint32_t *p, size_t n, uint32_t v, void *stream);
 
+// Plain streaming read of up to VQ_MAX_READ device buffers in one launch
+// (measurement only): sink[(m * grid_x + x) * words_per_wg + w] receives the
+// XOR of what wave w of workgroup (x, m) read.
+constexpr int VQ_MAX_READ = 64;
+struct ReadArgs {
+  const uint8_t *buf[VQ_MAX_READ];
+  uint32_t bytes[VQ_MAX_READ];
+  uint32_t *sink;
+  int32_t count;
+};
+int64_t stream_read_workgroups(uint32_t max_bytes);
+int stream_read_sink_words_per_wg();
+int launch_stream_read(const ReadArgs &a, int grid_x, void *stream);
+
 }  // namespace vqd

@@ -14,7 +14,10 @@ above the 256 MB Infinity Cache and the L2s) are laid out once.  The K timed
 steps of a repeat are K back-to-back calls on K consecutive copies, captured
 in HIP graphs and replayed on one stream; HIP events on that stream bracket
 each repeat.  Exactly K steps are timed per repeat, over R repeats that start
-at successive copies; the reported period is the median repeat's.
+at successive copies; the reported period is the median repeat's.  Before
+each repeat's first event an untimed replay of the previous window keeps the
+GPU busy, so the host's graph submission latency falls outside the timed
+span (timing.graph_from_idle reports the repeats without it).
 
 Prints one JSON line:
   value            weight bytes per layer / median call period (GB/s); us_per_layer
@@ -60,7 +63,7 @@ CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
 KERNEL_SRC = {1: "vq_kernels_wc.hip", 2: "vq_kernels_wc.hip", 3: "vq_kernels_wc.hip",
               4: "vq_kernels_wc.hip", 5: "vq_kernels.hip", 6: "vq_kernels_wc.hip",
               7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip", 9: "vq_kernels_wc.hip",
-              10: "vq_kernels_tok.hip"}
+              10: "vq_kernels_tok.hip", 11: "vq_kernels_wc.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 2 << 30       # distinct layer copies: at least this many weight bytes
 MAX_COPIES = 2048          # tiny layers: capped (then the copies are cache-resident)
@@ -74,7 +77,8 @@ WORKLOAD_NAMES = {1: "vq-linear-512x512-2bit-b1",
                   7: "qwen3-30b-a3b-moe-8-experts-down-2bit-b1",
                   8: "llama7b-attn-qkvo-4096x4096-2bit-b4",
                   9: "llama7b-mlp-gate-up-silu-fused-2bit-b1",
-                  10: "llama7b-attn-qkvo-4096x4096-2bit-b16"}
+                  10: "llama7b-attn-qkvo-4096x4096-2bit-b16",
+                  11: "llama7b-attn-qkvo-4096x4096-2bit-b1-qkv-shared-codebook"}
 
 
 def parse():
@@ -163,16 +167,26 @@ class Timer:
         self.torch.cuda.synchronize()
         return n * self.K
 
-    def time(self, repeats: int):
+    def time(self, repeats: int, lead_in: bool = True):
+        """Per repeat: synchronize, (lead-in) replay the previous window
+        untimed, record e0, replay the K timed calls, record e1, synchronize.
+        The lead-in keeps the GPU busy while the host submits the timed
+        graph, so e0..e1 spans exactly the K calls back to back and not the
+        host's submission latency from an idle GPU (lead_in=False measures
+        that too)."""
         torch = self.torch
         out = []
+        n = len(self.reps)
         for r in range(repeats):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             with torch.cuda.stream(self.stream):
+                if lead_in:
+                    for g in self.reps[(r - 1) % n]:
+                        g.replay()
                 e0.record(self.stream)
-                for g in self.reps[r % len(self.reps)]:
+                for g in self.reps[r % n]:
                     g.replay()
                 e1.record(self.stream)
             torch.cuda.synchronize()
@@ -322,6 +336,10 @@ def main():
             base.append(vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits,
                                          tokens=tokens, device=dev))
     xs = [torch.from_numpy(mi.x).to(dev) for mi in mis]
+    lead = [synth.shared_leader(args.workload, m) for m in range(wl.count)]
+    for m, l in enumerate(lead):          # shared groups pass one codebook and one x
+        if l != m:
+            base[m].wc, xs[m] = base[l].wc, xs[l]
     # Further copies, each with its own weights: seeded uniform random bytes in
     # the device layouts (uniform bytes are uniform indices and Bernoulli(0.5)
     # sign bits), a codebook drawn N(0, 0.02), scales U(0.001, 0.01) laid out by
@@ -331,9 +349,10 @@ def main():
     layers = [base]
     for c in range(1, copies):
         lay = []
-        for m in base:
-            wc = (torch.randn(m.wc.shape, generator=gen, device=dev, dtype=torch.float32)
-                  * 0.02).half()
+        for mm, m in enumerate(base):
+            wc = (lay[lead[mm]].wc if lead[mm] != mm else
+                  (torch.randn(m.wc.shape, generator=gen, device=dev, dtype=torch.float32)
+                   * 0.02).half())
             cp = vq.DeviceMatrix(m.K, m.N, m.d, m.nbits,
                                  torch.randint(0, 256, m.wi.shape, dtype=torch.uint8, device=dev,
                                                generator=gen), wc)
@@ -428,6 +447,11 @@ def main():
         f"{gbs:.1f} GB/s")
     timing = {"repeats": args.repeats, "steps_per_repeat": K, "warmup_steps_run": warm_done,
               "graph": st}
+    if not args.no_context:
+        idle = summary(main_t.time(args.repeats, lead_in=False), K)
+        timing["graph_from_idle"] = dict(idle, what="the same repeats with no lead-in: each "
+                                                    "includes the graph's submission latency")
+        say(f"# from an idle GPU (submission latency included): {idle['us_per_call']:.3f} us/layer")
 
     # ---- context: the read floor, plain stream launches, a warm figure, dense fp16
     read_gbs = None
@@ -472,6 +496,23 @@ def main():
         del wt
         timing["stream_launch"] = sl
         timing["warm_same_copy"] = ws_
+        if wl.shared and not residual and not tokens and not wl.gated_pairs:
+            # the same calls through vq_gemv_shared (shared matrices merged into units)
+            merged = {}
+
+            def merged_for(c):
+                if c not in merged:
+                    merged[c] = vq.prepare_gemv("vq_gemv_shared", layers[c], xs, wl.B, ys, ws,
+                                                ws.numel())
+                return merged[c]
+
+            mt = Timer(torch, merged_for, copies, K, stream)
+            mt.warm(args.warmup)
+            ms_ = summary(mt.time(args.repeats), K)
+            del mt
+            timing["vq_gemv_shared"] = dict(ms_, what="the same calls with the matrices that "
+                                                      "share a codebook and x merged into units")
+            say(f"# vq_gemv_shared (merged units): {ms_['us_per_call']:.3f} us/layer")
         timing["stream_read"] = dict(rs, bytes_per_call=read_bytes,
                                      what="vq_stream_read over each copy's device index layouts"
                                           + (", signs and scales" if residual else ""))

@@ -257,6 +257,26 @@ int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x,
             void *stream);
 
 /*
+ * vq_gemv for groups whose matrices share their codebook and input [EVA 2.A:
+ * one output codebook, the product of x with WC, serves the lookups of
+ * every row that uses that x and WC; EVA 2.B: the codebook stays on chip
+ * while indices stream].  Matrices of the group that pass the same wc and x
+ * pointers and have the same K and N are merged into one unit: their row
+ * groups are laid end to end and a workgroup's staged codebook and x serve
+ * rows of several of them.  Results are bitwise those of vq_gemv (every
+ * row's sums keep their order).  Arguments, formats, limits and errors as
+ * vq_gemv; the merge applies to (d, nbits) = (4, 8) calls that take the
+ * 8-wave burst kernel and is skipped otherwise.  On MI355X it measured no
+ * faster than vq_gemv (LLaMA-7B q/k/v sharing one codebook and x: 5.78
+ * against 5.63 us): each workgroup stages its own codebook copy either way,
+ * and the member lookup adds a dependent argument load to every wave's
+ * start.  vq_gemv therefore never merges.
+ */
+int vq_gemv_shared(const vq_matrix *m, int32_t count, const uint16_t *const *x,
+                   int32_t B, float *const *y, void *workspace, size_t ws_bytes,
+                   void *stream);
+
+/*
  * vq_gemv with an fp16 epilogue: the same sums, stored as fp16 for a
  * consumer that reads fp16 (the next layer's input), so no separate
  * conversion launch follows [EVA 2.B: the epilogue unit finishes the

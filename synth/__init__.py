@@ -24,6 +24,10 @@ Workloads (matrix shapes follow LLaMA-7B / LLaMA-13B / Gemma-2-9B linears):
   9  LLaMA-7B MLP gate and up projections (2 x 4096->11008), d=4, n=8, B=1,
      called as one gate/up pair with the SiLU gating fused (both use the
      gate's x)
+ 10  workload 2 for 16 tokens per call, B=16
+ 11  workload 2 with one codebook shared by q, k and v, which also share
+     their input x (the attention projections of one layer read the same
+     hidden state); o keeps its own codebook and x
 
 Distributions: x ~ N(0, 1), codebook ~ N(0, 0.02) (0.02 is the standard
 deviation), indices uniform over [0, 2^n), residual sign bits Bernoulli(0.5),
@@ -42,7 +46,7 @@ from typing import List, Optional
 import numpy as np
 
 __all__ = ["MatrixSpec", "Workload", "WORKLOADS", "workload", "matrix_inputs",
-           "seed_for", "small_matrix"]
+           "seed_for", "small_matrix", "shared_leader"]
 
 
 @dataclass(frozen=True)
@@ -65,6 +69,7 @@ class Workload:
     outlier_frac: float = 0.0   # fraction of input channels scaled
     outlier_scale: float = 1.0
     gated_pairs: bool = False   # matrices 2i, 2i+1 are a gate/up pair (SiLU gating fused)
+    shared: tuple = ()          # groups of matrices that share the first one's codebook and x
 
     @property
     def count(self) -> int:
@@ -103,6 +108,8 @@ WORKLOADS = {
                 gated_pairs=True),
     10: Workload(10, "LLaMA-7B attention projections q/k/v/o, 16 tokens, 2 bits/weight",
                  4, 8, 16, list(_LLAMA7B_ATTN)),
+    11: Workload(11, "LLaMA-7B attention projections, q/k/v sharing one codebook and x, "
+                     "2 bits/weight", 4, 8, 1, list(_LLAMA7B_ATTN), shared=((0, 1, 2),)),
 }
 
 
@@ -188,14 +195,32 @@ def draw(K: int, N: int, d: int, nbits: int, B: int, seed: int, *,
     return out
 
 
+def shared_leader(number: int, m: int) -> int:
+    """The matrix whose codebook and x matrix ``m`` uses (``m`` itself unless
+    it belongs to a shared group of the workload)."""
+    for g in WORKLOADS[number].shared:
+        if m in g:
+            return g[0]
+    return m
+
+
 def matrix_inputs(number: int, m: int, rows: Optional[int] = None) -> MatrixInputs:
-    """Inputs of matrix ``m`` of workload ``number`` (see module docstring)."""
+    """Inputs of matrix ``m`` of workload ``number`` (see module docstring).
+    A member of a shared group draws its own indices and takes the group's
+    first matrix's codebook and x."""
     w = WORKLOADS[number]
     spec = w.matrices[m]
-    return draw(spec.K, spec.N, w.d, w.nbits, w.B, seed_for(number, m),
-                residual=w.residual, group=w.group,
-                outlier_frac=w.outlier_frac, outlier_scale=w.outlier_scale,
-                rows=rows)
+    out = draw(spec.K, spec.N, w.d, w.nbits, w.B, seed_for(number, m),
+               residual=w.residual, group=w.group,
+               outlier_frac=w.outlier_frac, outlier_scale=w.outlier_scale,
+               rows=rows)
+    lead = shared_leader(number, m)
+    if lead != m:
+        ls = w.matrices[lead]
+        src = draw(ls.K, ls.N, w.d, w.nbits, w.B, seed_for(number, lead), rows=1,
+                   outlier_frac=w.outlier_frac, outlier_scale=w.outlier_scale)
+        out.x, out.wc = src.x, src.wc
+    return out
 
 
 def small_matrix(K: int, N: int, d: int, nbits: int, B: int = 1, seed: int = 7,
@@ -209,10 +234,11 @@ def weight_bytes(number: int) -> int:
     indices + codebooks (+ packed signs + fp16 alpha)."""
     w = WORKLOADS[number]
     total = 0
-    for s in w.matrices:
+    for m, s in enumerate(w.matrices):
         J = s.K // w.d
         total += (s.N * J * w.nbits + 7) // 8
-        total += (1 << w.nbits) * w.d * 2
+        if shared_leader(number, m) == m:               # a shared codebook counts once
+            total += (1 << w.nbits) * w.d * 2
         if w.residual:
             total += s.N * s.K // 8 + s.N * (s.K // w.group) * 2
     return total

@@ -491,6 +491,68 @@ def test_gemv_swiglu_f16_epilogue():
         assert torch.equal(y16[p].view(torch.int16), y32[p].half().view(torch.int16)), f"pair {p}"
 
 
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_gemv_shared_codebook_units(B):
+    # vq_gemv_shared: matrices that pass the same codebook and x and have the
+    # same shape are served as one unit (their row groups laid end to end,
+    # one staged codebook per workgroup): each within tolerance of the
+    # oracle and bitwise equal to its vq_gemv call alone; a same-shape matrix
+    # with its own codebook, and one of another shape sharing the codebook,
+    # stay apart
+    _say(f"gemv shared-codebook units B={B}")
+    base = synth.small_matrix(2048, 1000, 4, 8, B=B, seed=61)
+    mis = [base] + [synth.small_matrix(2048, 1000, 4, 8, B=B, seed=62 + i) for i in range(2)]
+    for mi in mis[1:]:
+        mi.x, mi.wc = base.x, base.wc
+    own = synth.small_matrix(2048, 1000, 4, 8, B=B, seed=70)
+    other = synth.small_matrix(2048, 333, 4, 8, B=B, seed=71)
+    other.x, other.wc = base.x, base.wc
+    mats = [_upload(mi) for mi in mis] + [_upload(own), _upload(other)]
+    for m in (mats[1], mats[2], mats[4]):
+        m.wc = mats[0].wc
+    x0 = torch.from_numpy(base.x).to(DEV)
+    xt = [x0, x0, x0, torch.from_numpy(own.x).to(DEV), x0]
+    ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
+    vq.vq_gemv_shared(mats, xt, B, ys)
+    torch.cuda.synchronize()
+    for i, (mi, y) in enumerate(zip(mis + [own, other], ys)):
+        got = y.cpu().numpy()
+        _assert_close(got, _oracle_plain(mi), f"shared unit matrix {i} B={B}")
+        alone = torch.full((B, mi.N), float("nan"), dtype=torch.float32, device=DEV)
+        vq.vq_gemv([mats[i]], [xt[i]], B, [alone], None, 0)
+        torch.cuda.synchronize()
+        assert np.array_equal(alone.cpu().numpy().view(np.uint32), got.view(np.uint32)), f"matrix {i}"
+
+
+def test_gemv_workload11_shared_codebook():
+    # LLaMA-7B q/k/v sharing one codebook and x with o alone: every row
+    # against the oracle through vq_gemv (the launch bench.py times) and
+    # through vq_gemv_shared (q/k/v one unit), both bitwise equal to the four
+    # matrices called one by one
+    _say("gemv workload 11 (q/k/v share a codebook and x)")
+    w = synth.workload(11)
+    mis = [synth.matrix_inputs(11, m) for m in range(w.count)]
+    mats = [_upload(mi) for mi in mis]
+    xt = [torch.from_numpy(mi.x).to(DEV) for mi in mis]
+    for m in range(w.count):
+        l = synth.shared_leader(11, m)
+        if l != m:
+            mats[m].wc, xt[m] = mats[l].wc, xt[l]
+    ys = [torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
+    yu = [torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
+    vq.vq_gemv(mats, xt, 1, ys, None, 0)
+    vq.vq_gemv_shared(mats, xt, 1, yu)
+    torch.cuda.synchronize()
+    for m, (mi, y, u) in enumerate(zip(mis, ys, yu)):
+        got = y.cpu().numpy()
+        _assert_close(got, _oracle_plain(mi), f"workload 11 matrix {m}")
+        alone = torch.empty((1, mi.N), dtype=torch.float32, device=DEV)
+        vq.vq_gemv([mats[m]], [xt[m]], 1, [alone], None, 0)
+        torch.cuda.synchronize()
+        assert np.array_equal(alone.cpu().numpy().view(np.uint32), got.view(np.uint32))
+        assert np.array_equal(u.cpu().numpy().view(np.uint32), got.view(np.uint32))
+
+
 def test_gemv_mixed_group():
     _say("gemv mixed shapes in one launch")
     mis = [synth.small_matrix(1024, 300, 4, 8, seed=1), synth.small_matrix(512, 2000, 4, 8, seed=2),

@@ -67,3 +67,16 @@ def test_weight_bytes_per_layer():
     assert synth.weight_bytes(8) == synth.weight_bytes(2) and synth.workload(8).B == 4
     assert synth.weight_bytes(9) == 2 * (11008 * 1024 + 2048) and synth.workload(9).gated_pairs
     assert synth.weight_bytes(10) == synth.weight_bytes(2) and synth.workload(10).B == 16
+    # a codebook shared by q, k and v counts once
+    assert synth.weight_bytes(11) == 4 * 4096 * 1024 + 2 * 2048
+
+
+def test_shared_group_inputs():
+    # members of a shared group take the first matrix's codebook and x and
+    # keep indices of their own; matrices outside the group keep their own
+    import numpy as np
+    q, k, o = (synth.matrix_inputs(11, m, rows=4) for m in (0, 1, 3))
+    assert synth.shared_leader(11, 2) == 0 and synth.shared_leader(11, 3) == 3
+    assert np.array_equal(q.x, k.x) and np.array_equal(q.wc, k.wc)
+    assert not np.array_equal(q.idx, k.idx)
+    assert not np.array_equal(q.wc, o.wc) and not np.array_equal(q.x, o.x)

@@ -73,6 +73,9 @@ _c = {
     "vq_gemv": _sig("vq_gemv", ctypes.c_int,
                     [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                      ctypes.POINTER(_vp), _vp, _sz, _vp]),
+    "vq_gemv_shared": _sig("vq_gemv_shared", ctypes.c_int,
+                           [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
+                            ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "vq_gemv_f16": _sig("vq_gemv_f16", ctypes.c_int,
                         [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                          ctypes.POINTER(_vp), _vp, _sz, _vp]),
@@ -242,6 +245,13 @@ def vq_gemv(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace, ws_by
                          ws_bytes, _stream(stream)), "vq_gemv")
 
 
+def vq_gemv_shared(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace=None,
+                   ws_bytes: int = 0, stream=None) -> None:
+    """vq_gemv with matrices that share codebook, x and shape merged into units."""
+    _check(_c["vq_gemv_shared"](_mat_array(mats), len(mats), _ptr_array(xs), B, _ptr_array(ys),
+                                _ptr(workspace), ws_bytes, _stream(stream)), "vq_gemv_shared")
+
+
 def vq_gemv_f16(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace, ws_bytes: int,
                 stream=None) -> None:
     """vq_gemv storing fp16 y (the fp32 sums rounded to nearest even)."""
@@ -323,8 +333,8 @@ class PreparedCall:
 
 def prepare_gemv(name: str, mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace=None,
                  ws_bytes: int = 0) -> PreparedCall:
-    """A PreparedCall of vq_gemv, vq_gemv_f16 or vq_gemv_residual."""
-    if name not in ("vq_gemv", "vq_gemv_f16", "vq_gemv_residual"):
+    """A PreparedCall of vq_gemv, vq_gemv_shared, vq_gemv_f16 or vq_gemv_residual."""
+    if name not in ("vq_gemv", "vq_gemv_f16", "vq_gemv_residual", "vq_gemv_shared"):
         raise ValueError(name)
     arr, xa, ya = _mat_array(mats), _ptr_array(xs), _ptr_array(ys)
     return PreparedCall(name, (arr, len(mats), xa, B, ya, _ptr(workspace), ws_bytes),

@@ -202,10 +202,62 @@ static size_t wc16_ws_bytes(const vq_matrix &a, int32_t B) {
   return ((size_t)1 << 20) + xb;
 }
 
+// Units of the 8-bit burst kernel: descriptors a.mat[0..count) (one matrix
+// each) merged where matrices share the codebook and x pointers and have
+// the same K and N (so the same split along J).  A unit of several members
+// lists their indices and outputs in u.mwi / u.my from u.a.mat[k].mem0 on
+// and covers nmem * ceil(N/16) row groups.  Returns false when no two
+// matrices share, so the call keeps one descriptor per matrix.
+static bool share_units(const WcArgs &a, WcUnitArgs &u) {
+  int unit_of[VQ_MAX_GROUP];
+  int nu = 0;
+  int lead[VQ_MAX_GROUP];
+  bool any = false;
+  for (int s = 0; s < a.count; ++s) {
+    const WcMat &d = a.mat[s];
+    unit_of[s] = -1;
+    for (int k = 0; k < nu; ++k) {
+      const WcMat &l = a.mat[lead[k]];
+      if (l.wc == d.wc && l.x == d.x && l.J == d.J && l.N == d.N && l.jsplit == d.jsplit) {
+        unit_of[s] = k;
+        any = true;
+        break;
+      }
+    }
+    if (unit_of[s] < 0) {
+      lead[nu] = s;
+      unit_of[s] = nu++;
+    }
+  }
+  if (!any) return false;
+  memset(&u, 0, sizeof(u));
+  u.a.count = nu;
+  int slot = 0;
+  for (int k = 0; k < nu; ++k) {
+    WcMat m = a.mat[lead[k]];
+    int n = 0;
+    for (int s = 0; s < a.count; ++s)
+      if (unit_of[s] == k) {
+        u.mwi[slot + n] = a.mat[s].wi;
+        u.my[slot + n] = a.mat[s].y;
+        ++n;
+      }
+    m.nmem = n;
+    m.mem0 = slot;
+    slot += n;
+    const int64_t ng = (m.N + 15) / 16;
+    const int per_wg = wc8_rows_per_wg(m.jsplit, wc8_burst_waves()) / 16;
+    m.nwg = (int32_t)((n * ng + per_wg - 1) / per_wg);
+    u.a.mat[k] = m;
+  }
+  return true;
+}
+
 // Virtual-OC kernels: whole rows per workgroup; only the 16-bit kernel takes
 // a workspace.
 static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                   void *const *y, bool yf16, void *workspace, size_t ws_bytes, void *stream) {
+                   void *const *y, bool yf16, void *workspace, size_t ws_bytes, void *stream,
+                   bool merge = false) {
   const Format f = format_of(m[0]);
   WcArgs args;
   memset(&args, 0, sizeof(args));
@@ -277,6 +329,18 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     }
     const int prep_blocks = (int)std::min<int64_t>((65536 + maxbj + 255) / 256, 4096);
     return hip_status(launch_wc16t(t, (int)max_wg, prep_blocks, stream));
+  }
+  if (merge && f == FMT_LUT8 && burst && w8 == wc8_burst_waves()) {
+    // vq_gemv_shared: matrices that pass the same codebook and x and have
+    // the same shape become one unit; their row groups are laid end to end,
+    // so a workgroup's staged codebook and x serve rows of several of them.
+    WcUnitArgs u;
+    if (share_units(args, u)) {
+      int64_t uwg = 0;
+      for (int k = 0; k < u.a.count; ++k) uwg = std::max<int64_t>(uwg, u.a.mat[k].nwg);
+      if (uwg > 0x7fffffff) return VQ_EUNSUPPORTED;
+      return hip_status(launch_wc8_units(u, (int)uwg, B, stream));
+    }
   }
   const int err = (f == FMT_LUT8)   ? launch_wc8(args, (int)max_wg, w8, burst, B, stream)
                                     : launch_wc12(args, (int)max_wg, max_j, stream);
@@ -498,6 +562,14 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K, int32_t 
 int vq_gemv(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B, float *const *y,
             void *workspace, size_t ws_bytes, void *stream) {
   return gemv_plain(m, count, x, B, y, workspace, ws_bytes, stream);
+}
+
+int vq_gemv_shared(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                   float *const *y, void *workspace, size_t ws_bytes, void *stream) {
+  const int st = check_group(m, count, x, B, y, false);
+  if (st != VQ_OK) return st;
+  return gemv_wc(m, count, x, B, reinterpret_cast<void *const *>(y), false, workspace, ws_bytes,
+                 stream, true);
 }
 
 int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,

@@ -90,8 +90,8 @@ __device__ __forceinline__ float wreduce_rows16(float (&a)[16], int lane) {
 // kernel arguments before the first one is used, so the scalar loads share
 // one round trip instead of one per dependent use (the early exit, then the
 // split, then the pointers), which the first vector loads would wait for.
-__device__ __forceinline__ WcMat load_wcmat(const WcArgs &args) {
-  const WcMat &R = args.mat[blockIdx.y];
+__device__ __forceinline__ WcMat load_wcmat(const WcArgs &args, int m) {
+  const WcMat &R = args.mat[m];
   WcMat M;
   M.wi = R.wi;
   M.wc = R.wc;
@@ -104,19 +104,23 @@ __device__ __forceinline__ WcMat load_wcmat(const WcArgs &args) {
   M.nwg = R.nwg;
   M.jsplit = R.jsplit;
   M.yf16 = R.yf16;
+  M.nmem = 1;                                 // units read their member fields themselves
+  M.mem0 = 0;
   __asm__ volatile("" ::"s"(M.wi), "s"(M.wc), "s"(M.x), "s"(M.y), "s"(M.J), "s"(M.N), "s"(M.B),
                    "s"(M.ldy), "s"(M.nwg), "s"(M.jsplit), "s"(M.yf16));
   return M;
 }
+__device__ __forceinline__ WcMat load_wcmat(const WcArgs &args) { return load_wcmat(args, blockIdx.y); }
 
 // Output element i of y: the fp32 sum, or (fp16 epilogue) that sum rounded
 // to the nearest fp16, ties to even, for a consumer that reads fp16.
-__device__ __forceinline__ void store_y(const WcMat &M, size_t i, float v) {
-  if (M.yf16)
-    reinterpret_cast<_Float16 *>(M.y)[i] = (_Float16)v;
+__device__ __forceinline__ void store_y(float *y, int yf16, size_t i, float v) {
+  if (yf16)
+    reinterpret_cast<_Float16 *>(y)[i] = (_Float16)v;
   else
-    M.y[i] = v;
+    y[i] = v;
 }
+__device__ __forceinline__ void store_y(const WcMat &M, size_t i, float v) { store_y(M.y, M.yf16, i, v); }
 
 // --------------------------------------------------------------------------
 // d = 4, n = 12, one token
@@ -142,23 +146,27 @@ __device__ __forceinline__ uint2 lds_u2(const char *base, uint32_t byte_addr) {
 }
 
 // One 64-subvector chunk of 16 rows: w[0..2] rows 0-7, w[3..5] rows 8-15.
+// All 16 reads are issued before the first product (16 LDS requests in
+// flight); row r adds its two products in dimension order.
 __device__ __forceinline__ void wc12_chunk(float (&acc)[16], const uint32_t (&w)[6], uint2 xj,
                                            const char *wc) {
-#define WC12_ONE(R, I, A, B, C)                                            \
-  {                                                                        \
-    const uint2 e = lds_u2(wc, wc12_addr<I>(A, B, C));                     \
-    acc[R] = __builtin_amdgcn_fdot2(h2(xj.x), h2(e.x), acc[R], false);     \
-    acc[R] = __builtin_amdgcn_fdot2(h2(xj.y), h2(e.y), acc[R], false);     \
+  uint2 e[16];
+#define WC12_RD(R, I, A, B, C) e[R] = lds_u2(wc, wc12_addr<I>(A, B, C));
+  WC12_RD(0, 0, w[0], w[1], w[2]) WC12_RD(1, 1, w[0], w[1], w[2])
+  WC12_RD(2, 2, w[0], w[1], w[2]) WC12_RD(3, 3, w[0], w[1], w[2])
+  WC12_RD(4, 4, w[0], w[1], w[2]) WC12_RD(5, 5, w[0], w[1], w[2])
+  WC12_RD(6, 6, w[0], w[1], w[2]) WC12_RD(7, 7, w[0], w[1], w[2])
+  WC12_RD(8, 0, w[3], w[4], w[5]) WC12_RD(9, 1, w[3], w[4], w[5])
+  WC12_RD(10, 2, w[3], w[4], w[5]) WC12_RD(11, 3, w[3], w[4], w[5])
+  WC12_RD(12, 4, w[3], w[4], w[5]) WC12_RD(13, 5, w[3], w[4], w[5])
+  WC12_RD(14, 6, w[3], w[4], w[5]) WC12_RD(15, 7, w[3], w[4], w[5])
+#undef WC12_RD
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[r] = __builtin_amdgcn_fdot2(h2(xj.x), h2(e[r].x), acc[r], false);
+    acc[r] = __builtin_amdgcn_fdot2(h2(xj.y), h2(e[r].y), acc[r], false);
   }
-  WC12_ONE(0, 0, w[0], w[1], w[2]) WC12_ONE(1, 1, w[0], w[1], w[2])
-  WC12_ONE(2, 2, w[0], w[1], w[2]) WC12_ONE(3, 3, w[0], w[1], w[2])
-  WC12_ONE(4, 4, w[0], w[1], w[2]) WC12_ONE(5, 5, w[0], w[1], w[2])
-  WC12_ONE(6, 6, w[0], w[1], w[2]) WC12_ONE(7, 7, w[0], w[1], w[2])
-  WC12_ONE(8, 0, w[3], w[4], w[5]) WC12_ONE(9, 1, w[3], w[4], w[5])
-  WC12_ONE(10, 2, w[3], w[4], w[5]) WC12_ONE(11, 3, w[3], w[4], w[5])
-  WC12_ONE(12, 4, w[3], w[4], w[5]) WC12_ONE(13, 5, w[3], w[4], w[5])
-  WC12_ONE(14, 6, w[3], w[4], w[5]) WC12_ONE(15, 7, w[3], w[4], w[5])
-#undef WC12_ONE
 }
 
 __device__ __forceinline__ void load_chunk12(uint32_t (&w)[6], const uint8_t *p) {
@@ -256,51 +264,98 @@ __global__ void __launch_bounds__(W * 64) wc12_kernel(const WcArgs args) {
 // --------------------------------------------------------------------------
 // Same walk as wc12_kernel over the 8-bit tile layout of vq_kernels.hip
 // (chunk (jt, rg): lane l = subvector 64 jt + l, byte i = row 16 rg + i).
-// The codebook (256 x 4 fp16, 2 KiB) is small enough to keep 16 copies in
-// LDS: entry c of copy k at byte 256 c + 8 k.  Lane l reads copy l % 16, so
-// the 16 lanes the LDS serves per cycle of an 8-byte read hit 16 different
-// bank pairs whatever their indices (measured: no slower than 32 copies),
-// and the address is one byte permute (byte 1 = the index, byte 0 =
-// 8 (l % 16)).  No partial sums leave the workgroup: there is no hand-off,
-// no workspace and no bound.
+// The output codebook is formed per index, OC[j][c] = x_j . WC[c], from a
+// codebook (256 x 4 fp16, 2 KiB) kept in LDS as 16 copies: entry c of copy
+// k at byte 256 c + 8 k, so copy k sits in banks 2k and 2k + 1 whatever c
+// is.  Lane l reads copy l % 16; the address is one byte permute (byte 1 =
+// the index, byte 0 = 8 (l % 16)).  Lanes l and l + 16 share a bank pair,
+// so each 64-lane 8-byte read takes two bank-conflict cycles whatever the
+// indices are (rocprofv3: 44% of the LDS-active cycles of the LLaMA-7B
+// q/k/v/o call).  32 copies, one bank pair per lane of a 32-lane half, are
+// conflict-free but measured no faster: staging twice the copies before the
+// first lookup costs what the conflicts save.  No partial sums leave the
+// workgroup: there is no hand-off, no workspace and no bound.
 template <int K>
 __device__ __forceinline__ uint32_t wc8_addr(uint32_t w, uint32_t base) {
   return __builtin_amdgcn_perm(w, base, 0x0C0C0000u | ((4u + K) << 8));
 }
 
-__device__ __forceinline__ void wc8_chunk(float (&acc)[16], const u32x4 &w, uint2 xj, const char *wcr,
-                                          uint32_t base) {
-#define WC8_ONE(R, Q, B)                                                   \
-  {                                                                        \
-    const uint2 e = lds_u2(wcr, wc8_addr<B>(w[Q], base));                  \
-    acc[R] = __builtin_amdgcn_fdot2(h2(xj.x), h2(e.x), acc[R], false);     \
-    acc[R] = __builtin_amdgcn_fdot2(h2(xj.y), h2(e.y), acc[R], false);     \
-  }
-  WC8_ONE(0, 0, 0) WC8_ONE(1, 0, 1) WC8_ONE(2, 0, 2) WC8_ONE(3, 0, 3)
-  WC8_ONE(4, 1, 0) WC8_ONE(5, 1, 1) WC8_ONE(6, 1, 2) WC8_ONE(7, 1, 3)
-  WC8_ONE(8, 2, 0) WC8_ONE(9, 2, 1) WC8_ONE(10, 2, 2) WC8_ONE(11, 2, 3)
-  WC8_ONE(12, 3, 0) WC8_ONE(13, 3, 1) WC8_ONE(14, 3, 2) WC8_ONE(15, 3, 3)
-#undef WC8_ONE
-}
-
 // One chunk for TB tokens: each codebook entry read from LDS serves every
-// token (two dot2 per token).  TB = 1 is wc8_chunk.
+// token (two dot2 per token); row r of token b adds its two products in
+// dimension order.  Up to two tokens, all 16 reads are issued before the
+// first product, so the wave has 16 LDS requests in flight instead of the
+// few the compiler's own schedule keeps (measured 0.1 us faster per
+// LLaMA-7B q/k/v/o call).  For four tokens the read results would push the
+// kernels past the register budget of two workgroups per CU, so each read
+// meets its products at once.
 template <int TB>
 __device__ __forceinline__ void wc8_chunk_tb(float (&acc)[TB][16], const u32x4 &w,
                                              const uint2 (&xj)[TB], const char *wcr, uint32_t base) {
-#define WC8TB_ONE(R, Q, K)                                                   \
-  {                                                                          \
-    const uint2 e = lds_u2(wcr, wc8_addr<K>(w[Q], base));                    \
-    _Pragma("unroll") for (int b = 0; b < TB; ++b) {                         \
-      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].x), h2(e.x), acc[b][R], false); \
-      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].y), h2(e.y), acc[b][R], false); \
-    }                                                                        \
+  if constexpr (TB <= 2) {
+    uint2 e[16];
+#define WC8TB_RD(R, Q, K) e[R] = lds_u2(wcr, wc8_addr<K>(w[Q], base));
+    WC8TB_RD(0, 0, 0) WC8TB_RD(1, 0, 1) WC8TB_RD(2, 0, 2) WC8TB_RD(3, 0, 3)
+    WC8TB_RD(4, 1, 0) WC8TB_RD(5, 1, 1) WC8TB_RD(6, 1, 2) WC8TB_RD(7, 1, 3)
+    WC8TB_RD(8, 2, 0) WC8TB_RD(9, 2, 1) WC8TB_RD(10, 2, 2) WC8TB_RD(11, 2, 3)
+    WC8TB_RD(12, 3, 0) WC8TB_RD(13, 3, 1) WC8TB_RD(14, 3, 2) WC8TB_RD(15, 3, 3)
+#undef WC8TB_RD
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        acc[b][r] = __builtin_amdgcn_fdot2(h2(xj[b].x), h2(e[r].x), acc[b][r], false);
+        acc[b][r] = __builtin_amdgcn_fdot2(h2(xj[b].y), h2(e[r].y), acc[b][r], false);
+      }
+  } else {
+#define WC8TB_ONE(R, Q, K)                                                           \
+  {                                                                                  \
+    const uint2 e = lds_u2(wcr, wc8_addr<K>(w[Q], base));                            \
+    _Pragma("unroll") for (int b = 0; b < TB; ++b) {                                 \
+      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].x), h2(e.x), acc[b][R], false);    \
+      acc[b][R] = __builtin_amdgcn_fdot2(h2(xj[b].y), h2(e.y), acc[b][R], false);    \
+    }                                                                                \
   }
-  WC8TB_ONE(0, 0, 0) WC8TB_ONE(1, 0, 1) WC8TB_ONE(2, 0, 2) WC8TB_ONE(3, 0, 3)
-  WC8TB_ONE(4, 1, 0) WC8TB_ONE(5, 1, 1) WC8TB_ONE(6, 1, 2) WC8TB_ONE(7, 1, 3)
-  WC8TB_ONE(8, 2, 0) WC8TB_ONE(9, 2, 1) WC8TB_ONE(10, 2, 2) WC8TB_ONE(11, 2, 3)
-  WC8TB_ONE(12, 3, 0) WC8TB_ONE(13, 3, 1) WC8TB_ONE(14, 3, 2) WC8TB_ONE(15, 3, 3)
+    WC8TB_ONE(0, 0, 0) WC8TB_ONE(1, 0, 1) WC8TB_ONE(2, 0, 2) WC8TB_ONE(3, 0, 3)
+    WC8TB_ONE(4, 1, 0) WC8TB_ONE(5, 1, 1) WC8TB_ONE(6, 1, 2) WC8TB_ONE(7, 1, 3)
+    WC8TB_ONE(8, 2, 0) WC8TB_ONE(9, 2, 1) WC8TB_ONE(10, 2, 2) WC8TB_ONE(11, 2, 3)
+    WC8TB_ONE(12, 3, 0) WC8TB_ONE(13, 3, 1) WC8TB_ONE(14, 3, 2) WC8TB_ONE(15, 3, 3)
 #undef WC8TB_ONE
+  }
+}
+
+// The 2 KiB codebook of the 8-bit kernels, for workgroups of 8 waves,
+// fetched through the scalar data cache.  Thread t = 64 w + l of such a
+// workgroup writes entry 8 w + l/8 + 64 u (u < 4) into the replicas, so wave
+// w reads four 64-byte blocks with scalar loads (the codebook is not written
+// during the kernel).  Scalar loads do not queue behind the wave's vector
+// index loads: issued before them, and selected into lanes after them, the
+// codebook reaches LDS sooner than through vector loads (measured 0.25 us
+// per LLaMA-7B q/k/v/o call).
+struct Cb8Scalar {
+  uint32_t s[4][16];
+};
+__device__ __forceinline__ void cb8_scalar_issue(Cb8Scalar &c, const uint16_t *wc, int wave) {
+  typedef const __attribute__((address_space(4))) uint32_t cu32;
+  cu32 *cb = (cu32 *)wc;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c.s[u][i] = cb[16 * wave + 128 * u + i];
+}
+// Lane l's entries 8 w + l/8 + 64 u, as the vector path would have loaded them.
+__device__ __forceinline__ void cb8_scalar_select(const Cb8Scalar &c, int lane, uint2 (&ent)[4]) {
+  const int q = lane >> 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    uint32_t a = c.s[u][0], b = c.s[u][1];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      a = (q == k) ? c.s[u][2 * k] : a;
+      b = (q == k) ? c.s[u][2 * k + 1] : b;
+    }
+    ent[u] = uint2{a, b};
+  }
 }
 
 // TB: tokens per call the kernel is built for (1, 2 or 4; B <= TB).  A token
@@ -324,11 +379,20 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
   const int seg = (JT + S - 1) / S;
   const int kbeg = min(sg * seg, JT), kend = min(kbeg + seg, JT);
 
-  // 1. codebook entries for the replicas, then the first PF index chunks and
-  //    x slices: every load is issued before the first wait
+  // 1. codebook entries for the replicas (8 waves and up to two tokens:
+  //    scalar loads; four tokens keep the register budget of vector loads),
+  //    then the first PF index chunks and x slices: every load is issued
+  //    before the first wait
+  constexpr bool kScalarCb = W == 8 && TB <= 2;
   uint2 ent[RP];
+  Cb8Scalar cbs;
+  if constexpr (kScalarCb) {
+    cb8_scalar_issue(cbs, M.wc, wave);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
 #pragma unroll
-  for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
+    for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
+  }
   const uint8_t *wi = M.wi + (size_t)lane * 16;
   const size_t kstride = (size_t)NG * 1024;   // one 64-subvector tile of all row groups
   const uint8_t *wrg = wi + (size_t)rg * 1024;
@@ -344,6 +408,10 @@ __global__ void __launch_bounds__(W * 64) wc8_kernel(const WcArgs args) {
     buf[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrg + (size_t)k * kstride));
 #pragma unroll
     for (int b = 0; b < TB; ++b) xbuf[p][b] = xg[xt[b] + k * 64];
+  }
+  if constexpr (kScalarCb) {
+    __builtin_amdgcn_sched_barrier(0);
+    cb8_scalar_select(cbs, lane, ent);
   }
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
@@ -419,14 +487,17 @@ constexpr int kWcNontemporal = 2;
 // TB: tokens per call the kernel is built for (1, 2 or 4; the call's B <= TB,
 // tokens past B read zeros and are not stored).  Every token's sums are
 // formed in the same order as for one token.
-template <int W, int NCH, int PF0, int TB>
-__global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
+// UNITS: the call merged matrices that share the codebook, x and shape into
+// units (WcUnitArgs); mwi / my list the members' indices and outputs.
+template <int W, int NCH, int PF0, int TB, bool UNITS>
+__device__ __forceinline__ void wc8_burst_body(const WcArgs &args, const WcUnitArgs *ua) {
   constexpr int NT = W * 64;
   constexpr int RP = 2048 / NT;               // 16-byte replica stores per thread
   __shared__ __align__(16) char wcr[256 * 256];
   __shared__ float part[TB][W * 64];
-  const WcMat M = load_wcmat(args);
-  if ((int)blockIdx.x >= M.nwg) return;
+  const int unit = blockIdx.y, bx = blockIdx.x;   // workgroup x of matrix (or unit) y
+  const WcMat M = load_wcmat(args, unit);
+  if (bx >= M.nwg) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lS = 31 - __builtin_clz((unsigned)M.jsplit);   // the split is a power of two
@@ -434,13 +505,30 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
   const int rgl = wave >> lS, sg = wave & (S - 1);
   const int JT = M.J >> 6;
   const int NG = (M.N + 15) >> 4;
-  const int rgw = (int)blockIdx.x * (W >> lS) + rgl;
+  // Row group of the wave.  Matrices that share the codebook, x and their
+  // shape are laid end to end (nmem > 1): row group rgall of the unit is
+  // row group rgall mod NG of member rgall / NG, so one workgroup's staged
+  // codebook and x serve rows of several of them.  Each row's sums keep the
+  // order they have when its matrix is called alone.
+  const int rgall = bx * (W >> lS) + rgl;
+  int rgw = rgall;
+  const uint8_t *wib = M.wi;
+  float *yb = M.y;
+  if constexpr (UNITS) {
+    const int nmem = args.mat[unit].nmem, mem0 = args.mat[unit].mem0;
+    if (nmem > 1) {
+      const int mem = min(rgall / NG, nmem - 1);
+      rgw = rgall - mem * NG;
+      wib = ua->mwi[mem0 + mem];
+      yb = ua->my[mem0 + mem];
+    }
+  }
   const int rg = min(rgw, NG - 1);
   const int seg = (JT + S - 1) >> lS;
   const int kbeg = min(sg * seg, JT), kend = min(kbeg + seg, JT);
   const uint32_t kstride = (uint32_t)NG * 1024u;   // one 64-subvector tile of all row groups
   const __amdgpu_buffer_rsrc_t rwi = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(M.wi + (size_t)rg * 1024), (short)0, (int)(kstride * (uint32_t)JT),
+      const_cast<uint8_t *>(wib + (size_t)rg * 1024), (short)0, (int)(kstride * (uint32_t)JT),
       kWcBufferWord3);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(M.x), (short)0, M.B * M.J * 8, kWcBufferWord3);
@@ -451,10 +539,19 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
     return (k < kend && b < M.B) ? (uint32_t)(b * M.J + k * 64 + lane) * 8u : kWcOutOfRange;
   };
 
-  // 1. codebook entries for the replicas, the x slices, the first PF0 chunks
+  // 1. the codebook (up to two tokens: scalar loads; four tokens keep the
+  //    register budget of vector loads), the x slices, the first PF0 chunks
+  static_assert(W == 8, "the scalar codebook fetch serves workgroups of 8 waves");
+  constexpr bool kScalarCb = TB <= 2;
   uint2 ent[RP];
+  Cb8Scalar cbs;
+  if constexpr (kScalarCb) {
+    cb8_scalar_issue(cbs, M.wc, wave);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
 #pragma unroll
-  for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
+    for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 3];
+  }
   u32x4 buf[NCH];
   uint2 xbuf[NCH][TB];
 #pragma unroll
@@ -466,6 +563,10 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
   for (int p = 0; p < PF0; ++p)
     buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, wi_off(kbeg + p), 0, kWcNontemporal));
   // 2. replicas into LDS (waits for the codebook), then the rest of the segment
+  if constexpr (kScalarCb) {
+    __builtin_amdgcn_sched_barrier(0);
+    cb8_scalar_select(cbs, lane, ent);
+  }
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
     const int s = threadIdx.x + u * NT;       // entry s >> 3, copies 2 (s & 7) and + 1
@@ -508,8 +609,18 @@ __global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
   if ((lane & 3) == 0 && rgw < NG && row < M.N) {
 #pragma unroll
     for (int b = 0; b < TB; ++b)
-      if (b < M.B) store_y(M, (size_t)b * M.ldy + row, v[b]);
+      if (b < M.B) store_y(yb, M.yf16, (size_t)b * M.ldy + row, v[b]);
   }
+}
+
+template <int W, int NCH, int PF0, int TB>
+__global__ void __launch_bounds__(W * 64) wc8_burst_kernel(const WcArgs args) {
+  wc8_burst_body<W, NCH, PF0, TB, false>(args, nullptr);
+}
+
+template <int W, int NCH, int PF0, int TB>
+__global__ void __launch_bounds__(W * 64) wc8_burst_units_kernel(const WcUnitArgs args) {
+  wc8_burst_body<W, NCH, PF0, TB, true>(args.a, &args);
 }
 
 // --------------------------------------------------------------------------
@@ -853,6 +964,8 @@ int wc8_waves(int64_t indices, int max_split, int B) {
   return (B == 1 && indices <= ((int64_t)1 << 20) && max_split <= 4) ? 4 : WC8_W;
 }
 int wc8_rows_per_wg(int jsplit, int waves) { return waves / jsplit * 16; }
+// Waves per workgroup of the burst kernel (the waves for which it is built).
+int wc8_burst_waves() { return WC8_W; }
 // The burst kernel serves a call when every row fits in its waves' chunks
 // and the matrix's indices lie within one 32-bit buffer offset.
 bool wc8_burst_fits(int N, int J, int jsplit) {
@@ -883,6 +996,21 @@ int launch_wc8_swiglu(const WcPairArgs &a, int grid_x, int waves, int B, void *s
     hipLaunchKernelGGL((wc8_swiglu_kernel<2 * WC8_W, WC8_NCH, 2, 1>), grid, dim3(2 * WC8_W * 64), 0, st, a);
   else if (waves == 2 * WC8_W && B == 2)
     hipLaunchKernelGGL((wc8_swiglu_kernel<2 * WC8_W, WC8_NCH, 2, 2>), grid, dim3(2 * WC8_W * 64), 0, st, a);
+  else
+    return (int)hipErrorInvalidConfiguration;
+  return (int)hipGetLastError();
+}
+
+int launch_wc8_units(const WcUnitArgs &a, int grid_x, int B, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // report only this launch's error
+  const dim3 grid(grid_x, a.a.count), block(WC8_W * 64);
+  if (B == 1)
+    hipLaunchKernelGGL((wc8_burst_units_kernel<WC8_W, WC8_NCH, 2, 1>), grid, block, 0, st, a);
+  else if (B == 2)
+    hipLaunchKernelGGL((wc8_burst_units_kernel<WC8_W, WC8_NCH, 2, 2>), grid, block, 0, st, a);
+  else if (B <= 4)
+    hipLaunchKernelGGL((wc8_burst_units_kernel<WC8_W, WC8_NCH, 2, 4>), grid, block, 0, st, a);
   else
     return (int)hipErrorInvalidConfiguration;
   return (int)hipGetLastError();

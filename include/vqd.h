@@ -35,7 +35,9 @@
  *   - Outputs y are fp32 and overwritten (never accumulated into).
  *   - Results are bitwise reproducible run to run: every cross-workgroup
  *     reduction sums in a fixed order.
- *   - Calls are thread-safe; the library holds no mutable global state.
+ *   - Calls are thread-safe; the library holds no mutable global state,
+ *     except the per-GPU device scratch of vq_gemv_residual_noalloc (and its
+ *     address, looked up once per GPU under a lock).
  */
 #ifndef VQD_H
 #define VQD_H
@@ -305,6 +307,33 @@ int vq_gemv_f16(const vq_matrix *m, int32_t count, const uint16_t *const *x,
 int vq_gemv_residual(const vq_matrix *m, int32_t count,
                      const uint16_t *const *x, int32_t B, float *const *y,
                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * vq_gemv_residual for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results (bitwise) as vq_gemv_residual,
+ * with the workspace replaced by a fixed scratch array in the library's
+ * device code, one per GPU, kept until the process ends.  Its first
+ * VQ_NOALLOC_COUNTER_BYTES hold the completion counters and fixed-point
+ * accumulators, which every completed call leaves at zero; the rest of the
+ * VQ_NOALLOC_SCRATCH_BYTES hold float partials and rotated inputs.  No
+ * allocation, free or memset is made: the first call on a GPU looks up the
+ * array's device address once (hipGetSymbolAddress).  A call whose
+ * counters and accumulators need more than VQ_NOALLOC_COUNTER_BYTES, or
+ * whose partials and rotated inputs need more than VQ_NOALLOC_SCRATCH_BYTES
+ * - VQ_NOALLOC_COUNTER_BYTES, returns VQ_EWORKSPACE and enqueues nothing
+ * (the Gemma-2-9B MLP pair 3584 -> 14336 and 14336 -> 3584 needs 0.14 MB
+ * and 1.7 MB of them).  Every call on one GPU
+ * shares that GPU's array: calls that may overlap (different streams
+ * without ordering, or several host threads) race and give wrong results;
+ * order them.  A call that does not complete (a fault) can leave counters
+ * set for every later call in the process.  Other arguments, formats,
+ * limits and errors as vq_gemv_residual.
+ */
+#define VQ_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+#define VQ_NOALLOC_COUNTER_BYTES ((size_t)1 << 20)
+int vq_gemv_residual_noalloc(const vq_matrix *m, int32_t count, const uint16_t *const *x,
+                             int32_t B, float *const *y, void *stream);
 
 /*
  * Gate and up projections of a SiLU-gated MLP with the gating fused (the

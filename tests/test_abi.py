@@ -184,6 +184,22 @@ def test_gemv_residual_validation_errors():
     assert res >= 1024 * 4                       # x_rot at least
 
 
+def test_gemv_residual_noalloc_validation_errors():
+    # every check runs on the host before the scratch is looked up
+    c = vq._c["vq_gemv_residual_noalloc"]
+    arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)
+    ptrs = lambda n, v=FAKE: (ctypes.c_void_p * n)(*([v] * n))
+    assert c(arr([_m()]), 0, ptrs(1), 1, ptrs(1), None) == vq.VQ_EINVAL
+    assert c(arr([_m(signs=None)]), 1, ptrs(1), 1, ptrs(1), None) == vq.VQ_EINVAL
+    assert c(arr([_m()]), 1, ptrs(1), 2, ptrs(1), None) == vq.VQ_EUNSUPPORTED        # one token
+    assert c(arr([_m(alpha=FAKE + 16)]), 1, ptrs(1), 1, ptrs(1), None) == vq.VQ_EALIGN
+    # counters and accumulators beyond VQ_NOALLOC_COUNTER_BYTES (1 MiB): 8 bytes
+    # per row of a split matrix
+    assert c(arr([_m(K=512, N=140000)]), 1, ptrs(1), 1, ptrs(1), None) == vq.VQ_EWORKSPACE
+    # partials beyond the other 3 MiB: 56 splits x 16384 rows x 4 bytes
+    assert c(arr([_m(K=14336, N=16384)]), 1, ptrs(1), 1, ptrs(1), None) == vq.VQ_EWORKSPACE
+
+
 def test_other_entry_points_validate():
     c = vq._c
     assert c["vq_pack_indices"](FAKE, 10, 0, FAKE, None) == vq.VQ_EINVAL

@@ -82,6 +82,9 @@ _c = {
     "vq_gemv_residual": _sig("vq_gemv_residual", ctypes.c_int,
                              [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                               ctypes.POINTER(_vp), _vp, _sz, _vp]),
+    "vq_gemv_residual_noalloc": _sig("vq_gemv_residual_noalloc", ctypes.c_int,
+                                     [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
+                                      ctypes.POINTER(_vp), _vp]),
     "vq_gemv_swiglu": _sig("vq_gemv_swiglu", ctypes.c_int,
                            [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
     "vq_gemv_swiglu_f16": _sig("vq_gemv_swiglu_f16", ctypes.c_int,
@@ -265,6 +268,14 @@ def vq_gemv_residual(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspa
     _check(_c["vq_gemv_residual"](arr, len(mats), _ptr_array(xs), B, _ptr_array(ys),
                                   _ptr(workspace), ws_bytes, _stream(stream)),
            "vq_gemv_residual")
+
+
+def vq_gemv_residual_noalloc(mats: Sequence, xs: Sequence, B: int, ys: Sequence,
+                             stream=None) -> None:
+    """vq_gemv_residual on the library's fixed per-GPU device scratch (no workspace)."""
+    _check(_c["vq_gemv_residual_noalloc"](_mat_array(mats), len(mats), _ptr_array(xs), B,
+                                          _ptr_array(ys), _stream(stream)),
+           "vq_gemv_residual_noalloc")
 
 
 def vq_gemv_swiglu(gates: Sequence, ups: Sequence, xs: Sequence, B: int, ys: Sequence, workspace,

@@ -83,12 +83,16 @@ struct MatPlan {
 struct Plan {
   Lut8Shape shape;
   MatPlan mp[VQ_MAX_GROUP];
+  size_t zero_bytes;   // counters and accumulators: [0, zero_bytes)
   size_t bytes;
   int64_t grid;
 };
 
 // Workspace plan of the residual kernel (the other kernels take none).
-static void make_plan(const vq_matrix *m, int32_t count, int32_t B, Plan &p) {
+// Counters and accumulators come first; partials and rotated inputs start at
+// scratch_base, or right after the counters when scratch_base is 0.
+static void make_plan(const vq_matrix *m, int32_t count, int32_t B, Plan &p,
+                      size_t scratch_base = 0) {
   p.shape = lut8_shape_residual(m, count);
   const int JT = 64;
   size_t off = 0;
@@ -107,6 +111,8 @@ static void make_plan(const vq_matrix *m, int32_t count, int32_t B, Plan &p) {
     q.acc_off = off;
     if (q.nsplit > 1) off += round_up((size_t)q.rows_pad * sizeof(uint64_t), 256);
   }
+  p.zero_bytes = off;
+  if (scratch_base > off) off = scratch_base;
   p.grid = 0;
   for (int i = 0; i < count; ++i) {
     MatPlan &q = p.mp[i];
@@ -354,6 +360,9 @@ static int gemv_plain(const vq_matrix *m, int32_t count, const uint16_t *const *
   return gemv_wc(m, count, x, B, reinterpret_cast<void *const *>(y), false, workspace, ws_bytes, stream);
 }
 
+static int residual_launch(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                           float *const *y, const Plan &p, char *ws, void *stream);
+
 static int gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                          float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   int st = check_group(m, count, x, B, y, true);
@@ -363,7 +372,28 @@ static int gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *cons
   if (p.grid > 0x7fffffff) return VQ_EUNSUPPORTED;
   if (!workspace || ws_bytes < p.bytes) return VQ_EWORKSPACE;
   if (!aligned(workspace, 256)) return VQ_EALIGN;
-  char *ws = static_cast<char *>(workspace);
+  return residual_launch(m, count, x, B, y, p, static_cast<char *>(workspace), stream);
+}
+
+// The residual call on this GPU's fixed device scratch: counters and
+// accumulators within its zero region, partials and rotated inputs above it.
+static int gemv_residual_noalloc(const vq_matrix *m, int32_t count, const uint16_t *const *x,
+                                 int32_t B, float *const *y, void *stream) {
+  int st = check_group(m, count, x, B, y, true);
+  if (st != VQ_OK) return st;
+  Plan p;
+  make_plan(m, count, B, p, VQ_NOALLOC_COUNTER_BYTES);
+  if (p.grid > 0x7fffffff) return VQ_EUNSUPPORTED;
+  if (p.zero_bytes > VQ_NOALLOC_COUNTER_BYTES || p.bytes > VQ_NOALLOC_SCRATCH_BYTES)
+    return VQ_EWORKSPACE;
+  void *ws = nullptr;
+  const int err = noalloc_scratch(&ws);
+  if (err) return hip_status(err);
+  return residual_launch(m, count, x, B, y, p, static_cast<char *>(ws), stream);
+}
+
+static int residual_launch(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                           float *const *y, const Plan &p, char *ws, void *stream) {
   Lut8Args args;
   memset(&args, 0, sizeof(args));
   args.count = count;
@@ -575,6 +605,11 @@ int vq_gemv_shared(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
 int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                      float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   return gemv_residual(m, count, x, B, y, workspace, ws_bytes, stream);
+}
+
+int vq_gemv_residual_noalloc(const vq_matrix *m, int32_t count, const uint16_t *const *x,
+                             int32_t B, float *const *y, void *stream) {
+  return gemv_residual_noalloc(m, count, x, B, y, stream);
 }
 
 int vq_gemv_f16(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,

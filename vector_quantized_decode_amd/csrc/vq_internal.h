@@ -142,6 +142,9 @@ int launch_build_oc(const uint16_t *x, int B, int K, int d, int nbits, const uin
 int launch_rht(const uint16_t *x, const int8_t *sign, int B, int K, int h, float scale,
                float *x_rot, void *stream);
 int launch_fill_u32(uint32_t *p, size_t n, uint32_t v, void *stream);
+// Device address of the calling thread's current GPU's no-allocation scratch
+// (VQ_NOALLOC_SCRATCH_BYTES); returns a hipError_t value.
+int noalloc_scratch(void **out);
 
 // Plain streaming read of up to VQ_MAX_READ device buffers in one launch
 // (measurement only): sink[(m * grid_x + x) * words_per_wg + w] receives the

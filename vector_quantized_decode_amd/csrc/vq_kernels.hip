@@ -43,6 +43,8 @@
 //     on the order in which they arrive (bitwise reproducible).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "vq_internal.h"
 
 namespace vqd {
@@ -602,6 +604,39 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     if ((lane & 1) == 0 && g * W + wave < M.rpw && rp < NP) store_dev(M.partial + (size_t)sp * M.rows_pad + row, rowval[g]);
   }
   split_finish(M, rb, 32 * M.rpw, flag);
+}
+
+// --------------------------------------------------------------------------
+// device scratch of vq_gemv_residual_noalloc
+// --------------------------------------------------------------------------
+// One array per GPU the library runs on, held until the process ends.  Bytes
+// [0, VQ_NOALLOC_COUNTER_BYTES) hold completion counters and fixed-point
+// accumulators: zero when the code object is loaded, and returned to zero by
+// every call that completes (the last workgroup of a row block clears what
+// it used), so no call has to clear them first.  The bytes above hold float
+// partials and rotated inputs, written before they are read in each call.
+static __device__ __align__(256) uint8_t scratch[VQ_NOALLOC_SCRATCH_BYTES];
+
+// Device address of this GPU's scratch (the array's name in host code is a
+// host-side stand-in, not a device address).  Looked up once per device,
+// with that device current, and kept.
+int noalloc_scratch(void **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return 0;
 }
 
 // --------------------------------------------------------------------------

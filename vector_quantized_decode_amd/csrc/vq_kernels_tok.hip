@@ -109,7 +109,7 @@ __device__ __forceinline__ void wc8t_exchange(u32x4 (&v)[8]) {
 }
 
 template <int W, int RW>
-__global__ void __launch_bounds__(W * 64) wc8t_kernel(const WcArgs args) {
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4))) wc8t_kernel(const WcArgs args) {
   constexpr int NT = W * 64;
   constexpr int RP = 4096 / NT;               // 16-byte replica stores per thread
   __shared__ __align__(16) char wcr[256 * 256];
@@ -179,15 +179,23 @@ __global__ void __launch_bounds__(W * 64) wc8t_kernel(const WcArgs args) {
     for (int q = 0; q < 8; ++q)
       xn[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off(k + 1, q), 0, 0));
     __builtin_amdgcn_sched_barrier(0);
+    // product (q, r) in order q-major; its two entries (subvectors 16 g + 2 q
+    // and + 1: bytes 2 (q & 1) and + 1 of word q >> 1) are read one product
+    // ahead, so each LDS read overlaps the previous product
+    auto entries = [&](int q, int r) -> u32x4 {
+      const uint32_t w = ib[r][q >> 1];
+      const uint2 e0 = lds_u2(wcr, wc8t_addr(w, base, 2u * (q & 1)));
+      const uint2 e1 = lds_u2(wcr, wc8t_addr(w, base, 2u * (q & 1) + 1u));
+      return u32x4{e0.x, e0.y, e1.x, e1.y};
+    };
+    u32x4 bnext = entries(0, 0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
-        // subvectors 16 g + 2 q and + 1: bytes 2 (q & 1) and + 1 of word q >> 1
-        const uint32_t w = ib[r][q >> 1];
-        const uint2 e0 = lds_u2(wcr, wc8t_addr(w, base, 2u * (q & 1)));
-        const uint2 e1 = lds_u2(wcr, wc8t_addr(w, base, 2u * (q & 1) + 1u));
-        const u32x4 bw = u32x4{e0.x, e0.y, e1.x, e1.y};
+        const u32x4 bw = bnext;
+        if (q * RW + r + 1 < 8 * RW) bnext = entries((q * RW + r + 1) / RW, (q * RW + r + 1) % RW);
+        __builtin_amdgcn_sched_barrier(0);     // the next reads stay ahead of this product
         const u32x4 xq = xa[q < 4 ? 2 * q : 2 * (q - 4) + 1];
         acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xq),
                                                         __builtin_bit_cast(half8_t, bw), acc[r], 0, 0, 0);

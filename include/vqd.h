@@ -70,7 +70,10 @@ typedef enum { VQ_F16 = 0, VQ_F32 = 1 } vq_dtype;
  *             multiple of 256.  All matrices of one call share (d, nbits).
  *   wi        packed indices in the DEVICE layout made by vq_repack_wi
  *             (16-byte aligned).
- *   wc        fp16 codebook [2^nbits][d] (16-byte aligned).
+ *   wc        fp16 codebook in the DEVICE layout made by vq_repack_wc
+ *             (16-byte aligned): for (4, 8) and (4, 12) that is the
+ *             canonical [2^nbits][d]; for (8, 16) it is dimension-major,
+ *             [8][65536] (element (t, c) = WC[c][t]).
  *   Residual fields (vq_gemv_residual only, (d, nbits) = (4, 8); ignored
  *   by vq_gemv):
  *   signs     sign bits in the DEVICE layout made by vq_repack_signs
@@ -131,6 +134,20 @@ const char *vq_last_error(void);
 size_t vq_wi_device_bytes(int32_t N, int32_t K, int32_t d, int32_t nbits);
 
 /*
+ * Codebook device layout [EVA 2.B: the codebook stays on chip while indices
+ * stream; with 65536 centroids one dimension of it fits in LDS at a time].
+ * vq_wc_device_bytes gives its size (2^nbits * d * 2 bytes, zero for a
+ * format without a kernel).  vq_repack_wc writes it from the canonical fp16
+ * codebook wc [2^nbits][d]: for (8, 16) dimension-major, element t * 65536 + c
+ * = WC[c][t]; for (4, 8) and (4, 12) an unchanged copy.  Both pointers
+ * 16-byte aligned (VQ_EALIGN), not overlapping.  A load-time step,
+ * asynchronous on `stream`, not part of the timed decode.
+ */
+size_t vq_wc_device_bytes(int32_t d, int32_t nbits);
+int vq_repack_wc(const uint16_t *wc, int32_t d, int32_t nbits, void *device_layout,
+                 void *stream);
+
+/*
  * Sign-bit device layout ("tile-32x32-skew"): NP = ceil(N/32) pairs of 16
  * row groups.  Canonical sign byte p of row r holds the bits of weights
  * 8p .. 8p+7 (canonical [N][K/8], bit k%8 = weight k, 1 means +1).  Chunk
@@ -154,8 +171,8 @@ size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group);
 /*
  * Workspace bytes needed by vq_gemv (residual = 0) or vq_gemv_residual
  * (residual = 1) for these matrices and B tokens.  vq_gemv takes none (0)
- * except for (d, nbits) = (8, 16): 1 MiB + B*K*2 bytes (each rounded up to
- * 256) per matrix; the residual call needs its split-K accumulators, completion
+ * except for (d, nbits) = (8, 16): B*K*2 bytes (rounded up to 256) per
+ * matrix; the residual call needs its split-K accumulators, completion
  * counters, float partials for non-finite inputs and the rotated inputs of
  * Hadamard blocks above 2048.  Returns 0 on invalid arguments too.
  *
@@ -245,11 +262,11 @@ int vq_rht(const uint16_t *x, const int8_t *sign, int32_t B, int32_t K,
  *            (4-byte aligned), overwritten.
  *   workspace / ws_bytes  (d, nbits) = (8, 16): at least
  *            vq_workspace_bytes(m, count, B, 0) bytes, 256-byte aligned
- *            (VQ_EWORKSPACE / VQ_EALIGN otherwise): per matrix the codebook
- *            by dimension and x by dimension, rewritten by every call.
+ *            (VQ_EWORKSPACE / VQ_EALIGN otherwise): per matrix x by
+ *            dimension, rewritten by every call.
  *            Other formats: unused (vq_workspace_bytes gives 0); any value.
  * All matrices are served by one kernel launch ((8, 16): a pre-pass that
- * fills the workspace, then the lookup kernel).  Supported:
+ * writes x by dimension into the workspace, then the lookup kernel).  Supported:
  * (d, nbits) = (4, 8) with 1 <= B <= 4, (4, 12) with B == 1, (8, 16) with
  * 1 <= B <= 16 and K <= 65536; 1 <= count <= VQ_MAX_GROUP.  A matrix sums in
  * the same order alone or in a group.

@@ -49,6 +49,10 @@ def test_device_layout_sizes():
     assert vq.vq_wi_device_bytes(20, 256, 8, 16) == 32 * 32 * 2
     assert vq.vq_wi_device_bytes(16, 128, 8, 16) == 0                 # J not a multiple of 32
     assert vq.vq_wi_device_bytes(16, 1024, 4, 10) == 0                # no kernel for (4, 10)
+    assert vq.vq_wc_device_bytes(4, 8) == 2048
+    assert vq.vq_wc_device_bytes(4, 12) == 32768
+    assert vq.vq_wc_device_bytes(8, 16) == 1 << 20
+    assert vq.vq_wc_device_bytes(4, 10) == 0                      # no kernel for (4, 10)
     assert vq.vq_signs_device_bytes(14336, 3584) == 14336 * 448
     assert vq.vq_signs_device_bytes(100, 512) == 128 * 64            # rows padded to 32
     assert vq.vq_alpha_device_bytes(3584, 14336, 128) == 3584 * 112 * 2 + 256   # + header
@@ -88,11 +92,12 @@ def test_gemv_validation_errors():
     assert _gemv([_m(d=8, nbits=16)], ok_x, 17, ok_y, None, 0) == vq.VQ_EUNSUPPORTED  # <= 16 tokens
     # one kernel per call: every matrix of a group has the same (d, nbits)
     assert _gemv([_m(), _m(d=4, nbits=12)], ok_x * 2, 1, ok_y * 2, None, 0) == vq.VQ_EUNSUPPORTED
-    # the 12-bit format takes no workspace; the 16-bit one 1 MiB (the codebook
-    # by dimension) plus B*K*2 bytes (x by dimension) per matrix
+    # the 12-bit format takes no workspace; the 16-bit one B*K*2 bytes (x by
+    # dimension) per matrix, each rounded up to 256
     assert vq.vq_workspace_bytes([_m(d=4, nbits=12)], 1) == 0
-    assert vq.vq_workspace_bytes([_m(d=8, nbits=16)], 16) == (1 << 20) + 16 * 1024 * 2
-    assert vq.vq_workspace_bytes([_m(d=8, nbits=16, K=1280)] * 2, 3) == 2 * ((1 << 20) + 7680)
+    assert vq.vq_workspace_bytes([_m(d=8, nbits=16)], 16) == 16 * 1024 * 2
+    assert vq.vq_workspace_bytes([_m(d=8, nbits=16, K=1280)] * 2, 3) == 2 * 7680
+    assert vq.vq_workspace_bytes([_m(d=8, nbits=16, K=1280)], 1) == 2560
     need16 = vq.vq_workspace_bytes([_m(d=8, nbits=16)], 4)
     assert _gemv([_m(d=8, nbits=16)], ok_x, 4, ok_y, None, 0) == vq.VQ_EWORKSPACE
     assert _gemv([_m(d=8, nbits=16)], ok_x, 4, ok_y, FAKE, need16 - 1) == vq.VQ_EWORKSPACE
@@ -218,6 +223,10 @@ def test_other_entry_points_validate():
     assert c["vq_repack_wi_rows"](FAKE + 8, 64, 1024, FAKE, None) == vq.VQ_EALIGN
     assert c["vq_repack_wi_rows"](FAKE, 64, 1024, FAKE + 4, None) == vq.VQ_EALIGN
     assert c["vq_repack_signs"](FAKE, 64, 1000, FAKE, None) == vq.VQ_EUNSUPPORTED
+    assert c["vq_repack_wc"](None, 8, 16, FAKE, None) == vq.VQ_EINVAL
+    assert c["vq_repack_wc"](FAKE, 4, 10, FAKE, None) == vq.VQ_EUNSUPPORTED
+    assert c["vq_repack_wc"](FAKE + 8, 8, 16, FAKE, None) == vq.VQ_EALIGN
+    assert c["vq_repack_wc"](FAKE, 8, 16, FAKE + 2, None) == vq.VQ_EALIGN
     assert c["vq_repack_alpha"](FAKE, 64, 1024, 100, FAKE, None) == vq.VQ_EINVAL
     assert c["vq_build_oc"](FAKE, 1, 10, 4, 8, FAKE, FAKE, vq.VQ_F32, None) == vq.VQ_EINVAL
     assert c["vq_build_oc"](FAKE, 1, 16, 4, 8, FAKE, FAKE, 7, None) == vq.VQ_EINVAL

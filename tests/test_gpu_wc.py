@@ -91,6 +91,20 @@ def test_repack_wi16_bitexact(N, K):
     assert np.array_equal(dev.cpu().numpy().view(np.uint16), _host_wi16(idx, N, J))
 
 
+@pytest.mark.parametrize("d,nbits", [(8, 16), (4, 8), (4, 12)])
+def test_repack_wc_bitexact(d, nbits):
+    # (8, 16): dimension-major, element t * 65536 + c = WC[c][t]; the other
+    # formats keep the canonical layout
+    _say(f"repack codebook d={d} n={nbits}")
+    rng = np.random.default_rng(d * 100 + nbits)
+    wc = rng.integers(0, 65536, size=(1 << nbits, d), dtype=np.uint16)
+    dev = torch.full((vq.vq_wc_device_bytes(d, nbits) // 2,), 0x5A5A, dtype=torch.int16, device=DEV)
+    vq.vq_repack_wc(torch.from_numpy(wc.view(np.int16)).to(DEV), d, nbits, dev)
+    torch.cuda.synchronize()
+    want = wc.T.reshape(-1) if (d, nbits) == (8, 16) else wc.reshape(-1)
+    assert np.array_equal(dev.cpu().numpy().view(np.uint16), want)
+
+
 # ------------------------------------------------------------------ GEMV
 def _run(mats, xs, B):
     ys = [torch.full((B, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]

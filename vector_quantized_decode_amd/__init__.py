@@ -57,6 +57,8 @@ _c = {
     "vq_last_error": _sig("vq_last_error", ctypes.c_char_p, []),
     "vq_wi_device_bytes": _sig("vq_wi_device_bytes", _sz, [_i32, _i32, _i32, _i32]),
     "vq_signs_device_bytes": _sig("vq_signs_device_bytes", _sz, [_i32, _i32]),
+    "vq_wc_device_bytes": _sig("vq_wc_device_bytes", _sz, [_i32, _i32]),
+    "vq_repack_wc": _sig("vq_repack_wc", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "vq_alpha_device_bytes": _sig("vq_alpha_device_bytes", _sz, [_i32, _i32, _i32]),
     "vq_workspace_bytes": _sig("vq_workspace_bytes", _sz,
                                [ctypes.POINTER(vq_matrix), _i32, _i32, _i32]),
@@ -145,6 +147,15 @@ def vq_last_error() -> str:
 
 def vq_wi_device_bytes(N: int, K: int, d: int, nbits: int) -> int:
     return _c["vq_wi_device_bytes"](N, K, d, nbits)
+
+
+def vq_wc_device_bytes(d: int, nbits: int) -> int:
+    return _c["vq_wc_device_bytes"](d, nbits)
+
+
+def vq_repack_wc(wc, d: int, nbits: int, device_layout, stream=None) -> None:
+    _check(_c["vq_repack_wc"](_ptr(wc), d, nbits, _ptr(device_layout), _stream(stream)),
+           "vq_repack_wc")
 
 
 def vq_signs_device_bytes(N: int, K: int) -> int:
@@ -393,7 +404,7 @@ def upload_matrix(idx, wc, K: int, N: int, d: int, nbits: int, *, sign_bits=None
     """Copy host inputs to the device and build the device layouts with the
     library's pack and repack kernels.
 
-    idx: integer array [N][K/d]; wc: fp16 [2^n][d]; sign_bits: {0,1} [N][K];
+    idx: integer array [N][K/d]; wc: fp16 [2^n][d] (laid out by vq_repack_wc); sign_bits: {0,1} [N][K];
     alpha: fp16 [N][K/group]; rht_sign: int8 [K].  tokens: lay WI out in row
     tiles (vq_repack_wi_rows, what vq_gemv_tokens reads) instead of vq_repack_wi's layout.
     """
@@ -410,7 +421,9 @@ def upload_matrix(idx, wc, K: int, N: int, d: int, nbits: int, *, sign_bits=None
         wi = torch.empty(vq_wi_device_bytes(N, K, d, nbits), dtype=torch.uint8, device=device)
         vq_repack_wi(canon, N, K, d, nbits, wi, stream)
     wc_t = torch.from_numpy(np.ascontiguousarray(wc, dtype=np.float16)).to(device)
-    m = DeviceMatrix(K, N, d, nbits, wi, wc_t)
+    wc_dev = torch.empty(vq_wc_device_bytes(d, nbits) // 2, dtype=torch.float16, device=device)
+    vq_repack_wc(wc_t, d, nbits, wc_dev, stream)
+    m = DeviceMatrix(K, N, d, nbits, wi, wc_dev)
     if sign_bits is not None:
         sb = torch.from_numpy(np.ascontiguousarray(sign_bits, dtype=np.uint8).astype(np.int32)).to(device)
         canon_s = torch.empty(N * K // 8, dtype=torch.uint8, device=device)

@@ -201,11 +201,10 @@ static int check_group(const vq_matrix *m, int32_t count, const uint16_t *const 
   return VQ_OK;
 }
 
-// Workspace of the 16-bit kernel: per matrix the codebook split by
-// dimension (1 MiB) and x's values by dimension (B K fp16), 256-byte aligned.
+// Workspace of the 16-bit kernel: per matrix x's values by dimension
+// (B K fp16), 256-byte aligned.
 static size_t wc16_ws_bytes(const vq_matrix &a, int32_t B) {
-  const size_t xb = ((size_t)B * a.K * 2 + 255) / 256 * 256;
-  return ((size_t)1 << 20) + xb;
+  return ((size_t)B * a.K * 2 + 255) / 256 * 256;
 }
 
 // Units of the 8-bit burst kernel: descriptors a.mat[0..count) (one matrix
@@ -328,12 +327,11 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
     char *w = static_cast<char *>(workspace);
     for (int s = 0; s < count; ++s) {
       const vq_matrix &a = m[order[s]];
-      t.wct[s] = reinterpret_cast<uint16_t *>(w);
-      t.xt[s] = reinterpret_cast<uint16_t *>(w + ((size_t)1 << 20));
+      t.xt[s] = reinterpret_cast<uint16_t *>(w);
       w += wc16_ws_bytes(a, B);
       maxbj = std::max<int64_t>(maxbj, (int64_t)B * (a.K / a.d));
     }
-    const int prep_blocks = (int)std::min<int64_t>((65536 + maxbj + 255) / 256, 4096);
+    const int prep_blocks = (int)std::min<int64_t>((maxbj + 255) / 256, 4096);
     return hip_status(launch_wc16t(t, (int)max_wg, prep_blocks, stream));
   }
   if (merge && f == FMT_LUT8 && burst && w8 == wc8_burst_waves()) {
@@ -474,6 +472,24 @@ size_t vq_wi_device_bytes(int32_t N, int32_t K, int32_t d, int32_t nbits) {
     case FMT_WC16: return (J % 32) ? 0 : rows * (size_t)J * 2;
     default: return 0;
   }
+}
+
+size_t vq_wc_device_bytes(int32_t d, int32_t nbits) {
+  if (format_of(d, nbits) == FMT_NONE) return 0;
+  return ((size_t)1 << nbits) * (size_t)d * 2;
+}
+
+int vq_repack_wc(const uint16_t *wc, int32_t d, int32_t nbits, void *device_layout, void *stream) {
+  if (!wc || !device_layout) return VQ_EINVAL;
+  const Format f = format_of(d, nbits);
+  if (f == FMT_NONE) return VQ_EUNSUPPORTED;
+  if (!aligned(wc, 16) || !aligned(device_layout, 16)) return VQ_EALIGN;
+  if (f != FMT_WC16) {                 // the canonical layout is the device layout
+    const size_t n = vq_wc_device_bytes(d, nbits);
+    return hip_status((int)hipMemcpyAsync(device_layout, wc, n, hipMemcpyDeviceToDevice,
+                                          reinterpret_cast<hipStream_t>(stream)));
+  }
+  return hip_status(launch_repack_wc16(wc, static_cast<uint16_t *>(device_layout), stream));
 }
 
 size_t vq_signs_device_bytes(int32_t N, int32_t K) {

@@ -84,11 +84,11 @@ struct WcPairArgs {
   const uint16_t *wc2[VQ_MAX_GROUP];
 };
 
-// The 16-bit kernel's per-matrix scratch (in the caller's workspace): the
-// codebook split by dimension and x's values in the order the kernel reads.
+// The 16-bit kernel's per-matrix scratch (in the caller's workspace): x's
+// values by dimension in the order the kernel reads them.  The codebook
+// (WcMat::wc) is in the dimension-major layout of vq_repack_wc.
 struct Wc16tArgs {
   WcArgs a;
-  uint16_t *wct[VQ_MAX_GROUP];   // [8][65536] fp16
   uint16_t *xt[VQ_MAX_GROUP];    // [8][B][K/8] fp16
 };
 
@@ -113,6 +113,7 @@ int wc16t_jsplit(int J);
 int wc16t_rows_per_wg(int jsplit);
 bool wc16t_fits(int N, int J, int jsplit);
 int launch_wc16t(const Wc16tArgs &a, int grid_x, int prep_blocks, void *stream);
+int launch_repack_wc16(const uint16_t *wc, uint16_t *wct, void *stream);
 int launch_repack_wi12(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
 int launch_repack_wi16(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);
 

@@ -745,32 +745,33 @@ __global__ void __launch_bounds__(W * 64) wc8_swiglu_kernel(const WcPairArgs arg
 // y[b][r] = sum_t sum_j x[b][8 j + t] WC[c_rj][t]: for each dimension t the
 // table WC[.][t] (65536 fp16, 128 KiB) fits in LDS, and the contraction over
 // j runs on the matrix cores with x's dimension-t values as A and the looked-
-// up table values as B.  A pre-pass writes the tables (dimension-major) and
-// x's dimension-t values in the order the A operand reads them.
-//   wct[t][c]                      = WC[c][t]
+// up table values as B.  The codebook comes in its load-time dimension-major
+// layout (vq_repack_wc: wct[t][c] = WC[c][t]); a pre-pass writes x's
+// dimension-t values in the order the A operand reads them:
 //   xt[t][b][jb][s][i] (16 B runs) = x[b][8 (32 jb + s + 4 i) + t]
 __global__ void wc16_prep_kernel(const Wc16tArgs args) {
   const WcMat &M = args.a.mat[blockIdx.y];
-  uint16_t *wct = args.wct[blockIdx.y];
   uint16_t *xt = args.xt[blockIdx.y];
   const int J = M.J, JB = J >> 5;
   const int64_t nx = (int64_t)M.B * J;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < 65536 + nx;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    if (e < 65536) {
-      const u32x4 v = reinterpret_cast<const u32x4 *>(M.wc)[e];
+  for (int64_t f = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; f < nx;
+       f += (int64_t)gridDim.x * blockDim.x) {
+    const int b = (int)(f / J), j = (int)(f % J);
+    const u32x4 v = reinterpret_cast<const u32x4 *>(M.x + (size_t)b * J * 8)[j];
+    const int jb = j >> 5, r = j & 31, sub = r & 3, i = r >> 2;
+    const size_t pos = ((size_t)b * JB + jb) * 32 + sub * 8 + i;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) wct[(size_t)t * 65536 + e] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
-    } else {
-      const int64_t f = e - 65536;
-      const int b = (int)(f / J), j = (int)(f % J);
-      const u32x4 v = reinterpret_cast<const u32x4 *>(M.x + (size_t)b * J * 8)[j];
-      const int jb = j >> 5, r = j & 31, sub = r & 3, i = r >> 2;
-      const size_t pos = ((size_t)b * JB + jb) * 32 + sub * 8 + i;
+    for (int t = 0; t < 8; ++t)
+      xt[(size_t)t * M.B * J + pos] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
+  }
+}
+
+// Load-time layout of a (d = 8, n = 16) codebook: wct[t][c] = WC[c][t].
+__global__ void repack_wc16_kernel(const uint16_t *wc, uint16_t *wct) {
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < 65536; c += gridDim.x * blockDim.x) {
+    const u32x4 v = reinterpret_cast<const u32x4 *>(wc)[c];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        xt[(size_t)t * M.B * J + pos] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
-    }
+    for (int t = 0; t < 8; ++t) wct[(size_t)t * 65536 + c] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
   }
 }
 
@@ -780,7 +781,7 @@ __global__ void __launch_bounds__(W * 64) wc16t_kernel(const Wc16tArgs args) {
   __shared__ __align__(16) _Float16 tbl[65536];
   const WcMat M = load_wcmat(args.a);
   if ((int)blockIdx.x >= M.nwg) return;
-  const uint16_t *wct = args.wct[blockIdx.y];
+  const uint16_t *wct = M.wc;                         // dimension-major (vq_repack_wc)
   const uint16_t *xt = args.xt[blockIdx.y];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1052,6 +1053,13 @@ int wc16t_rows_per_wg(int jsplit) { return 16 / jsplit * 16; }
 bool wc16t_fits(int N, int J, int jsplit) {
   return (J / 32 + jsplit - 1) / jsplit <= 16 && (int64_t)((N + 15) / 16) * (J / 32) * 1024 < ((int64_t)1 << 31);
 }
+int launch_repack_wc16(const uint16_t *wc, uint16_t *wct, void *stream) {
+  (void)hipGetLastError();  // report only this launch's error
+  hipLaunchKernelGGL(repack_wc16_kernel, dim3(256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     wc, wct);
+  return (int)hipGetLastError();
+}
+
 int launch_wc16t(const Wc16tArgs &a, int grid_x, int prep_blocks, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error

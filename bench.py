@@ -346,27 +346,37 @@ def main():
     # vq_repack_alpha, rotation signs uniform over +-1.
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 * args.workload + 99)
+    # each matrix's copies are drawn by one generator call and sliced (all
+    # slices stay 16-byte aligned): a few launches per matrix, not per copy
+    nc = copies - 1
+    draws = []
+    for mm, m in enumerate(base):
+        d = {"wi": torch.randint(0, 256, (nc, *m.wi.shape), dtype=torch.uint8, device=dev,
+                                 generator=gen)}
+        if lead[mm] == mm:
+            d["wc"] = (torch.randn((nc, *m.wc.shape), generator=gen, device=dev,
+                                   dtype=torch.float32) * 0.02).half()
+        if residual:
+            d["signs"] = torch.randint(0, 256, (nc, *m.signs.shape), dtype=torch.uint8, device=dev,
+                                       generator=gen)
+            d["alpha"] = (torch.rand((nc, m.N, m.K // m.group), generator=gen, device=dev,
+                                     dtype=torch.float32) * 0.009 + 0.001).half()
+            d["rht"] = torch.randint(0, 2, (nc, m.K), generator=gen, device=dev,
+                                     dtype=torch.int8) * 2 - 1
+        draws.append(d)
     layers = [base]
     for c in range(1, copies):
         lay = []
         for mm, m in enumerate(base):
-            wc = (lay[lead[mm]].wc if lead[mm] != mm else
-                  (torch.randn(m.wc.shape, generator=gen, device=dev, dtype=torch.float32)
-                   * 0.02).half())
-            cp = vq.DeviceMatrix(m.K, m.N, m.d, m.nbits,
-                                 torch.randint(0, 256, m.wi.shape, dtype=torch.uint8, device=dev,
-                                               generator=gen), wc)
+            d = draws[mm]
+            wc = lay[lead[mm]].wc if lead[mm] != mm else d["wc"][c - 1]
+            cp = vq.DeviceMatrix(m.K, m.N, m.d, m.nbits, d["wi"][c - 1], wc)
             if residual:
-                cp.signs = torch.randint(0, 256, m.signs.shape, dtype=torch.uint8, device=dev,
-                                         generator=gen)
-                G = m.K // m.group
-                al = (torch.rand((m.N, G), generator=gen, device=dev, dtype=torch.float32)
-                      * 0.009 + 0.001).half()
+                cp.signs = d["signs"][c - 1]
                 cp.alpha = torch.empty_like(m.alpha)
-                vq.vq_repack_alpha(al, m.N, m.K, m.group, cp.alpha)
+                vq.vq_repack_alpha(d["alpha"][c - 1], m.N, m.K, m.group, cp.alpha)
                 cp.group, cp.had_block = m.group, m.had_block
-                cp.rht_sign = (torch.randint(0, 2, (m.K,), generator=gen, device=dev,
-                                             dtype=torch.int8) * 2 - 1)
+                cp.rht_sign = d["rht"][c - 1]
             lay.append(cp)
         layers.append(lay)
     ydt = torch.float16 if f16_out else torch.float32

@@ -17,8 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvqd.so")
 ARCH = os.environ.get("VQD_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["vq_api.cpp", "vq_kernels.hip", "vq_kernels_wc.hip", "vq_kernels_tok.hip",
-           "vq_kernels_read.hip"]
+SOURCES = ["vq_api.cpp", "vq_shapes.cpp", "vq_kernels.hip", "vq_kernels_wc.hip",
+           "vq_kernels_tok.hip", "vq_kernels_read.hip"]
 
 
 def hipcc() -> str:

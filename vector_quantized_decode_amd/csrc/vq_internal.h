@@ -9,6 +9,15 @@
 
 namespace vqd {
 
+// Launch shapes shared by the kernels' launchers and the host shape rules.
+constexpr int WC12_W = 4;      // waves per workgroup, 12-bit kernel
+constexpr int WC12_PF = 2;     // chunks in flight per wave, 12-bit kernel
+constexpr int WC8_W = 8;       // waves per workgroup, 8-bit kernels
+constexpr int WC8_NCH = 4;     // chunks per wave of the burst kernel
+constexpr int TK_W = 8;        // waves per workgroup, token kernel
+constexpr int RD_W = 8;        // waves per workgroup, streaming read (as the 8-bit lookup kernels)
+constexpr int RD_NCH = 4;      // 1 KiB chunks per wave, streaming read (as the burst kernel)
+
 // Per-matrix descriptor of the 8-bit lookup GEMV kernels.  Lives in the
 // kernel-argument segment; all pointers are device pointers.
 struct Lut8Mat {
@@ -106,6 +115,7 @@ int wc8_swiglu_waves(int max_split);
 int launch_wc8_swiglu(const WcPairArgs &a, int grid_x, int waves, int B, void *stream);
 int wc8t_jsplit(int J, int B);
 int wc8t_max_rw(int B);
+int wc8t_max_cols(int B);
 int wc8t_rows_per_wg(int jsplit, int rw);
 int launch_wc8t(const WcArgs &a, int grid_x, int rw, void *stream);
 int launch_repack_wi8_rows(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);

@@ -12,8 +12,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int RD_W = 8;                 // waves per workgroup (as the 8-bit lookup kernels)
-constexpr int RD_NCH = 4;               // 1 KiB chunks per wave (as the 8-bit burst kernel)
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNontemporal = 2;
 
@@ -44,13 +42,6 @@ __global__ void __launch_bounds__(RD_W * 64) stream_read_kernel(const ReadArgs a
 }
 
 }  // namespace
-
-int64_t stream_read_workgroups(uint32_t max_bytes) {
-  const int64_t per_wg = (int64_t)RD_W * RD_NCH * 1024;
-  return ((int64_t)max_bytes + per_wg - 1) / per_wg;
-}
-
-int stream_read_sink_words_per_wg() { return RD_W; }
 
 int launch_stream_read(const ReadArgs &a, int grid_x, void *stream) {
   (void)hipGetLastError();  // report only this launch's error

@@ -20,7 +20,6 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TK_W = 8;                      // waves per workgroup
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every record: loads zeros
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNontemporal = 2;
@@ -259,24 +258,6 @@ __global__ void repack_wi8_rows_kernel(const uint8_t *canon, int N, int J, uint8
 // --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
-// Columns of 64 subvectors per wave and the most row groups per wave: more
-// tokens mean more x per column, which more row groups per wave share, and
-// shorter segments keep more waves on the rows (measured on 4 x 4096 x 4096:
-// up to 12 tokens four columns and two row groups, above that two columns
-// and four row groups).
-static int wc8t_max_cols(int B) { return B > 12 ? 2 : 4; }
-int wc8t_max_rw(int B) { return B > 12 ? 4 : 2; }
-// Waves per row group along J for the token kernel: the smallest power of
-// two (at most 8) that leaves each wave at most wc8t_max_cols(B) columns.  It
-// depends on the row length and the token count alone, so a matrix sums in
-// the same order alone or in a group.
-int wc8t_jsplit(int J, int B) {
-  const int jt = J / 64, cols = wc8t_max_cols(B);
-  int s = 1;
-  while (s < TK_W && (jt + s - 1) / s > cols) s *= 2;
-  return s;
-}
-int wc8t_rows_per_wg(int jsplit, int rw) { return TK_W / jsplit * rw * 16; }
 int launch_repack_wi8_rows(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream) {
   const int64_t total = (int64_t)(J >> 6) * ((N + 15) >> 4) * 64;
   int64_t blocks = (total + 255) / 256;

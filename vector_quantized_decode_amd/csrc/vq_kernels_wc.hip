@@ -929,51 +929,6 @@ static int wgrid(int64_t work, int block) {
   return (int)g;
 }
 
-constexpr int WC12_W = 4;
-constexpr int WC12_PF = 2;
-constexpr int WC8_W = 8;       // waves per workgroup, 8-bit kernels
-constexpr int WC8_NCH = 4;     // chunks per wave of the burst kernel
-
-int wc12_rows_per_wg(int jsplit) { return WC12_W / jsplit * 16; }
-// Waves per row group along J for the 12-bit kernel.  Two chunks in flight
-// per wave and short segments measured fastest: with fewer loads queued the
-// codebook and each wave's first chunks come back sooner.
-int wc12_jsplit(int J) {
-  const int JT = J / 64;
-  return JT <= 12 ? 1 : (JT <= 24 ? 2 : 4);
-}
-// Waves per row group along J for the 8-bit kernels: the smallest power of
-// two (at most 8) that leaves each wave at most four 64-subvector chunks,
-// doubled while the matrix has fewer than 64 workgroups of 8 waves and the
-// row has chunks to spare.  It depends on the matrix alone, so a matrix sums
-// in the same order alone or in a group, whichever kernel serves the group.
-int wc8_jsplit(int N, int J) {
-  const int64_t ng = (N + 15) / 16;
-  const int jt = J / 64;
-  int s = 1;
-  while (s < WC8_W && (jt + s - 1) / s > WC8_NCH) s *= 2;
-  while (2 * s <= WC8_W && 2 * s <= jt && (ng * s + WC8_W - 1) / WC8_W < 64 &&
-         (jt <= 2 || (jt + 2 * s - 1) / (2 * s) >= 2))
-    s *= 2;
-  return s;
-}
-// Waves per workgroup: 8, or 4 for one-token calls of at most 2^20 indices
-// whose splits allow it (there more, smaller workgroups start sooner; measured 2.7 against
-// 3.1 us for one 512 x 512 matrix).  Only the number of row groups per
-// workgroup changes, not the order of any sum.
-int wc8_waves(int64_t indices, int max_split, int B) {
-  return (B == 1 && indices <= ((int64_t)1 << 20) && max_split <= 4) ? 4 : WC8_W;
-}
-int wc8_rows_per_wg(int jsplit, int waves) { return waves / jsplit * 16; }
-// Waves per workgroup of the burst kernel (the waves for which it is built).
-int wc8_burst_waves() { return WC8_W; }
-// The burst kernel serves a call when every row fits in its waves' chunks
-// and the matrix's indices lie within one 32-bit buffer offset.
-bool wc8_burst_fits(int N, int J, int jsplit) {
-  const int64_t bytes = (int64_t)((N + 15) / 16) * 1024 * (J / 64);
-  return (J / 64 + jsplit - 1) / jsplit <= WC8_NCH && bytes < ((int64_t)1 << 31);
-}
-
 int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   (void)max_j;
   (void)hipGetLastError();  // report only this launch's error
@@ -982,9 +937,6 @@ int launch_wc12(const WcArgs &a, int grid_x, int max_j, void *stream) {
   return (int)hipGetLastError();
 }
 
-// Waves of the fused gate/up kernel: two row-group slots per output row
-// group, so 8 waves for a split of up to 4 and 16 for a split of 8.
-int wc8_swiglu_waves(int max_split) { return max_split <= 4 ? WC8_W : 2 * WC8_W; }
 int launch_wc8_swiglu(const WcPairArgs &a, int grid_x, int waves, int B, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error
@@ -1039,20 +991,6 @@ int launch_wc8(const WcArgs &a, int grid_x, int waves, bool burst, int B, void *
   return (int)hipGetLastError();
 }
 
-// Waves per row group along J for the 16-bit kernel: the smallest power of
-// two (at most 16) that leaves each wave at most 16 blocks of 32 subvectors
-// (its indices stay in registers for the eight passes).
-int wc16t_jsplit(int J) {
-  const int JB = J / 32;
-  int s = 1;
-  while (s < 16 && (JB + s - 1) / s > 16) s *= 2;
-  return s;
-}
-int wc16t_rows_per_wg(int jsplit) { return 16 / jsplit * 16; }
-// Rows of at most 256 blocks (K <= 65536), indices within 32-bit offsets.
-bool wc16t_fits(int N, int J, int jsplit) {
-  return (J / 32 + jsplit - 1) / jsplit <= 16 && (int64_t)((N + 15) / 16) * (J / 32) * 1024 < ((int64_t)1 << 31);
-}
 int launch_repack_wc16(const uint16_t *wc, uint16_t *wct, void *stream) {
   (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(repack_wc16_kernel, dim3(256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),

@@ -1,134 +1,155 @@
-"""Offline 3.125-bit quantizer: rotated vector quantization plus a 1-bit residual.
+"""Offline 3.125-bit quantizer for the rotated-residual decode path.
 
-Produces, from a weight matrix W [N][K], the inputs vq_gemv_residual decodes:
-an fp16 codebook of 256 centroids of dimension 4, one 8-bit index per block of
-4 rotated weights, one residual sign per weight and one fp16 scale per group of
-128 weights, together with the rotation (a random +-1 diagonal and the
-Hadamard block size).  It follows the pipeline of "Replacing MatMul with SRAM
-lookup: a 3-bit edge inference architecture" (section details: randomized
-Hadamard rotation of W, blocks of D = 4, K-means with K = 256, residual, its
-signs, an optimal scale per group of G = 128, dense sign packing).  It runs on
-the host in numpy, once per weight matrix; nothing of it is on the decode path.
+From a weight matrix W [N][K] it makes what vq_gemv_residual decodes: a 256 x 4
+fp16 codebook, an 8-bit codeword per group of 4 consecutive rotated weights,
+one sign bit per weight and one fp16 scale per 128 weights of a row, plus the
+rotation (a random +-1 diagonal and a Hadamard block size).  The method is the
+3.125-bit edge format of "Replacing MatMul with SRAM lookup: a 3-bit edge
+inference architecture" (section details): rotate the weights by a randomized
+Hadamard transform, cluster their 4-vectors into 256 centroids, and encode
+what the centroids miss with one sign per weight and one scale per 128.  It
+runs on the host in numpy, once per matrix, off the decode path.
 
 Readings where that page is silent:
-  * The rotation is the one the decode applies to x: x_rot = Q^T x with
-    Q^T = blockdiag(H_h) diag(s) / sqrt(h), H_h the Sylvester Hadamard matrix
-    of the largest power of two h dividing K; so W_rot = W Q and
-    W_rot x_rot = W x.
-  * "Sensitivity-aware" K-means weighs each weight's squared error by a
-    sensitivity; none is known for synthetic weights, so the default weighs
-    all weights equally (plain Lloyd iterations).  A sensitivity array can be
-    passed; it weighs both the assignment distances and the centroid means.
-  * A zero residual takes the sign +1 (bit 1).
-  * The optimal scale of a group is the one minimizing its (weighted) squared
-    error sum w (R - alpha s)^2 with s = sign(R): alpha = sum w |R| / sum w.
+  * The rotation is the decode's own: the decode rotates x into
+    x' = blockdiag(H_h) diag(s) x / sqrt(h), H_h the Sylvester Hadamard matrix
+    of the largest power of two h dividing K.  Turning every row of W the
+    same way keeps the product: W' x' = W x.
+  * The page weighs the clustering by weight sensitivity; synthetic weights
+    have none, so every coordinate weighs 1 unless a sensitivity array is
+    given, which then weighs both the nearest-centroid search and the
+    centroid updates (weighted Lloyd rounds).
+  * A coordinate the centroid matches exactly gets sign bit 1 (+1).
+  * Each group's scale is the one that minimizes its weighted squared error
+    between the miss and scale * sign, i.e. the weighted mean of |miss|.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 
 __all__ = ["Quantized", "rotate_rows", "quantize_rotated_residual"]
 
+QUAD = 4            # weights per codeword
+TABLE = 256         # codebook entries (8-bit codewords)
+SCALE_GROUP = 128   # weights sharing one residual scale
+_CHUNK = 8192       # 4-vectors per distance evaluation (bounds the temporary array)
+
 
 @dataclass
 class Quantized:
     wc: np.ndarray          # float16 [256][4] codebook
-    idx: np.ndarray         # uint8 [N][K/4] centroid of each block of 4 rotated weights
+    idx: np.ndarray         # uint8 [N][K/4] codeword of each group of 4 rotated weights
     sign_bits: np.ndarray   # uint8 {0,1} [N][K], 1 means +1
-    alpha: np.ndarray       # float16 [N][K/group]
+    alpha: np.ndarray       # float16 [N][K/group] residual scales
     rht_sign: np.ndarray    # int8 {-1,+1} [K]
     had_block: int
     group: int
-    objective: List[float] = field(default_factory=list)   # K-means objective per iteration
+    objective: List[float] = field(default_factory=list)   # clustering error after each round
 
 
-def _fwht_last(a: np.ndarray, h: int) -> np.ndarray:
-    """Unnormalized Walsh-Hadamard transform (Sylvester order) of every
-    length-h block along the last axis, by radix-2 butterflies."""
-    out = np.array(a, dtype=np.float64, copy=True)
-    lead = out.shape[:-1]
-    K = out.shape[-1]
-    v = out.reshape(*lead, K // h, h)
-    step = 1
-    while step < h:
-        v = v.reshape(*lead, K // h, h // (2 * step), 2, step)
-        top = v[..., 0, :].copy()
-        bot = v[..., 1, :].copy()
-        v[..., 0, :] = top + bot
-        v[..., 1, :] = top - bot
-        step *= 2
-    return v.reshape(*lead, K)
+# ------------------------------------------------------------------ rotation
+def _hadamard_blocks(a: np.ndarray, h: int) -> np.ndarray:
+    """Each length-h block along the last axis of ``a`` multiplied by the
+    (unnormalized) Sylvester Hadamard matrix H_h: log2 h rounds of pairwise
+    sums and differences, pair distance 1, 2, 4, ..."""
+    x = np.array(a, dtype=np.float64, copy=True)
+    shape = x.shape
+    span = 1
+    while span < h:
+        pairs = x.reshape(-1, 2, span)          # [..., first half, second half] of each 2*span run
+        lo = pairs[:, 0, :].copy()
+        pairs[:, 0, :] += pairs[:, 1, :]
+        pairs[:, 1, :] = lo - pairs[:, 1, :]
+        x = pairs.reshape(shape)
+        span *= 2
+    return x
 
 
 def rotate_rows(W: np.ndarray, rht_sign: np.ndarray, h: int) -> np.ndarray:
-    """W_rot = W Q with Q = diag(s) blockdiag(H_h) / sqrt(h), row by row."""
-    Ws = np.asarray(W, dtype=np.float64) * rht_sign.astype(np.float64)[None, :]
-    return _fwht_last(Ws, h) / np.sqrt(h)
+    """Every row w of W turned to w' = blockdiag(H_h) diag(s) w / sqrt(h)."""
+    flipped = np.asarray(W, dtype=np.float64) * rht_sign.astype(np.float64)[None, :]
+    return _hadamard_blocks(flipped, h) / np.sqrt(h)
 
 
-def _kmeans(blocks: np.ndarray, sens: np.ndarray, k: int, iters: int,
-            rng: np.random.Generator):
-    """Weighted Lloyd iterations on the rows of ``blocks`` (n x D); ``sens``
-    (n x D) weighs each coordinate's squared error.  Returns centroids,
-    assignments and the objective after each assignment step."""
-    n = blocks.shape[0]
-    cent = blocks[rng.choice(n, size=k, replace=n < k)].copy()
-    hist: List[float] = []
-    assign = np.zeros(n, dtype=np.int64)
-    for _ in range(iters):
-        # weighted distance sum_t w_t (v_t - c_t)^2, in chunks of rows
-        for a in range(0, n, 8192):
-            v, w = blocks[a:a + 8192], sens[a:a + 8192]
-            d = (w[:, None, :] * (v[:, None, :] - cent[None, :, :]) ** 2).sum(axis=2)
-            assign[a:a + 8192] = d.argmin(axis=1)
-        err = (sens * (blocks - cent[assign]) ** 2).sum()
-        hist.append(float(err))
-        # weighted means; an empty centroid keeps its place
-        num = np.zeros_like(cent)
-        den = np.zeros_like(cent)
-        np.add.at(num, assign, sens * blocks)
-        np.add.at(den, assign, sens)
-        filled = den > 0
-        cent[filled] = num[filled] / den[filled]
-    return cent, assign, hist
+# ------------------------------------------------------------------ clustering
+def _nearest(vecs: np.ndarray, weight: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Index of the table row with the least weighted squared distance, per row of vecs."""
+    out = np.empty(vecs.shape[0], dtype=np.int64)
+    for lo in range(0, vecs.shape[0], _CHUNK):
+        v, w = vecs[lo:lo + _CHUNK], weight[lo:lo + _CHUNK]
+        dist = np.einsum("nkd,nd->nk", (v[:, None, :] - table[None, :, :]) ** 2, w)
+        out[lo:lo + _CHUNK] = dist.argmin(axis=1)
+    return out
 
 
+def _lloyd(vecs: np.ndarray, weight: np.ndarray, seeds: np.ndarray,
+           rounds: int) -> Tuple[np.ndarray, np.ndarray, List[float]]:
+    """Weighted Lloyd rounds from the initial table ``seeds``: each round
+    assigns every vector its nearest entry, records the weighted error, and
+    moves every used entry to the weighted mean of its vectors (an unused one
+    stays put)."""
+    table = seeds.copy()
+    trace: List[float] = []
+    code = np.zeros(vecs.shape[0], dtype=np.int64)
+    for _ in range(rounds):
+        code = _nearest(vecs, weight, table)
+        trace.append(float((weight * (vecs - table[code]) ** 2).sum()))
+        wsum = np.zeros_like(table)
+        wvec = np.zeros_like(table)
+        np.add.at(wsum, code, weight)
+        np.add.at(wvec, code, weight * vecs)
+        used = wsum > 0
+        table[used] = wvec[used] / wsum[used]
+    return table, code, trace
+
+
+# ------------------------------------------------------------------ residual
+def _sign_scale(miss: np.ndarray, weight: np.ndarray, group: int) -> Tuple[np.ndarray, np.ndarray]:
+    """One bit per weight (1 where the miss is >= 0) and, per group of
+    ``group`` weights of a row, the scale minimizing the weighted error
+    sum w (miss - a sign)^2: a = sum w |miss| / sum w."""
+    N, K = miss.shape
+    bits = (miss >= 0).astype(np.uint8)
+    num = (weight * np.abs(miss)).reshape(N, K // group, group).sum(axis=2)
+    den = weight.reshape(N, K // group, group).sum(axis=2)
+    return bits, num / np.maximum(den, 1e-300)
+
+
+# ------------------------------------------------------------------ the format
 def quantize_rotated_residual(W: np.ndarray, *, seed: int = 0, iters: int = 12,
-                              sensitivity: Optional[np.ndarray] = None, group: int = 128,
-                              d: int = 4, k: int = 256) -> Quantized:
-    """Quantize W [N][K] to the 3.125-bit format (d = 4, k = 256, group = 128)."""
-    W = np.asarray(W, dtype=np.float64)
-    N, K = W.shape
-    if d != 4 or k != 256 or group != 128:
+                              sensitivity: Optional[np.ndarray] = None, group: int = SCALE_GROUP,
+                              d: int = QUAD, k: int = TABLE) -> Quantized:
+    """Quantize W [N][K] to the 3.125-bit format the residual decode reads
+    (d = 4, 256 codebook entries, one scale per 128 weights); ``iters``
+    Lloyd rounds from ``k`` seed vectors drawn from the matrix."""
+    if d != QUAD or k != TABLE or group != SCALE_GROUP:
         raise ValueError("the decode kernels take d = 4, 256 centroids and groups of 128")
+    weights = np.asarray(W, dtype=np.float64)
+    N, K = weights.shape
     if K % 256:
         raise ValueError("K must be a multiple of 256")
     rng = np.random.default_rng(seed)
-    rht_sign = np.where(rng.integers(0, 2, size=K) == 1, 1, -1).astype(np.int8)
+    diag = np.where(rng.integers(0, 2, size=K) == 1, 1, -1).astype(np.int8)
     h = K & (-K)
-    W_rot = rotate_rows(W, rht_sign, h)
+    turned = rotate_rows(weights, diag, h)
 
-    blocks = W_rot.reshape(N * (K // d), d)
-    sens = (np.ones_like(blocks) if sensitivity is None
-            else np.asarray(sensitivity, dtype=np.float64).reshape(N * (K // d), d))
-    cent, assign, hist = _kmeans(blocks, sens, k, iters, rng)
+    quads = turned.reshape(-1, QUAD)
+    if sensitivity is None:
+        wq = np.ones_like(quads)
+    else:
+        wq = np.asarray(sensitivity, dtype=np.float64).reshape(-1, QUAD)
+    seeds = quads[rng.choice(quads.shape[0], size=TABLE, replace=quads.shape[0] < TABLE)]
+    table, _, trace = _lloyd(quads, wq, seeds, iters)
 
-    # the decode reads the codebook in fp16: each block takes its nearest fp16
-    # centroid, and the residual is taken against it
-    wc = cent.astype(np.float16)
-    wc64 = wc.astype(np.float64)
-    for a in range(0, blocks.shape[0], 8192):
-        v, w = blocks[a:a + 8192], sens[a:a + 8192]
-        assign[a:a + 8192] = (w[:, None, :] * (v[:, None, :] - wc64[None, :, :]) ** 2).sum(axis=2).argmin(axis=1)
-    approx = wc64[assign].reshape(N, K)
-    residual = W_rot - approx
-    sign_bits = (residual >= 0).astype(np.uint8)
-    sw = sens.reshape(N, K)
-    g_abs = (sw * np.abs(residual)).reshape(N, K // group, group).sum(axis=2)
-    g_w = sw.reshape(N, K // group, group).sum(axis=2)
-    alpha = (g_abs / np.maximum(g_w, 1e-300)).astype(np.float16)
-    return Quantized(wc=wc, idx=assign.reshape(N, K // d).astype(np.uint8), sign_bits=sign_bits,
-                     alpha=alpha, rht_sign=rht_sign, had_block=h, group=group, objective=hist)
+    # the decode holds the table in fp16, so codewords are chosen against the
+    # rounded table, and the residual encodes what that table misses
+    table16 = table.astype(np.float16)
+    code = _nearest(quads, wq, table16.astype(np.float64))
+    miss = turned - table16.astype(np.float64)[code].reshape(N, K)
+    bits, scale = _sign_scale(miss, wq.reshape(N, K), group)
+    return Quantized(wc=table16, idx=code.reshape(N, K // QUAD).astype(np.uint8), sign_bits=bits,
+                     alpha=scale.astype(np.float16), rht_sign=diag, had_block=h, group=group,
+                     objective=trace)

@@ -99,26 +99,35 @@ def parse():
                    help="fp16 outputs (the fp16 epilogue: vq_gemv_f16, vq_gemv_swiglu_f16)")
     p.add_argument("--dense-only", action="store_true",
                    help="only the dense fp16 GEMV context run (prints its JSON)")
+    p.add_argument("--call", choices=["default", "oc"], default="default",
+                   help="oc: time vq_gemv_oc (the output-codebook tile form) instead of vq_gemv "
+                        "(d=4, n=8, one token, no residual)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return p.parse_args()
 
 
-def kernel_source_sha(workload: int) -> str:
-    with open(os.path.join(CSRC, KERNEL_SRC[workload]), "rb") as f:
+OC_SRC = "vq_kernels.hip"  # source of vq_gemv_oc's kernel
+
+
+def kernel_source_sha(workload: int, call: str = "default") -> str:
+    src = OC_SRC if call == "oc" else KERNEL_SRC[workload]
+    with open(os.path.join(CSRC, src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def committed_traffic(workload: int):
+def committed_traffic(workload: int, call: str = "default"):
     """HBM bytes per launch of the lookup kernel from the committed counter
-    summary of this workload, if it was taken on the current kernel source."""
-    sha = kernel_source_sha(workload)
+    summary of this workload and call, if it was taken on the current kernel
+    source."""
+    sha = kernel_source_sha(workload, call)
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         text = open(path).read()
-        m = re.search(r"traffic-record: workload=(\d+) kernel_sha=(\w+) "
+        m = re.search(r"traffic-record: workload=(\d+)(?: call=(\w+))? kernel_sha=(\w+) "
                       r"fetch_bytes=([\d.]+) write_bytes=([\d.]+)", text)
-        if m and int(m.group(1)) == workload and m.group(2) == sha:
-            return float(m.group(3)) + float(m.group(4)), os.path.basename(path)
+        if m and int(m.group(1)) == workload and (m.group(2) or "default") == call \
+                and m.group(3) == sha:
+            return float(m.group(4)) + float(m.group(5)), os.path.basename(path)
     return None, None
 
 
@@ -318,6 +327,12 @@ def main():
     if f16_out and (residual or tokens):
         say("--f16-out applies to the plain and fused gate/up workloads")
         sys.exit(2)
+    # the plain one-token 8-bit workloads, which vq_gemv_oc also serves
+    oc_able = (wl.d, wl.nbits, wl.B) == (4, 8, 1) and not residual and not wl.gated_pairs
+    oc = args.call == "oc"
+    if oc and (not oc_able or f16_out):
+        say("--call oc applies to plain d=4, n=8, one-token workloads with fp32 outputs")
+        sys.exit(2)
     layer_bytes = synth.weight_bytes(args.workload)
     K = args.steps
     c0 = args.copies or min(MAX_COPIES, max(1, -(-COPY_BYTES // layer_bytes)))
@@ -381,7 +396,7 @@ def main():
         layers.append(lay)
     ydt = torch.float16 if f16_out else torch.float32
     ys = [torch.empty((wl.B, m.N), dtype=ydt, device=dev) for m in base]
-    ws = vq.alloc_workspace(base, wl.B, residual=residual, device=dev)
+    ws = vq.alloc_workspace(base, wl.B, residual=residual or oc, device=dev)
 
     prepared = {}
 
@@ -396,7 +411,8 @@ def main():
             # gate/up pairs share the gate's x and write one gated output per pair
             pc = vq.prepare_gemv_swiglu(lay[0::2], lay[1::2], xs[0::2], wl.B, ys[0::2], f16=f16_out)
         else:
-            name = "vq_gemv_residual" if residual else ("vq_gemv_f16" if f16_out else "vq_gemv")
+            name = ("vq_gemv_residual" if residual else "vq_gemv_oc" if oc
+                    else "vq_gemv_f16" if f16_out else "vq_gemv")
             pc = vq.prepare_gemv(name, lay, xs, wl.B, ys, ws, ws.numel())
         prepared[c] = pc
         return pc
@@ -523,6 +539,25 @@ def main():
             timing["vq_gemv_shared"] = dict(ms_, what="the same calls with the matrices that "
                                                       "share a codebook and x merged into units")
             say(f"# vq_gemv_shared (merged units): {ms_['us_per_call']:.3f} us/layer")
+        if oc_able and not oc and not f16_out:
+            # the same calls in the output-codebook tile form (vq_gemv_oc)
+            ws_oc = vq.alloc_workspace(base, wl.B, residual=True, device=dev)
+            oc_calls = {}
+
+            def oc_for(c):
+                if c not in oc_calls:
+                    oc_calls[c] = vq.prepare_gemv("vq_gemv_oc", layers[c], xs, wl.B, ys, ws_oc,
+                                                  ws_oc.numel())
+                return oc_calls[c]
+
+            ot = Timer(torch, oc_for, copies, K, stream)
+            ot.warm(args.warmup)
+            os_ = summary(ot.time(args.repeats), K)
+            del ot
+            timing["vq_gemv_oc"] = dict(os_, what="the same calls in the output-codebook tile "
+                                                  "form: an OC tile per workgroup in LDS, rows "
+                                                  "split along K, a fixed-point atomic per row")
+            say(f"# vq_gemv_oc (output-codebook tiles): {os_['us_per_call']:.3f} us/layer")
         timing["stream_read"] = dict(rs, bytes_per_call=read_bytes,
                                      what="vq_stream_read over each copy's device index layouts"
                                           + (", signs and scales" if residual else ""))
@@ -587,7 +622,7 @@ def main():
                "us_per_layer": round(med * 1e6, 1)}
         say(f"# cpu oracle: {med * 1e3:.1f} ms/layer over {len(reps)} runs")
 
-    traffic, traffic_src = committed_traffic(args.workload)
+    traffic, traffic_src = committed_traffic(args.workload, args.call)
     if f16_out:
         traffic, traffic_src = None, None   # the counters were taken with fp32 outputs
     roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
@@ -596,7 +631,7 @@ def main():
             "launches_per_call": 2 if wl.nbits == 16 else 1,
             "algorithmic_bytes_per_launch": layer_bytes,
             "traffic_source": traffic_src,
-            "kernel_source_sha": kernel_source_sha(args.workload)}
+            "kernel_source_sha": kernel_source_sha(args.workload, args.call)}
     if read_gbs is not None:
         roof["stream_read_gbs"] = round(read_gbs, 2)
         roof["frac_of_stream_read"] = round(gbs / read_gbs, 4)
@@ -619,6 +654,7 @@ def main():
                    "K_N": [[s.K, s.N] for s in wl.matrices], "d": wl.d, "nbits": wl.nbits,
                    "B": wl.B, "weight_bytes_per_layer": layer_bytes, "layer_copies": copies,
                    "distinct_codebooks_per_copy": True, "launch": "hip graph",
+                   "call": "vq_gemv_oc" if oc else "default",
                    "operands": "f16", "accumulate": "f32", "y": "f16" if f16_out else "f32"},
         "timing": timing,
         "roofline": roof,

@@ -169,8 +169,8 @@ size_t vq_signs_device_bytes(int32_t N, int32_t K);
 size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group);
 
 /*
- * Workspace bytes needed by vq_gemv (residual = 0) or vq_gemv_residual
- * (residual = 1) for these matrices and B tokens.  vq_gemv takes none (0)
+ * Workspace bytes needed by vq_gemv (residual = 0) or by vq_gemv_residual
+ * and vq_gemv_oc (residual = 1) for these matrices and B tokens.  vq_gemv takes none (0)
  * except for (d, nbits) = (8, 16): B*K*2 bytes (rounded up to 256) per
  * matrix; the residual call needs its split-K accumulators, completion
  * counters, float partials for non-finite inputs and the rotated inputs of
@@ -178,8 +178,8 @@ size_t vq_alpha_device_bytes(int32_t N, int32_t K, int32_t group);
  *
  * A workspace serves one call kind on one group of matrices: the (m, count,
  * B, residual) it was sized for.  Set it up with vq_workspace_init before
- * the first call of that kind and group; every vq_gemv_residual call on that
- * group that completes leaves its completion counters and accumulators at
+ * the first call of that kind and group; every vq_gemv_residual or
+ * vq_gemv_oc call on that group that completes leaves its counters and accumulators at
  * zero again, so further calls on the same group need no set-up.  Before
  * the same buffer serves another group or another call kind, call
  * vq_workspace_init again: the residual call places its counters at offsets
@@ -308,6 +308,32 @@ int vq_gemv_shared(const vq_matrix *m, int32_t count, const uint16_t *const *x,
 int vq_gemv_f16(const vq_matrix *m, int32_t count, const uint16_t *const *x,
                 int32_t B, uint16_t *const *y, void *workspace, size_t ws_bytes,
                 void *stream);
+
+/*
+ * VQ GEMV in the output-codebook form [EVA 2.A, 2.B]: the y of vq_gemv,
+ * computed as the pages lay it out.  Each workgroup forms the output
+ * codebook tile OC[j][c] = x_j . WC[c] of 64 subvectors and all 256
+ * centroids in LDS (fp32, on the matrix cores), stored so that subvector
+ * j's entries sit in LDS bank j mod 64 and lane j always reads them: the 64
+ * lookups of a wave hit 64 different banks whatever the indices.  Rows are
+ * split along K into tiles of 256 inputs; the workgroups sharing a row add
+ * their partial sums with one fixed-point atomic per row (integer adds, so
+ * the result does not depend on arrival order and is bitwise reproducible)
+ * and the last one stores the row.  The sums run in another order than
+ * vq_gemv's, so the two agree within rounding, not bitwise.
+ *   Arguments as vq_gemv.  workspace / ws_bytes: at least
+ *   vq_workspace_bytes(m, count, B, 1) bytes, 256-byte aligned, set up by
+ *   vq_workspace_init, under the residual call's rules (a completed call
+ *   leaves the counters and accumulators at zero again).  Supported: (d,
+ *   nbits) = (4, 8), B == 1, K a multiple of 256, the vq_repack_wi index
+ *   layout that vq_gemv reads, and below 2^31 bytes of device indices per
+ *   matrix.  On MI355X vq_gemv, which forms each entry when an index asks
+ *   for it and needs no cross-workgroup hand-off, measured faster; this
+ *   call keeps the pages' formulation available and measurable.
+ */
+int vq_gemv_oc(const vq_matrix *m, int32_t count, const uint16_t *const *x,
+               int32_t B, float *const *y, void *workspace, size_t ws_bytes,
+               void *stream);
 
 /*
  * Rotated VQ GEMV plus 1-bit residual [EDGE section details]: with

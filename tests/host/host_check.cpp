@@ -19,7 +19,7 @@
 
 // ------------------------------------------------------------------ stand-ins
 namespace {
-enum Kind { NONE, WC8, WC8_UNITS, WC12, WC16T, SWIGLU, WC8T, RESIDUAL, READ, OTHER };
+enum Kind { NONE, WC8, WC8_UNITS, WC12, WC16T, SWIGLU, WC8T, RESIDUAL, OCTILE, READ, OTHER };
 struct Last {
   Kind kind = NONE;
   int grid_x = 0, waves = 0, B = 0, rw = 0, prep_blocks = 0;
@@ -86,8 +86,8 @@ int launch_wc16t(const Wc16tArgs &a, int grid_x, int prep_blocks, void *) {
   last.kind = WC16T; last.w16 = a; last.grid_x = grid_x; last.prep_blocks = prep_blocks;
   return 0;
 }
-int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *) {
-  last.kind = RESIDUAL; last.res = a; last.shape = s; last.grid_x = grid_x;
+int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *, bool residual) {
+  last.kind = residual ? RESIDUAL : OCTILE; last.res = a; last.shape = s; last.grid_x = grid_x;
   return 0;
 }
 int launch_rht(const uint16_t *, const int8_t *, int, int, int, float, float *, void *) {
@@ -369,6 +369,53 @@ void check_residual() {
   }
 }
 
+// The output-codebook form of the plain call: the residual kernel with no
+// rotation, signs or scales, on the residual call's workspace plan.
+void check_oc() {
+  const std::vector<std::vector<int>> groups[] = {{{4096, 4096, 4096, 4096}, {4096, 4096, 4096, 4096}},
+                                                  {{256, 11008, 33024}, {17, 4096, 40}},
+                                                  {{512}, {512}}};
+  for (const auto &g : groups) {
+    const int n = (int)g[0].size();
+    std::vector<vq_matrix> m;
+    for (int i = 0; i < n; ++i) {
+      vq_matrix q = mat(g[0][i], g[1][i]);
+      q.signs = nullptr; q.alpha = nullptr;         // not read by this call
+      q.wi = P(0x1000000 * (i + 1));
+      m.push_back(q);
+    }
+    std::vector<const uint16_t *> x(n, static_cast<const uint16_t *>(P(0x400000)));
+    std::vector<float *> y(n, static_cast<float *>(P(0x800000)));
+    const size_t need = vq_workspace_bytes(m.data(), n, 1, 1);
+    CHECK(need > 0, "oc workspace");
+    const uintptr_t ws = FAKE + 0x40000000;
+    CHECK(vq_gemv_oc(m.data(), n, x.data(), 1, y.data(), reinterpret_cast<void *>(ws), need, nullptr) == VQ_OK,
+          "oc group K0=%d", g[0][0]);
+    CHECK(last.kind == OCTILE, "oc kind");
+    for (int i = 0; i < n; ++i) {
+      const vqd::Lut8Mat &d = last.res.mat[i];
+      CHECK(!d.signs && !d.alpha && !d.alpha_hdr && !d.rs, "oc matrix %d reads residual inputs", i);
+      CHECK(d.had == 1 && d.fused == 1, "oc matrix %d rotates", i);
+    }
+    check_residual_regions(ws, need, need, m.data(), n);
+    CHECK(vq_gemv_oc(m.data(), n, x.data(), 1, y.data(), reinterpret_cast<void *>(ws), need - 1, nullptr) ==
+              VQ_EWORKSPACE, "short oc workspace");
+    CHECK(vq_gemv_oc(m.data(), n, x.data(), 2, y.data(), reinterpret_cast<void *>(ws), need, nullptr) ==
+              VQ_EUNSUPPORTED, "oc with two tokens");
+  }
+  vq_matrix q = mat(4096, 4096, 4, 12);
+  const uint16_t *x1[] = {static_cast<const uint16_t *>(P(0x400000))};
+  float *y1[] = {static_cast<float *>(P(0x800000))};
+  CHECK(vq_gemv_oc(&q, 1, x1, 1, y1, reinterpret_cast<void *>(FAKE + 0x40000000), (size_t)1 << 30, nullptr) ==
+            VQ_EUNSUPPORTED, "oc with 12-bit indices");
+  q = mat(4096, 2097152);                         // 2^31 bytes of device indices
+  CHECK(vq_gemv_oc(&q, 1, x1, 1, y1, reinterpret_cast<void *>(FAKE + 0x40000000), (size_t)1 << 30, nullptr) ==
+            VQ_EUNSUPPORTED, "oc past 2^31 index bytes");
+  q = mat(4096, 2097120);                         // the largest row count below it
+  CHECK(vq_gemv_oc(&q, 1, x1, 1, y1, reinterpret_cast<void *>(FAKE + 0x40000000), (size_t)1 << 30, nullptr) ==
+            VQ_OK, "oc just below 2^31 index bytes");
+}
+
 void check_stream_read() {
   const size_t sizes[] = {16, 1 << 20, 4194304, 12845056, ((size_t)1 << 31) - 16};
   std::vector<const void *> b(5, P());
@@ -389,6 +436,7 @@ int main() {
   check_plain_shapes();
   check_tokens();
   check_residual();
+  check_oc();
   check_stream_read();
   if (failures) {
     fprintf(stderr, "%d host check(s) failed\n", failures);

@@ -189,6 +189,22 @@ def test_gemv_residual_validation_errors():
     assert res >= 1024 * 4                       # x_rot at least
 
 
+def test_gemv_oc_validation_errors():
+    c = vq._c["vq_gemv_oc"]
+    arr = lambda ms: (vq.vq_matrix * len(ms))(*ms)
+    ptrs = lambda n, v=FAKE: (ctypes.c_void_p * n)(*([v] * n))
+    ws = vq.vq_workspace_bytes([_m(signs=None, alpha=None)], 1, residual=True)
+    assert ws > 0
+    assert c(arr([_m()]), 0, ptrs(1), 1, ptrs(1), FAKE, ws, None) == vq.VQ_EINVAL
+    assert c(arr([_m()]), 1, ptrs(1), 2, ptrs(1), FAKE, ws, None) == vq.VQ_EUNSUPPORTED   # one token
+    assert c(arr([_m(d=4, nbits=12)]), 1, ptrs(1), 1, ptrs(1), FAKE, ws, None) == vq.VQ_EUNSUPPORTED
+    assert c(arr([_m(K=65536, N=131072)]), 1, ptrs(1), 1, ptrs(1), FAKE, 1 << 30, None) == vq.VQ_EUNSUPPORTED
+    assert c(arr([_m()]), 1, ptrs(1), 1, ptrs(1), None, 0, None) == vq.VQ_EWORKSPACE
+    assert c(arr([_m()]), 1, ptrs(1), 1, ptrs(1), FAKE, ws - 1, None) == vq.VQ_EWORKSPACE
+    assert c(arr([_m()]), 1, ptrs(1), 1, ptrs(1), FAKE + 16, ws, None) == vq.VQ_EALIGN
+    assert c(arr([_m(wi=FAKE + 8)]), 1, ptrs(1), 1, ptrs(1), FAKE, ws, None) == vq.VQ_EALIGN
+
+
 def test_gemv_residual_noalloc_validation_errors():
     # every check runs on the host before the scratch is looked up
     c = vq._c["vq_gemv_residual_noalloc"]

@@ -1,9 +1,9 @@
 """Graph replay of the library's calls (the way bench.py times them).
 
-A HIP graph captured from vq_gemv / vq_gemv_residual / vq_gemv_swiglu must give, on every
+A HIP graph captured from vq_gemv / vq_gemv_oc / vq_gemv_residual / vq_gemv_swiglu must give, on every
 replay, bitwise the result of the same call made eagerly: the calls record
-only kernels (no memset nodes), the residual call's counters and
-accumulators are left at zero by every call, and the 16-bit call rewrites
+only kernels (no memset nodes), the residual and output-codebook calls'
+counters and accumulators are left at zero by every call, and the 16-bit call rewrites
 its workspace each time.  Each replay follows eager work of its own (the
 outputs poisoned with NaN, an unrelated eager call) and a synchronization.
 """
@@ -33,6 +33,9 @@ def _case(kind):
     if kind == "residual":
         mis = [synth.small_matrix(1024, 200, 4, 8, seed=34, residual=True),
                synth.small_matrix(3584, 96, 4, 8, seed=35, residual=True)]
+        return mis, 1, True
+    if kind == "oc":
+        mis = [synth.small_matrix(4096, 700, 4, 8, seed=47), synth.small_matrix(768, 300, 4, 8, seed=48)]
         return mis, 1, True
     if kind == "wc12":
         return [synth.small_matrix(1024, 300, 4, 12, seed=36)], 1, False
@@ -64,12 +67,13 @@ def _upload(mi, residual, tokens=False):
     return vq.upload_matrix(mi.idx, mi.wc, mi.K, mi.N, mi.d, mi.nbits, device=DEV)
 
 
-@pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "wc12", "wc16", "swiglu",
+@pytest.mark.parametrize("kind", ["lut8", "lut8_tokens", "residual", "oc", "wc12", "wc16", "swiglu",
                                   "tokens16", "tokens5", "f16"])
 def test_graph_replays_match_eager(kind):
     print(f"[graph] {kind}", flush=True)
     mis, B, residual = _case(kind)
-    mats = [_upload(mi, residual, tokens=kind.startswith("tokens")) for mi in mis]
+    # the output-codebook call takes the residual call's workspace, not its inputs
+    mats = [_upload(mi, residual and kind != "oc", tokens=kind.startswith("tokens")) for mi in mis]
     xs = [torch.from_numpy(mi.x).to(DEV) for mi in mis]
     ydt = torch.float16 if kind == "f16" else torch.float32
     ys = [torch.full((B, m.N), float("nan"), dtype=ydt, device=DEV) for m in mats]
@@ -78,6 +82,8 @@ def test_graph_replays_match_eager(kind):
     if kind.startswith("tokens"):
         def call(ms, xs_, B_, ys_, ws_, n_, stream=None):
             vq.vq_gemv_tokens(ms, xs_, B_, ys_, stream=stream)
+    if kind == "oc":
+        call = vq.vq_gemv_oc
     if kind == "swiglu":
         def call(ms, xs_, B_, ys_, ws_, n_, stream=None):
             vq.vq_gemv_swiglu(ms[0::2], ms[1::2], xs_[0::2], B_, ys_[0::2], ws_, n_, stream=stream)

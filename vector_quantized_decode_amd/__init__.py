@@ -81,6 +81,9 @@ _c = {
     "vq_gemv_f16": _sig("vq_gemv_f16", ctypes.c_int,
                         [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                          ctypes.POINTER(_vp), _vp, _sz, _vp]),
+    "vq_gemv_oc": _sig("vq_gemv_oc", ctypes.c_int,
+                       [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
+                        ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "vq_gemv_residual": _sig("vq_gemv_residual", ctypes.c_int,
                              [ctypes.POINTER(vq_matrix), _i32, ctypes.POINTER(_vp), _i32,
                               ctypes.POINTER(_vp), _vp, _sz, _vp]),
@@ -273,6 +276,14 @@ def vq_gemv_f16(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace, w
                              _ptr(workspace), ws_bytes, _stream(stream)), "vq_gemv_f16")
 
 
+def vq_gemv_oc(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace, ws_bytes: int,
+               stream=None) -> None:
+    """vq_gemv's result through the output-codebook tile kernel (workspace of
+    vq_workspace_bytes(..., residual=True))."""
+    _check(_c["vq_gemv_oc"](_mat_array(mats), len(mats), _ptr_array(xs), B, _ptr_array(ys),
+                            _ptr(workspace), ws_bytes, _stream(stream)), "vq_gemv_oc")
+
+
 def vq_gemv_residual(mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace,
                      ws_bytes: int, stream=None) -> None:
     arr = _mat_array(mats)
@@ -355,8 +366,9 @@ class PreparedCall:
 
 def prepare_gemv(name: str, mats: Sequence, xs: Sequence, B: int, ys: Sequence, workspace=None,
                  ws_bytes: int = 0) -> PreparedCall:
-    """A PreparedCall of vq_gemv, vq_gemv_shared, vq_gemv_f16 or vq_gemv_residual."""
-    if name not in ("vq_gemv", "vq_gemv_f16", "vq_gemv_residual", "vq_gemv_shared"):
+    """A PreparedCall of vq_gemv, vq_gemv_shared, vq_gemv_f16, vq_gemv_oc or
+    vq_gemv_residual."""
+    if name not in ("vq_gemv", "vq_gemv_f16", "vq_gemv_residual", "vq_gemv_shared", "vq_gemv_oc"):
         raise ValueError(name)
     arr, xa, ya = _mat_array(mats), _ptr_array(xs), _ptr_array(ys)
     return PreparedCall(name, (arr, len(mats), xa, B, ya, _ptr(workspace), ws_bytes),

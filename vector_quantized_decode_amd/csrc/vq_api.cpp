@@ -359,7 +359,8 @@ static int gemv_plain(const vq_matrix *m, int32_t count, const uint16_t *const *
 }
 
 static int residual_launch(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                           float *const *y, const Plan &p, char *ws, void *stream);
+                           float *const *y, const Plan &p, char *ws, void *stream,
+                           bool residual = true);
 
 static int gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                          float *const *y, void *workspace, size_t ws_bytes, void *stream) {
@@ -390,8 +391,25 @@ static int gemv_residual_noalloc(const vq_matrix *m, int32_t count, const uint16
   return residual_launch(m, count, x, B, y, p, static_cast<char *>(ws), stream);
 }
 
+// The output-codebook form of the plain call: the residual call's kernel,
+// plan and workspace with no rotation and no residual term.
+static int gemv_oc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+                   float *const *y, void *workspace, size_t ws_bytes, void *stream) {
+  int st = check_group(m, count, x, B, y, false);
+  if (st != VQ_OK) return st;
+  if (format_of(m[0]) != FMT_LUT8 || B != 1) return VQ_EUNSUPPORTED;
+  for (int i = 0; i < count; ++i)
+    if ((int64_t)(m[i].N + 31) / 32 * 32 * (m[i].K / 4) >= ((int64_t)1 << 31)) return VQ_EUNSUPPORTED;
+  Plan p;
+  make_plan(m, count, B, p);
+  if (p.grid > 0x7fffffff) return VQ_EUNSUPPORTED;
+  if (!workspace || ws_bytes < p.bytes) return VQ_EWORKSPACE;
+  if (!aligned(workspace, 256)) return VQ_EALIGN;
+  return residual_launch(m, count, x, B, y, p, static_cast<char *>(workspace), stream, false);
+}
+
 static int residual_launch(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
-                           float *const *y, const Plan &p, char *ws, void *stream) {
+                           float *const *y, const Plan &p, char *ws, void *stream, bool residual) {
   Lut8Args args;
   memset(&args, 0, sizeof(args));
   args.count = count;
@@ -403,8 +421,8 @@ static int residual_launch(const vq_matrix *m, int32_t count, const uint16_t *co
     d.wc = m[i].wc;
     d.x = x[i];
     d.xr = reinterpret_cast<const float *>(ws + q.xrot_off);
-    d.signs = static_cast<const uint8_t *>(m[i].signs);
-    d.alpha = static_cast<const uint16_t *>(m[i].alpha);
+    d.signs = residual ? static_cast<const uint8_t *>(m[i].signs) : nullptr;
+    d.alpha = residual ? static_cast<const uint16_t *>(m[i].alpha) : nullptr;
     d.y = y[i];
     d.partial = q.nsplit > 1 ? reinterpret_cast<float *>(ws + q.partial_off) : nullptr;
     d.counter = reinterpret_cast<uint32_t *>(ws + q.counter_off);
@@ -415,12 +433,13 @@ static int residual_launch(const vq_matrix *m, int32_t count, const uint16_t *co
     d.nrb = q.nrb;
     d.rpw = q.rpw;
     d.acc = reinterpret_cast<uint64_t *>(ws + q.acc_off);
-    const int h = m[i].rht_sign ? m[i].had_block : 1;
-    d.rs = m[i].rht_sign;
+    const int h = residual && m[i].rht_sign ? m[i].had_block : 1;
+    d.rs = residual ? m[i].rht_sign : nullptr;
     d.had = h;
     d.had_scale = (float)(1.0 / sqrt((double)h));
-    d.alpha_hdr = reinterpret_cast<const uint32_t *>(static_cast<const char *>(m[i].alpha) +
-                                                     alpha_body_bytes(m[i].N, m[i].K));
+    d.alpha_hdr = residual ? reinterpret_cast<const uint32_t *>(static_cast<const char *>(m[i].alpha) +
+                                                                alpha_body_bytes(m[i].N, m[i].K))
+                           : nullptr;
     // blocks up to 2048 are rotated inside the lookup kernel; larger ones first
     // by the rotation kernel, into the workspace
     d.fused = h <= 2048 ? 1 : 0;
@@ -435,7 +454,7 @@ static int residual_launch(const vq_matrix *m, int32_t count, const uint16_t *co
                      reinterpret_cast<float *>(ws + p.mp[i].xrot_off), stream);
     if (err) return hip_status(err);
   }
-  err = launch_lut8_residual(args, p.shape, max_wg, stream);
+  err = launch_lut8_residual(args, p.shape, max_wg, stream, residual);
   return hip_status(err);
 }
 
@@ -621,6 +640,11 @@ int vq_gemv_shared(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
 int vq_gemv_residual(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
                      float *const *y, void *workspace, size_t ws_bytes, void *stream) {
   return gemv_residual(m, count, x, B, y, workspace, ws_bytes, stream);
+}
+
+int vq_gemv_oc(const vq_matrix *m, int32_t count, const uint16_t *const *x, int32_t B,
+               float *const *y, void *workspace, size_t ws_bytes, void *stream) {
+  return gemv_oc(m, count, x, B, y, workspace, ws_bytes, stream);
 }
 
 int vq_gemv_residual_noalloc(const vq_matrix *m, int32_t count, const uint16_t *const *x,

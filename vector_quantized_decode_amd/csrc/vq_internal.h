@@ -141,7 +141,8 @@ Lut8Shape lut8_shape_residual(const vq_matrix *m, int32_t count);
 // Kernel launchers: return a hipError_t value (0 = success).
 // Lookup kernels: grid (grid_x, a.count), grid_x = the most workgroups any
 // matrix of the call needs.
-int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream);
+int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream,
+                         bool residual);
 int launch_pack(const uint32_t *idx, int64_t count, int nbits, uint8_t *out, void *stream);
 int launch_unpack(const uint8_t *packed, int64_t count, int nbits, uint32_t *out, void *stream);
 int launch_repack_wi8(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);

@@ -295,7 +295,10 @@ __device__ __forceinline__ float sign_of_byte(uint32_t s4, int t) {
   return (float)(int8_t)((s4 >> (8 * t)) & 0xffu);
 }
 
-template <int W, int STEPS, int NBX>
+// RES = false is the plain lookup GEMV in the output-codebook form [EVA
+// section 2.A]: the same OC tile, gather and hand-off with no rotation, no
+// sign table and no residual term (x itself is the tile's input).
+template <int W, int STEPS, int NBX, bool RES>
 __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args args) {
   static_assert(W == 16, "the OC tile takes waves 0-7, the sign table waves 8-15");
   constexpr int NT = W * 64;
@@ -336,14 +339,18 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   uint32_t sq[8];
   float4 xrw;
   if (wave == 0) {
-    const uint8_t *rsb = M.rs ? reinterpret_cast<const uint8_t *>(M.rs) : xb;
+    if constexpr (RES) {
+      const uint8_t *rsb = M.rs ? reinterpret_cast<const uint8_t *>(M.rs) : xb;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = kb + 256 * min(u, QS - 1) + 4 * lane;
-      xq[u] = *reinterpret_cast<const uint2 *>(xb + 2 * (size_t)e);
-      sq[u] = *reinterpret_cast<const uint32_t *>(rsb + e);
+      for (int u = 0; u < 8; ++u) {
+        const int e = kb + 256 * min(u, QS - 1) + 4 * lane;
+        xq[u] = *reinterpret_cast<const uint2 *>(xb + 2 * (size_t)e);
+        sq[u] = *reinterpret_cast<const uint32_t *>(rsb + e);
+      }
+      xrw = *reinterpret_cast<const float4 *>(M.xr + k0 + 4 * lane);
+    } else {
+      xq[0] = *reinterpret_cast<const uint2 *>(xb + 2 * (size_t)(k0 + 4 * lane));
     }
-    xrw = *reinterpret_cast<const float4 *>(M.xr + k0 + 4 * lane);
   }
   //    OC waves: centroids 32 wave + (lane % 32) as the MFMA A operand.  The
   //    eight OC waves hold the whole codebook, so max |WC| is taken from them.
@@ -355,7 +362,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
   u32x4 xbw[NBX];
 #pragma unroll
   for (int u = 0; u < NBX; ++u) xbw[u] = load16(xb + 16 * (size_t)min(t0 + u * NT, nxc - 1));
-  const uint32_t amax_bits = *M.alpha_hdr;
+  const uint32_t amax_bits = RES ? *M.alpha_hdr : 0u;
   __builtin_amdgcn_s_barrier();
 
   // 2. index, sign and alpha loads: per 32-row step, two index chunks, one
@@ -387,13 +394,20 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     const uint32_t oal = mine ? (uint32_t)(((sp * NP + rp) * 64 + lane) * 2) : kOutOfRange;
     va[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, oa, 0, kNontemporal));
     vb[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwi, ob, 0, kNontemporal));
-    vs[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, os, 0, kNontemporal));
-    al[g] = __builtin_amdgcn_raw_buffer_load_b16(ral, oal, 0, 0);
+    if constexpr (RES) {
+      vs[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, os, 0, kNontemporal));
+      al[g] = __builtin_amdgcn_raw_buffer_load_b16(ral, oal, 0, 0);
+    } else {
+      (void)os; (void)oal;
+    }
   };
   load_step(0);
 
   // 3. x_rot of subvector `lane` of this tile, formed by wave 0 into LDS
-  if (wave == 0) {
+  if (wave == 0 && !RES) {
+    const half2_t a = as_h2(xq[0].x), b = as_h2(xq[0].y);
+    *reinterpret_cast<float4 *>(xrs + 4 * lane) = make_float4((float)a.x, (float)a.y, (float)b.x, (float)b.y);
+  } else if (wave == 0) {
     float c[4] = {xrw.x, xrw.y, xrw.z, xrw.w};
     if (fused) {
       c[0] = c[1] = c[2] = c[3] = 0.f;
@@ -461,7 +475,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
       dst[m * 64] = a;
       dst[(m + 4) * 64] = b;
     }
-  } else {
+  } else if (RES) {
     // 5. sign table for sign byte p = 32*sp + (lane & 31): its 8 rotated
     //    inputs are x_rot 8p' .. 8p'+7 of the tile (p' = lane & 31); this
     //    wave writes high nibbles 2 (wave - 8) and 2 (wave - 8) + 1
@@ -547,7 +561,7 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
     float A[16], Bv[16], S[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t wq = va[g][q], wbq = vb[g][q], ws4 = vs[g][q];
+      const uint32_t wq = va[g][q], wbq = vb[g][q];
       A[4 * q + 0] = lds_at(lds, lut_addr<0>(wq, baseoc));
       A[4 * q + 1] = lds_at(lds, lut_addr<1>(wq, baseoc));
       A[4 * q + 2] = lds_at(lds, lut_addr<2>(wq, baseoc));
@@ -556,19 +570,25 @@ __global__ void __launch_bounds__(W * 64) lut8_residual_kernel(const Lut8Args ar
       Bv[4 * q + 1] = lds_at(lds, lut_addr<1>(wbq, baseoc));
       Bv[4 * q + 2] = lds_at(lds, lut_addr<2>(wbq, baseoc));
       Bv[4 * q + 3] = lds_at(lds, lut_addr<3>(wbq, baseoc));
-      S[4 * q + 0] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0400u));
-      S[4 * q + 1] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0501u));
-      S[4 * q + 2] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0602u));
-      S[4 * q + 3] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0703u));
+      if constexpr (RES) {
+        const uint32_t ws4 = vs[g][q];
+        S[4 * q + 0] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0400u));
+        S[4 * q + 1] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0501u));
+        S[4 * q + 2] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0602u));
+        S[4 * q + 3] = lds_at(lds, __builtin_amdgcn_perm(ws4, bsel[q], 0x0C0C0703u));
+      }
     }
-    // residual of (row r, group g): alpha times the sum over its 16 sign
-    // bytes; the two groups of a row sit in lanes 2r and 2r + 1
+    rowval[g] = reduce_rows32(A, Bv, lane);
+    if constexpr (RES) {
+      // residual of (row r, group g): alpha times the sum over its 16 sign
+      // bytes; the two groups of a row sit in lanes 2r and 2r + 1
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[i] += S[i + 8];
+      for (int i = 0; i < 8; ++i) S[i] += S[i + 8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[i] += S[i + 4];
-    const float sres = ((S[0] + S[2]) + (S[1] + S[3])) * (float)__builtin_bit_cast(_Float16, al[g]);
-    rowval[g] = reduce_rows32(A, Bv, lane) + (sres + dpp<DPP_QUAD_XOR1>(sres));
+      for (int i = 0; i < 4; ++i) S[i] += S[i + 4];
+      const float sres = ((S[0] + S[2]) + (S[1] + S[3])) * (float)__builtin_bit_cast(_Float16, al[g]);
+      rowval[g] += sres + dpp<DPP_QUAD_XOR1>(sres);
+    }
     const int row = (rb * M.rpw + g * W + wave) * 32 + rsel;
     if (packed && (lane & 1) == 0 && row < M.N) {
       term[g] = packed_term(rowval[g], fs);
@@ -642,25 +662,31 @@ int noalloc_scratch(void **out) {
 // --------------------------------------------------------------------------
 // launchers of the lookup kernels
 // --------------------------------------------------------------------------
-template <int STEPS, int NBX>
+template <int STEPS, int NBX, bool RES>
 static int launch_residual_t(const Lut8Args &a, int grid_x, hipStream_t st) {
   (void)hipGetLastError();  // report only this launch's error
-  hipLaunchKernelGGL((lut8_residual_kernel<16, STEPS, NBX>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
+  hipLaunchKernelGGL((lut8_residual_kernel<16, STEPS, NBX, RES>), dim3(grid_x, a.count), dim3(16 * 64), 0, st, a);
   return (int)hipGetLastError();
 }
 
-int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream) {
+template <bool RES>
+static int launch_lut8_t(const Lut8Args &a, const Lut8Shape &s, int grid_x, hipStream_t st) {
+  if (s.steps == 1 && s.nbx == 2) return launch_residual_t<1, 2, RES>(a, grid_x, st);
+  if (s.steps == 1 && s.nbx == 4) return launch_residual_t<1, 4, RES>(a, grid_x, st);
+  if (s.steps == 2 && s.nbx == 2) return launch_residual_t<2, 2, RES>(a, grid_x, st);
+  if (s.steps == 2 && s.nbx == 4) return launch_residual_t<2, 4, RES>(a, grid_x, st);
+  if (s.steps == 4 && s.nbx == 2) return launch_residual_t<4, 2, RES>(a, grid_x, st);
+  if (s.steps == 4 && s.nbx == 4) return launch_residual_t<4, 4, RES>(a, grid_x, st);
+  if (s.steps == 8 && s.nbx == 2) return launch_residual_t<8, 2, RES>(a, grid_x, st);
+  if (s.steps == 8 && s.nbx == 4) return launch_residual_t<8, 4, RES>(a, grid_x, st);
+  return (int)hipErrorInvalidConfiguration;
+}
+
+int launch_lut8_residual(const Lut8Args &a, const Lut8Shape &s, int grid_x, void *stream,
+                         bool residual) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (s.waves != 16) return (int)hipErrorInvalidConfiguration;
-  if (s.steps == 1 && s.nbx == 2) return launch_residual_t<1, 2>(a, grid_x, st);
-  if (s.steps == 1 && s.nbx == 4) return launch_residual_t<1, 4>(a, grid_x, st);
-  if (s.steps == 2 && s.nbx == 2) return launch_residual_t<2, 2>(a, grid_x, st);
-  if (s.steps == 2 && s.nbx == 4) return launch_residual_t<2, 4>(a, grid_x, st);
-  if (s.steps == 4 && s.nbx == 2) return launch_residual_t<4, 2>(a, grid_x, st);
-  if (s.steps == 4 && s.nbx == 4) return launch_residual_t<4, 4>(a, grid_x, st);
-  if (s.steps == 8 && s.nbx == 2) return launch_residual_t<8, 2>(a, grid_x, st);
-  if (s.steps == 8 && s.nbx == 4) return launch_residual_t<8, 4>(a, grid_x, st);
-  return (int)hipErrorInvalidConfiguration;
+  return residual ? launch_lut8_t<true>(a, s, grid_x, st) : launch_lut8_t<false>(a, s, grid_x, st);
 }
 
 // --------------------------------------------------------------------------

@@ -11,30 +11,36 @@ HBM before any timed region.
 Protocol.  C distinct copies of the layer (indices, codebooks, and for the
 residual workload signs, scales and rotation signs; >= 2 GiB in total, far
 above the 256 MB Infinity Cache and the L2s) are laid out once.  The K timed
-steps of a repeat are K back-to-back calls on K consecutive copies, captured
-in HIP graphs and replayed on one stream; HIP events on that stream bracket
-each repeat.  Exactly K steps are timed per repeat, over R repeats that start
-at successive copies; the reported period is the median repeat's.  Before
-each repeat's first event an untimed replay of the previous window keeps the
-GPU busy, so the host's graph submission latency falls outside the timed
-span (timing.graph_from_idle reports the repeats without it).
+steps of a repeat are K back-to-back calls on K consecutive copies; HIP
+events on the launch stream bracket each repeat, and the reported period is
+the median of R repeats that start at successive copies.  The K calls are
+timed two ways: captured in one HIP graph and replayed (an untimed replay of
+the previous window first, so the host's submission latency falls outside
+the timed span; timing.graph_from_idle reports the repeats without it), and
+issued one by one from Python after a spin kernel that lets the host queue
+them (timing.stream_launch).  A graph replay carries about 10 us of fixed
+cost, which matters for small K; single launches cost slightly more per
+call.  value uses the faster of the two medians (timing.reported names it);
+the read floor and the dense context are timed the same way.
 
 Prints one JSON line:
   value            weight bytes per layer / median call period (GB/s); us_per_layer
-  timing           median, min and max repeat times; the same K calls issued
-                   one by one from Python (plain stream launches) instead of
-                   from a graph; a warm figure (one copy repeated, cache-resident)
+  timing           median, min and max repeat times of both protocols; stream
+                   launches from an idle GPU (host submission included); a warm
+                   figure (one copy repeated, cache-resident); vq_gemv_oc (the
+                   output-codebook tile form) on the plain one-token 8-bit
+                   workloads; vq_gemv_shared on workloads with shared codebooks
   roofline         the lookup kernel (one launch per call; 16-bit indices add a
                    pre-pass launch, counted in): algorithmic bytes per call over
                    the median call period.  stream_read_gbs: a plain streaming
                    read (vq_stream_read) of the same copies' device index
-                   layouts (plus signs and scales), same K, same graphs, same
+                   layouts (plus signs and scales), same K, same protocols, same
                    repeats; frac_of_stream_read = achieved / stream_read_gbs.
                    traffic = HBM bytes per launch from the committed rocprofv3
                    counter summary, when it was taken on the current kernel
                    source (else null)
   context          a dense fp16 GEMV at the same shapes (torch.mm on fp16
-                   weights, C' distinct copies >= 2 GiB, same protocol):
+                   weights, C' distinct copies >= 2 GiB, same protocols):
                    context, not a target
   cpu_baseline     the float64 CPU oracle on the same layer, timed on the host
                    (one thread), repeated until >= --cpu-seconds
@@ -203,22 +209,46 @@ class Timer:
         return out
 
 
-def time_stream_launches(torch, call_for, copies: int, K: int, repeats: int, stream):
+def time_stream_launches(torch, call_for, copies: int, K: int, repeats: int, stream,
+                         lead_in: bool = True):
     """The same K calls issued one by one from Python (prepared ctypes
-    arguments), no graph."""
+    arguments), no graph.  With lead_in, a spin kernel (torch.cuda._sleep,
+    about 8 us per call) runs before e0 so that the host has queued the K
+    calls by the time the GPU reaches them: e0..e1 then spans the K calls
+    back to back, not the host's submission rate."""
     out = []
     for r in range(repeats):
         calls = [call_for((r * K + i) % copies) for i in range(K)]
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        e0.record(stream)
-        for f in calls:
-            f(stream)
-        e1.record(stream)
+        with torch.cuda.stream(stream):
+            if lead_in:
+                torch.cuda._sleep(20000 * K)
+            e0.record(stream)
+            for f in calls:
+                f(stream)
+            e1.record(stream)
         torch.cuda.synchronize()
         out.append(e0.elapsed_time(e1))
     return out
+
+
+def time_both(torch, call_for, copies: int, K: int, repeats: int, warmup: int, stream):
+    """Exactly K calls per repeat over the same layer copies, timed two ways:
+    one HIP graph of the K calls (Timer), and the K calls issued one by one
+    behind a spin lead-in.  A graph replay costs about 10 us of fixed time,
+    which a window of few calls cannot amortize; single launches cost a
+    little more per call.  Returns the faster protocol's summary, both
+    summaries, the faster one's name, the untimed warm-up calls run and the
+    Timer."""
+    t = Timer(torch, call_for, copies, K, stream)
+    warm = t.warm(warmup)
+    g = summary(t.time(repeats), K)
+    s = dict(summary(time_stream_launches(torch, call_for, copies, K, repeats, stream), K),
+             what="the K calls issued one by one after a spin lead-in")
+    best, launch = (g, "hip graph") if g["us_per_call"] <= s["us_per_call"] else (s, "stream launches")
+    return best, g, s, launch, warm, t
 
 
 def summary(ms_list, K):
@@ -266,12 +296,13 @@ def dense_gemv_run(args) -> dict:
             dense_for(c)(stream)
     torch.cuda.synchronize()
     dcop = dcopies if K > dcopies else -(-dcopies // K) * K
-    dt = Timer(torch, dense_for, dcop, K, stream)
-    dt.warm(args.warmup)
-    ds = summary(dt.time(args.repeats), K)
+    ds, dg, dsl, dlaunch, _, _ = time_both(torch, dense_for, dcop, K, args.repeats, args.warmup,
+                                           stream)
     return dict(ds, weight_bytes_per_layer=dense_bytes,
                 gbs=round(dense_bytes / (ds["us_per_call"] * 1e-6) / 1e9, 1),
-                copies=dcopies, launch="hip graph", blas="rocBLAS (torch preferred_blas_library)",
+                copies=dcopies, launch=dlaunch, graph_us_per_call=dg["us_per_call"],
+                stream_launch_us_per_call=dsl["us_per_call"],
+                blas="rocBLAS (torch preferred_blas_library)",
                 what="torch.mm of fp16 [N][K] weights with x^T, the workload's shapes and "
                      "tokens; context, not target")
 
@@ -462,17 +493,18 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K back-to-back calls per repeat
-    main_t = Timer(torch, call_for, copies, K, stream)
-    warm_done = main_t.warm(args.warmup)
-    ms = main_t.time(args.repeats)
-    st = summary(ms, K)
-    us_per_layer = st["us_per_call"]
+    best, st, sl, launch, warm_done, main_t = time_both(torch, call_for, copies, K, args.repeats,
+                                                         args.warmup, stream)
+    say(f"# graph: {args.repeats} x {K} steps (median {st['median_ms']:.4f} ms, "
+        f"min {st['min_ms']:.4f}, max {st['max_ms']:.4f}): {st['us_per_call']:.3f} us/layer")
+    say(f"# stream launches after a lead-in: {args.repeats} x {K} steps (median "
+        f"{sl['median_ms']:.4f} ms, min {sl['min_ms']:.4f}, max {sl['max_ms']:.4f}): "
+        f"{sl['us_per_call']:.3f} us/layer")
+    us_per_layer = best["us_per_call"]
     gbs = layer_bytes / (us_per_layer * 1e-6) / 1e9
-    say(f"# timed {args.repeats} x {K} steps (median {st['median_ms']:.4f} ms, "
-        f"min {st['min_ms']:.4f}, max {st['max_ms']:.4f}): {us_per_layer:.3f} us/layer, "
-        f"{gbs:.1f} GB/s")
+    say(f"# timed ({launch}): {us_per_layer:.3f} us/layer, {gbs:.1f} GB/s")
     timing = {"repeats": args.repeats, "steps_per_repeat": K, "warmup_steps_run": warm_done,
-              "graph": st}
+              "graph": st, "stream_launch": sl, "reported": launch}
     if not args.no_context:
         idle = summary(main_t.time(args.repeats, lead_in=False), K)
         timing["graph_from_idle"] = dict(idle, what="the same repeats with no lead-in: each "
@@ -505,22 +537,24 @@ def main():
             return read_prepared[c]
 
         read_bytes = sum(nb0)
-        rt = Timer(torch, read_for, copies, K, stream)
-        rt.warm(args.warmup)
-        rs = summary(rt.time(args.repeats), K)
-        read_gbs = read_bytes / (rs["us_per_call"] * 1e-6) / 1e9
-        say(f"# stream read of {read_bytes} B per call: {rs['us_per_call']:.3f} us, "
-            f"{read_gbs:.1f} GB/s")
+        rs, rg, rsl, rlaunch, _, rt = time_both(torch, read_for, copies, K, args.repeats,
+                                                args.warmup, stream)
         del rt
+        read_gbs = read_bytes / (rs["us_per_call"] * 1e-6) / 1e9
+        say(f"# stream read of {read_bytes} B per call ({rlaunch}): {rs['us_per_call']:.3f} us, "
+            f"{read_gbs:.1f} GB/s (graph {rg['us_per_call']:.3f}, stream launches "
+            f"{rsl['us_per_call']:.3f})")
 
-        sl = summary(time_stream_launches(torch, call_for, copies, K, args.repeats, stream), K)
-        say(f"# plain stream launches: {sl['us_per_call']:.3f} us/layer")
+        sn = summary(time_stream_launches(torch, call_for, copies, K, args.repeats, stream,
+                                          lead_in=False), K)
+        say(f"# stream launches from an idle GPU (host submission rate included): "
+            f"{sn['us_per_call']:.3f} us/layer")
         wt = Timer(torch, call_for, copies, K, stream, same_copy=True)
         wt.warm(args.warmup)
         ws_ = summary(wt.time(args.repeats), K)
         say(f"# warm (copy 0 repeated): {ws_['us_per_call']:.3f} us/layer")
         del wt
-        timing["stream_launch"] = sl
+        timing["stream_launch_from_idle"] = sn
         timing["warm_same_copy"] = ws_
         if wl.shared and not residual and not tokens and not wl.gated_pairs:
             # the same calls through vq_gemv_shared (shared matrices merged into units)
@@ -532,12 +566,12 @@ def main():
                                                 ws.numel())
                 return merged[c]
 
-            mt = Timer(torch, merged_for, copies, K, stream)
-            mt.warm(args.warmup)
-            ms_ = summary(mt.time(args.repeats), K)
+            ms_, _, _, mlaunch, _, mt = time_both(torch, merged_for, copies, K, args.repeats,
+                                                  args.warmup, stream)
             del mt
-            timing["vq_gemv_shared"] = dict(ms_, what="the same calls with the matrices that "
-                                                      "share a codebook and x merged into units")
+            timing["vq_gemv_shared"] = dict(ms_, launch=mlaunch,
+                                            what="the same calls with the matrices that share a "
+                                                 "codebook and x merged into units")
             say(f"# vq_gemv_shared (merged units): {ms_['us_per_call']:.3f} us/layer")
         if oc_able and not oc and not f16_out:
             # the same calls in the output-codebook tile form (vq_gemv_oc)
@@ -550,15 +584,17 @@ def main():
                                                   ws_oc.numel())
                 return oc_calls[c]
 
-            ot = Timer(torch, oc_for, copies, K, stream)
-            ot.warm(args.warmup)
-            os_ = summary(ot.time(args.repeats), K)
+            os_, _, _, olaunch, _, ot = time_both(torch, oc_for, copies, K, args.repeats,
+                                                  args.warmup, stream)
             del ot
-            timing["vq_gemv_oc"] = dict(os_, what="the same calls in the output-codebook tile "
+            timing["vq_gemv_oc"] = dict(os_, launch=olaunch,
+                                        what="the same calls in the output-codebook tile "
                                                   "form: an OC tile per workgroup in LDS, rows "
                                                   "split along K, a fixed-point atomic per row")
             say(f"# vq_gemv_oc (output-codebook tiles): {os_['us_per_call']:.3f} us/layer")
-        timing["stream_read"] = dict(rs, bytes_per_call=read_bytes,
+        timing["stream_read"] = dict(rs, bytes_per_call=read_bytes, launch=rlaunch,
+                                     graph_us_per_call=rg["us_per_call"],
+                                     stream_launch_us_per_call=rsl["us_per_call"],
                                      what="vq_stream_read over each copy's device index layouts"
                                           + (", signs and scales" if residual else ""))
 
@@ -653,7 +689,7 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.workload], "matrices": wl.count,
                    "K_N": [[s.K, s.N] for s in wl.matrices], "d": wl.d, "nbits": wl.nbits,
                    "B": wl.B, "weight_bytes_per_layer": layer_bytes, "layer_copies": copies,
-                   "distinct_codebooks_per_copy": True, "launch": "hip graph",
+                   "distinct_codebooks_per_copy": True, "launch": launch,
                    "call": "vq_gemv_oc" if oc else "default",
                    "operands": "f16", "accumulate": "f32", "y": "f16" if f16_out else "f32"},
         "timing": timing,

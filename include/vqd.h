@@ -22,6 +22,16 @@
  * s = +1 for a set sign bit and -1 for a clear one, group g = weights
  * [128 g, 128 g + 128) of the row.
  *
+ * Two forms compute it.  The output-codebook tile (vq_gemv_oc and
+ * vq_gemv_residual) holds an OC tile in LDS with one bank per lane, so its
+ * lookups never collide [EVA 2.A], and joins the K-slices of a row with one
+ * fixed-point atomic per row.  The per-index form (vq_gemv and the other
+ * calls) forms each OC entry when an index asks for it, from codebook copies
+ * in LDS, with whole rows per workgroup and no join; at d = 4, n = 8 its 16
+ * copies put two lanes on each bank pair, so about 44% of its LDS-active
+ * cycles are bank conflicts (the token call's 32 copies have none).  The
+ * per-index form measured faster on MI355X and is the default.
+ *
  * Conventions for every call below.
  *   - Tensor pointers are DEVICE pointers owned by the caller unless a
  *     parameter says "host".  The library never allocates, frees, copies

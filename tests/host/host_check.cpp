@@ -144,7 +144,7 @@ void check_wcmats(const vqd::WcArgs &a, int grid_x, Kind kind, int waves, bool b
   for (int s = 0; s < a.count; ++s) {
     const vqd::WcMat &d = a.mat[s];
     CHECK(d.B == B, "B");
-    CHECK(pow2(d.jsplit), "split %d not a power of two", d.jsplit);
+    if (kind != WC16T) CHECK(pow2(d.jsplit), "split %d not a power of two", d.jsplit);
     const int64_t NG = (d.N + 15) / 16;
     int rows_per_wg = 0;
     if (kind == WC8) {
@@ -164,7 +164,11 @@ void check_wcmats(const vqd::WcArgs &a, int grid_x, Kind kind, int waves, bool b
     } else if (kind == WC16T) {
       rows_per_wg = vqd::wc16t_rows_per_wg(d.jsplit);
       const int JB = d.J / 32;
+      CHECK(d.jsplit >= 1 && d.jsplit <= 16 && rows_per_wg >= 16, "16-bit split %d", d.jsplit);
       CHECK((JB + d.jsplit - 1) / d.jsplit <= 16, "16-bit segment of %d blocks", (JB + d.jsplit - 1) / d.jsplit);
+      // the S segments of ceil(JB / S) blocks cover the row
+      const int seg = (JB + d.jsplit - 1) / d.jsplit;
+      CHECK((int64_t)seg * d.jsplit >= JB, "16-bit segments miss blocks: JB=%d S=%d", JB, d.jsplit);
       CHECK(NG * JB * 1024 < ((int64_t)1 << 31), "16-bit buffer");
     }
     CHECK((int64_t)d.nwg * rows_per_wg >= d.N, "rows %d not covered: %d x %d", d.N, d.nwg, rows_per_wg);
@@ -175,7 +179,13 @@ void check_wcmats(const vqd::WcArgs &a, int grid_x, Kind kind, int waves, bool b
       if (d.wi == static_cast<const uint8_t *>(m[i].wi) && d.N == m[i].N && d.J == m[i].K / m[i].d) found = true;
     CHECK(found, "descriptor %d matches no matrix", s);
   }
-  CHECK(grid_x == maxwg, "grid %d vs %lld", grid_x, (long long)maxwg);
+  if (kind == WC16T) {                              // a flat grid of every workgroup
+    int64_t total = 0;
+    for (int s = 0; s < a.count; ++s) total += a.mat[s].nwg;
+    CHECK(grid_x == total, "16-bit grid %d vs %lld", grid_x, (long long)total);
+  } else {
+    CHECK(grid_x == maxwg, "grid %d vs %lld", grid_x, (long long)maxwg);
+  }
 }
 
 int gemv(vq_matrix *m, int count, int B, void *ws = nullptr, size_t wsb = 0) {

@@ -332,7 +332,10 @@ static int gemv_wc(const vq_matrix *m, int32_t count, const uint16_t *const *x, 
       maxbj = std::max<int64_t>(maxbj, (int64_t)B * (a.K / a.d));
     }
     const int prep_blocks = (int)std::min<int64_t>((maxbj + 255) / 256, 4096);
-    return hip_status(launch_wc16t(t, (int)max_wg, prep_blocks, stream));
+    int64_t total_wg = 0;                            // the lookup kernel's flat grid
+    for (int s = 0; s < count; ++s) total_wg += args.mat[s].nwg;
+    if (total_wg > 0x7fffffff) return VQ_EUNSUPPORTED;
+    return hip_status(launch_wc16t(t, (int)total_wg, prep_blocks, stream));
   }
   if (merge && f == FMT_LUT8 && burst && w8 == wc8_burst_waves()) {
     // vq_gemv_shared: matrices that pass the same codebook and x and have

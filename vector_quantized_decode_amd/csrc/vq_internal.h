@@ -63,7 +63,7 @@ struct WcMat {
   int32_t B;              // tokens
   int32_t ldy;            // y row stride (N)
   int32_t nwg;            // workgroups of this matrix
-  int32_t jsplit;         // waves sharing a row group along J (1, 2, 4)
+  int32_t jsplit;         // waves sharing a row group along J
   int32_t yf16;           // 1: y holds fp16 (the fp32 sum rounded to nearest even)
   int32_t nmem;           // 8-bit burst kernel: matrices sharing wc, x and shape laid
                           // end to end by row group (1: this matrix alone)
@@ -122,6 +122,8 @@ int launch_repack_wi8_rows(const uint8_t *canon, int N, int J, uint8_t *dev, voi
 int wc16t_jsplit(int J);
 int wc16t_rows_per_wg(int jsplit);
 bool wc16t_fits(int N, int J, int jsplit);
+// The 16-bit lookup kernel takes a flat grid of grid_x = the call's total
+// workgroups (the pre-pass keeps its (prep_blocks, count) grid).
 int launch_wc16t(const Wc16tArgs &a, int grid_x, int prep_blocks, void *stream);
 int launch_repack_wc16(const uint16_t *wc, uint16_t *wct, void *stream);
 int launch_repack_wi12(const uint8_t *canon, int N, int J, uint8_t *dev, void *stream);

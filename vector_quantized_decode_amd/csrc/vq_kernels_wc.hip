@@ -779,21 +779,37 @@ template <int W, int NBLK>
 __global__ void __launch_bounds__(W * 64) wc16t_kernel(const Wc16tArgs args) {
   constexpr int NT = W * 64;
   __shared__ __align__(16) _Float16 tbl[65536];
-  const WcMat M = load_wcmat(args.a);
-  if ((int)blockIdx.x >= M.nwg) return;
+  // A flat grid of the call's workgroups, matrix after matrix: workgroup
+  // blockIdx.x is workgroup b of matrix m.  One workgroup fills a CU, and
+  // workgroups go to the XCDs in turn, so a grid without empty workgroups
+  // gives every XCD the same count (a 2-D grid padded to the largest matrix
+  // put 33 on some XCDs of 32 CUs and ran them in two rounds).
+  int m = 0, b = (int)blockIdx.x;
+  while (m + 1 < args.a.count && b >= args.a.mat[m].nwg) {
+    b -= args.a.mat[m].nwg;
+    ++m;
+  }
+  const WcMat M = load_wcmat(args.a, m);
+  if (b >= M.nwg) return;
   const uint16_t *wct = M.wc;                         // dimension-major (vq_repack_wc)
-  const uint16_t *xt = args.xt[blockIdx.y];
+  const uint16_t *xt = args.xt[m];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lS = 31 - __builtin_clz((unsigned)M.jsplit);
-  const int S = 1 << lS;
-  const int rgl = wave >> lS, sg = wave & (S - 1);
+  // S waves per row group, W / S row groups per workgroup; the W mod S
+  // waves past them fill tables and wait at the barriers but own no rows
+  // (the divisions by the run-time S are made wave-uniform again, so that
+  // the segment bounds stay scalar and the block loop branches on them)
+  const int S = M.jsplit;
+  const int rpg = __builtin_amdgcn_readfirstlane(W / S);
+  const int rgl = __builtin_amdgcn_readfirstlane(wave / S);
+  const int sg = wave - rgl * S;
+  const bool active = rgl < rpg;
   const int JB = M.J >> 5;
   const int NG = (M.N + 15) >> 4;
-  const int rgw = (int)blockIdx.x * (W >> lS) + rgl;
+  const int rgw = b * rpg + rgl;
   const int rg = min(rgw, NG - 1);
-  const int seg = (JB + S - 1) >> lS;
-  const int kbeg = min(sg * seg, JB), kend = min(kbeg + seg, JB);
+  const int seg = __builtin_amdgcn_readfirstlane((JB + S - 1) / S);
+  const int kbeg = active ? min(sg * seg, JB) : JB, kend = min(kbeg + seg, JB);
   const int tok = lane & 15, sub = lane >> 4;
   const bool has_tok = tok < M.B;
 
@@ -842,13 +858,13 @@ __global__ void __launch_bounds__(W * 64) wc16t_kernel(const Wc16tArgs args) {
     f32x4_t *part = reinterpret_cast<f32x4_t *>(tbl);
     part[wave * 64 + lane] = acc;
     __syncthreads();
-    if (sg != 0) return;
+    if (!active || sg != 0) return;
     for (int q = 1; q < S; ++q) {
       const f32x4_t o = part[(wave + q) * 64 + lane];
       acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
     }
   }
-  if (rgw < NG) {
+  if (active && rgw < NG) {
     const int row = rgw * 16 + tok;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1002,7 +1018,7 @@ int launch_wc16t(const Wc16tArgs &a, int grid_x, int prep_blocks, void *stream) 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // report only this launch's error
   hipLaunchKernelGGL(wc16_prep_kernel, dim3(prep_blocks, a.a.count), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((wc16t_kernel<16, 16>), dim3(grid_x, a.a.count), dim3(16 * 64), 0, st, a);
+  hipLaunchKernelGGL((wc16t_kernel<16, 16>), dim3(grid_x), dim3(16 * 64), 0, st, a);
   return (int)hipGetLastError();
 }
 

@@ -49,13 +49,18 @@ bool wc8_burst_fits(int N, int J, int jsplit) {
 // Waves of the fused gate/up kernel: two row-group slots per output row
 // group, so 8 waves for a split of up to 4 and 16 for a split of 8.
 int wc8_swiglu_waves(int max_split) { return max_split <= 4 ? WC8_W : 2 * WC8_W; }
-// Waves per row group along J for the 16-bit kernel: the smallest power of
-// two (at most 16) that leaves each wave at most 16 blocks of 32 subvectors
-// (its indices stay in registers for the eight passes).
+// Waves per row group along J for the 16-bit kernel: the smallest count (at
+// most 16) that leaves each wave at most 12 blocks of 32 subvectors, else 16
+// (a wave's indices stay in registers for the eight passes, up to 16
+// blocks).  A workgroup of 16 waves holds 16 / S row groups and leaves
+// 16 mod S waves without rows: S need not divide 16, so that matrices of
+// different row lengths in one call get about the same blocks per wave
+// (LLaMA-13B shapes: 10 blocks per wave at K = 5120, 11 at K = 13824, where
+// a power-of-two split gave 14).
 int wc16t_jsplit(int J) {
   const int JB = J / 32;
   int s = 1;
-  while (s < 16 && (JB + s - 1) / s > 16) s *= 2;
+  while (s < 16 && (JB + s - 1) / s > 12) ++s;
   return s;
 }
 int wc16t_rows_per_wg(int jsplit) { return 16 / jsplit * 16; }

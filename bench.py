@@ -68,7 +68,7 @@ CSRC = os.path.join(ROOT, "vector_quantized_decode_amd", "csrc")
 # source of each workload's lookup kernel
 KERNEL_SRC = {1: "vq_kernels_wc.hip", 2: "vq_kernels_wc.hip", 3: "vq_kernels_wc.hip",
               4: "vq_kernels_wc.hip", 5: "vq_kernels.hip", 6: "vq_kernels_wc.hip",
-              7: "vq_kernels_wc.hip", 8: "vq_kernels_wc.hip", 9: "vq_kernels_wc.hip",
+              7: "vq_kernels_wc.hip", 8: "vq_kernels_tok.hip", 9: "vq_kernels_wc.hip",
               10: "vq_kernels_tok.hip", 11: "vq_kernels_wc.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 2 << 30       # distinct layer copies: at least this many weight bytes
@@ -352,8 +352,9 @@ def main():
     torch.cuda.set_device(dev)
     wl = synth.workload(args.workload)
     residual = wl.residual
-    # more than 4 tokens at d=4, n=8: the matrix-core call, on the row-tile index layout
-    tokens = (wl.d, wl.nbits) == (4, 8) and wl.B > 4
+    # 4 or more tokens at d=4, n=8: the matrix-core call, on the row-tile index
+    # layout (from 4 tokens on it measured faster than the dot-product call)
+    tokens = (wl.d, wl.nbits) == (4, 8) and wl.B >= 4
     f16_out = bool(args.f16_out)
     if f16_out and (residual or tokens):
         say("--f16-out applies to the plain and fused gate/up workloads")

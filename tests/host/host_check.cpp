@@ -426,6 +426,40 @@ void check_oc() {
             VQ_OK, "oc just below 2^31 index bytes");
 }
 
+// The fused gate/up call: every output row covered by a workgroup's slot
+// pairs, and the split and wave count its kernel is built for (16 waves for
+// a split of 8, else 8).
+void check_swiglu() {
+  for (int B : {1, 2})
+    for (int K : {256, 2048, 4096, 8192, 14336, 32768})
+      for (int N : {1, 17, 700, 11008, 14336}) {
+        vq_matrix g[2] = {mat(K, N), mat(K, N)};
+        vq_matrix u[2] = {mat(K, N), mat(K, N)};
+        g[1].wi = P(0x1000000); u[0].wi = P(0x2000000); u[1].wi = P(0x3000000);
+        const uint16_t *x[2] = {static_cast<const uint16_t *>(P(0x400000)), static_cast<const uint16_t *>(P(0x410000))};
+        float *y[2] = {static_cast<float *>(P(0x800000)), static_cast<float *>(P(0x810000))};
+        for (int cnt : {1, 2}) {
+          const int st = vq_gemv_swiglu(g, u, cnt, x, B, y, nullptr, 0, nullptr);
+          if (st == VQ_EUNSUPPORTED) continue;                 // rows past the burst kernel
+          CHECK(st == VQ_OK, "swiglu K=%d N=%d B=%d: %d", K, N, B, st);
+          CHECK(last.kind == SWIGLU, "swiglu kind");
+          CHECK(last.waves == 8 || last.waves == 16, "swiglu waves %d", last.waves);
+          int64_t maxwg = 0;
+          for (int s = 0; s < cnt; ++s) {
+            const vqd::WcMat &d = last.pair.a.mat[s];
+            CHECK(pow2(d.jsplit) && 2 * d.jsplit <= last.waves, "swiglu split %d waves %d", d.jsplit, last.waves);
+            const int R = last.waves / d.jsplit / 2 * 16;
+            CHECK((int64_t)d.nwg * R >= d.N && (int64_t)(d.nwg - 1) * R < d.N, "swiglu rows N=%d", d.N);
+            maxwg = std::max<int64_t>(maxwg, d.nwg);
+          }
+          CHECK(last.grid_x == maxwg, "swiglu grid");
+          int maxs = 1;
+          for (int s = 0; s < cnt; ++s) maxs = std::max(maxs, last.pair.a.mat[s].jsplit);
+          CHECK(last.waves == (maxs > 4 ? 16 : 8), "swiglu waves %d for split %d", last.waves, maxs);
+        }
+      }
+}
+
 void check_stream_read() {
   const size_t sizes[] = {16, 1 << 20, 4194304, 12845056, ((size_t)1 << 31) - 16};
   std::vector<const void *> b(5, P());
@@ -447,6 +481,7 @@ int main() {
   check_tokens();
   check_residual();
   check_oc();
+  check_swiglu();
   check_stream_read();
   if (failures) {
     fprintf(stderr, "%d host check(s) failed\n", failures);

@@ -441,6 +441,17 @@ def test_gemv_tokens_agrees_with_plain_call():
     _assert_close(yt, yp.astype(np.float64), "tokens against plain")
 
 
+def test_gemv_tokens_workload8_four_tokens():
+    # LLaMA-7B q/k/v/o for 4 tokens through the matrix-core call, the launch
+    # bench.py times for 4 tokens: every output of every matrix
+    _say("gemv_tokens workload 8 (4 x 4096x4096, 4 tokens, one launch)")
+    w = synth.workload(8)
+    mis = [synth.matrix_inputs(8, m) for m in range(w.count)]
+    ys = _run_tokens([_upload_rows(mi) for mi in mis], [mi.x for mi in mis], 4)
+    for m, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _dequant_all_rows(mi), f"workload 8 (tokens) matrix {m}")
+
+
 def test_gemv_workload10_sixteen_tokens():
     # LLaMA-7B q/k/v/o for 16 tokens in one launch, in the launch bench.py
     # times: all 16 x 4096 outputs of every matrix

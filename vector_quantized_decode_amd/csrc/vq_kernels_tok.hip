@@ -131,10 +131,13 @@ __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4))
       const_cast<uint16_t *>(M.x), (short)0, M.B * M.J * 8, kBufferWord3);
   // row groups past the matrix, columns past the segment and tokens past B
   // read zeros (rows past N within the last group are zero in the layout)
+  // (a wave-uniform select of the base, then the lane's offset: no branch,
+  // so the scalar codebook loads stay ahead of these loads)
   auto wi_off = [&](int r, int k) -> uint32_t {
     const int rg = rg0 + r;
-    return (k < kend && rg < NG) ? ((uint32_t)k * (uint32_t)NG + (uint32_t)rg) * 1024u + (uint32_t)lane * 16u
-                                 : kOutOfRange;
+    const bool in = (k < kend) & (rg < NG);
+    const uint32_t b = in ? ((uint32_t)k * (uint32_t)NG + (uint32_t)rg) * 1024u : kOutOfRange;
+    return b + (uint32_t)lane * 16u;
   };
   auto x_off = [&](int k, int i) -> uint32_t {
     return (k < kend && m16 < M.B)
@@ -142,10 +145,21 @@ __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4))
                : kOutOfRange;
   };
 
-  // 1. codebook entries for the replicas, the first column's indices and x
-  uint2 ent[RP];
+  // 1. codebook entries for the replicas, through the scalar data cache:
+  //    thread 64 w + l replicates entries 4 w + l / 16 + 32 u (u < 8), so
+  //    wave w reads the eight 32-byte runs at entry 4 w + 32 u with scalar
+  //    loads, issued before the vector loads of the first column (they do
+  //    not queue behind those), and each lane picks its entry of each run
+  //    after them.  Then the first column's indices and x.
+  static_assert(W == 8 && RP == 8, "the scalar codebook fetch serves workgroups of 8 waves");
+  typedef const __attribute__((address_space(4))) uint32_t cu32;
+  cu32 *cbs = (cu32 *)M.wc;
+  uint32_t sc[RP][8];
 #pragma unroll
-  for (int u = 0; u < RP; ++u) ent[u] = reinterpret_cast<const uint2 *>(M.wc)[(threadIdx.x + u * NT) >> 4];
+  for (int u = 0; u < RP; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sc[u][i] = cbs[8 * wave + 64 * u + i];
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 ib[RW], xa[8];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -153,6 +167,21 @@ __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     xa[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off(kbeg, q), 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
+  uint2 ent[RP];
+  {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      uint32_t a = sc[u][0], b = sc[u][1];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) {
+        a = (q == k) ? sc[u][2 * k] : a;
+        b = (q == k) ? sc[u][2 * k + 1] : b;
+      }
+      ent[u] = uint2{a, b};
+    }
+  }
   // 2. replicas into LDS: entry s >> 4, copies 2 (s & 15) and + 1
 #pragma unroll
   for (int u = 0; u < RP; ++u) {

@@ -145,6 +145,26 @@ def test_gemv_16bit_shapes(K, N, B):
     _assert_close(y, ref, f"16-bit K={K} N={N} B={B}")
 
 
+def test_gemv_16bit_mixed_group_flat_grid():
+    # the 16-bit lookup kernel takes a flat grid of the call's workgroups and
+    # each workgroup finds its matrix by a scan; a group of eight matrices of
+    # different row lengths (splits of 1, 2, 3, 5, 10 and 16 waves, so
+    # some workgroups leave waves without rows), tiny and ragged row counts,
+    # and in an order the launcher sorts: every row against the oracle and
+    # each matrix bitwise its result alone
+    shapes = [(256, 1), (5120, 37), (13824, 100), (2048, 16), (1024, 333), (30720, 20),
+              (65536, 17), (8192, 700)]
+    _say(f"gemv 16-bit mixed group of {len(shapes)}")
+    mis = [synth.small_matrix(K, N, 8, 16, B=5, seed=900 + i) for i, (K, N) in enumerate(shapes)]
+    mats = [_up(mi) for mi in mis]
+    ys = _run(mats, [mi.x for mi in mis], 5)
+    for i, (mi, y) in enumerate(zip(mis, ys)):
+        _assert_close(y, _dequant_rows(mi), f"16-bit group matrix {i} K={mi.K} N={mi.N}")
+    for i in (0, 2, 6):
+        (y1,) = _run([mats[i]], [mis[i].x], 5)
+        assert np.array_equal(y1.view(np.uint32), ys[i].view(np.uint32)), f"matrix {i} alone"
+
+
 @pytest.mark.parametrize("d,nbits,B", [(4, 8, 1), (4, 8, 4), (4, 12, 1), (8, 16, 1), (8, 16, 16)])
 def test_gemv_longest_supported_rows(d, nbits, B):
     # K = 65536, the longest row each 16-bit call takes (16 waves x 16 blocks

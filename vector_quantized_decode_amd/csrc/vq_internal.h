@@ -52,7 +52,10 @@ struct Lut8Args {
   int32_t count;
 };
 
-// Per-matrix descriptor of the virtual-OC kernels (n = 12 and n = 16).
+// Per-matrix descriptor of the per-index kernels (n = 8, 12 and 16, and the
+// token kernel).  Matrix m is served by workgroups (x, m) of a 2-D grid as
+// wide as the largest matrix needs, except for the 16-bit lookup kernel,
+// which takes a flat grid of every matrix's workgroups in turn.
 struct WcMat {
   const uint8_t *wi;      // WI: device layout tile-16x64(-12), tile-16x32-16 or row tiles
   const uint16_t *wc;     // fp16 codebook [2^n][d]

@@ -1,6 +1,6 @@
-// HIP kernels of libvqd for large codebooks (gfx950): the output codebook is
-// kept virtual -- each entry OC[j][c] = x_j . WC[c] is formed when an index
-// asks for it.
+// HIP kernels of libvqd in the per-index form (gfx950): each output-codebook
+// entry OC[j][c] = x_j . WC[c] is formed when an index asks for it, from a
+// codebook held in LDS, and a workgroup covers whole rows.
 //
 // Sources, cited by page title and section:
 //   [EVA]  "EVA: Accelerating LLM Decoding via an Efficient Vector
@@ -9,18 +9,20 @@
 //          lookups into it by the weight indices) and section 2.B (the
 //          codebooks stay on chip while indices stream in tiles).
 //
-// Why virtual.  A workgroup that owns R rows would build 2^n OC entries per
-// subvector for R lookups per subvector.  At n = 8 and R = 512 that is half an
-// entry per lookup and the OC tile pays for itself (vq_kernels.hip).  At
-// n = 12 (4096 centroids) the rows of a matrix number 4096-11008, so any tile
-// costs at least one entry -- one LDS store -- per lookup, and splitting the
-// subvectors over workgroups adds a cross-workgroup hand-off.  Forming the
-// entry at lookup time costs the same arithmetic (a d-term dot product) and
-// needs only the codebook on chip:
+// Why per index.  An OC tile in LDS (vq_kernels.hip) covers 256 inputs of
+// every centroid, so a row spans K / 256 workgroups that must meet again; on
+// MI355X that join cost more than forming entries per index at n = 8 (LLaMA-7B
+// q/k/v/o: 7.4 against 5.8 us), and at n = 12 or 16 any tile costs at least
+// one LDS store per lookup.  Forming the entry at lookup time costs the same
+// d-term dot product and needs only the codebook on chip:
+//   * wc8_burst_kernel / wc8_kernel (d = 4, n = 8, 1-4 tokens): the 2 KiB
+//     codebook in 16 LDS copies; a lane owns one subvector of a 16-row chunk
+//     and forms x_j . WC[c] for its 16 indices with two fp16 dot products
+//     each.  wc8_swiglu_kernel and wc8_burst_units_kernel are its gate/up and
+//     shared-codebook forms.
 //   * wc12_kernel (d = 4, n = 12, one token): WC (4096 x 4 fp16, 32 KiB) sits
 //     in LDS; a lane owns one subvector j, reads WC[c] (8 bytes) for each
 //     index and adds x_j . WC[c] with two packed fp16 dot products into fp32.
-//     Each workgroup covers whole rows: no partial sums leave it.
 //   * wc16t_kernel (d = 8, n = 16, up to 16 tokens): the codebook (65536 x 8
 //     fp16, 1 MiB) does not fit in LDS, but one of its dimensions does
 //     (65536 fp16, 128 KiB).  The kernel makes eight passes, one per

@@ -54,3 +54,23 @@ def test_bench_json_line_fields():
     assert t["steps_per_repeat"] == 6 and t["repeats"] == 3
     assert t["reported"] in ("hip graph", "stream launches")
     assert d["parity"]["pass"] is True
+
+
+@pytest.mark.gpu
+def test_bench_oc_call_line():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cmd = [sys.executable, BENCH, "--workload", "1", "--call", "oc", "--steps", "4", "--warmup", "2",
+           "--repeats", "3", "--no-cpu", "--no-context"]
+    print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-3000:]
+    d = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1])
+    assert d["config"]["call"] == "vq_gemv_oc" and d["steps"] == 4
+    assert d["parity"]["pass"] is True and d["value"] > 0
+    # a call that the output-codebook form does not serve is refused
+    r = subprocess.run([sys.executable, BENCH, "--workload", "3", "--call", "oc", "--steps", "2"],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 2
+

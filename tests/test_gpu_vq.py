@@ -782,3 +782,25 @@ def test_gemv_residual_large_magnitudes():
     mi.alpha = (mi.alpha.astype(np.float64) * 50.0).astype(np.float16)
     (y,), _ = _run_gemv([_upload(mi, residual=True)], [mi.x], residual=True)
     _assert_close(y, _oracle_res(mi), "residual large magnitudes")
+
+
+# ------------------------------------------------------------------ the read floor
+def test_stream_read_reads_every_word():
+    # the measurement kernel must read every byte it is timed on: each
+    # wavefront stores the XOR of what it read, so the XOR of the sink equals
+    # the XOR of every 32-bit word of the buffers (loads past a buffer's end
+    # return zeros, which leave it unchanged)
+    _say("vq_stream_read XOR check")
+    sizes = [16, (1 << 20) + 48, (4 << 20) + 1024]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    bufs = [torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV, generator=g) for n in sizes]
+    words = vq.vq_stream_read_sink_words(sizes)
+    sink = torch.zeros(words, dtype=torch.int32, device=DEV)
+    vq.vq_stream_read(bufs, sizes, sink, words)
+    torch.cuda.synchronize()
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+    exp = 0
+    for b in bufs:
+        exp ^= int(np.bitwise_xor.reduce(b.cpu().numpy().view(np.uint32)))
+    assert got == exp
